@@ -1,0 +1,183 @@
+/*
+ * la.h -- C ABI of liblinattn: causal linear attention (Lightning Attention
+ * forward) for AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (page title, then section):
+ *   [Tut]    "六十四：MiniMax-01" (LLM tutorial, lesson 64), section 3
+ *            "Lightning Attention 的定位": phi(q)^T phi(k) similarity, the
+ *            causal (i <= t) normalised form, and the recurrent state
+ *            S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t).
+ *   [Arch]   "MiniMax-Text-01 405B MoE模型架构与训练策略解析", section 2.1:
+ *            Q, K, V = SiLU(.), Y = Q (K^T V), out = RMSNorm(Y) * sigmoid(X).
+ *   [Deploy] xdnf.cn/news/303307 (MoE memory under long context), section 3:
+ *            lightning-attention block size 256 with tail pad options
+ *            {32, 64, 128}, chunked prefill; section 6: prefill and decode
+ *            run as separate calls.
+ *
+ * What every call computes, per sequence and head (phi = SiLU, applied to the
+ * pre-activation q, k and v that the caller passes):
+ *     S <- S + phi(k_t) phi(v_t)^T          (d x d, fp32 state)
+ *     z <- z + phi(k_t)                     (normalised mode only)
+ *     y_t = phi(q_t)^T S                    (read after the update: i <= t)
+ *     y_t = y_t / (phi(q_t)^T z)            (normalised mode only, no epsilon)
+ * and, when gated, per token over a group of features (default all H*d):
+ *     out_t = y_t / sqrt(mean(y_t^2) + eps) * w * sigmoid(x_t).
+ * There is no 1/sqrt(d) scale and no decay.
+ *
+ * Conventions shared by all calls.
+ *   - Every tensor argument is a DEVICE pointer to contiguous row-major data,
+ *     16-byte aligned.  Shapes are given per argument below.
+ *   - The caller owns every buffer.  The library never allocates device
+ *     memory; scratch space comes from the caller through `workspace`
+ *     (size from the matching *_workspace_bytes query).
+ *   - Calls are asynchronous and stream-ordered on `hip_stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream); they never
+ *     synchronise the device.
+ *   - All validation runs on the host before any HIP call.  On
+ *     LA_ERR_INVALID_ARGUMENT, LA_ERR_UNSUPPORTED or
+ *     LA_ERR_WORKSPACE_TOO_SMALL the call has no side effects.
+ *   - LA_ERR_HIP reports a failed kernel launch (hipGetLastError); device
+ *     buffers may then be partly written.
+ *   - `out` must not overlap any input.  `state_out` may equal `state_in` and
+ *     `z_out` may equal `z_in` (exact aliasing only).
+ *   - No C++ exception crosses this interface; no global mutable state, so
+ *     calls on distinct streams with distinct buffers may run concurrently.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, bad size, bad option */
+    LA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. d not in {64,128}) */
+    LA_ERR_WORKSPACE_TOO_SMALL = 3,
+    LA_ERR_HIP = 4                 /* a HIP launch failed */
+} la_status_t;
+
+typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
+
+/* Options.  Start from la_default_options().
+ *   block_size  tokens per block of the blocked evaluation: intra-block terms
+ *               use the masked quadratic form, inter-block terms the carried
+ *               state ([Arch] 2.1, [Deploy] 3).  Mathematically every block
+ *               size gives the same result; it changes fp32 rounding order
+ *               only.  0 = library default (64).  The bf16 d=128 matrix-core
+ *               path implements 64; the fp32 path implements 32, 64, 128
+ *               and 256.  Other values: LA_ERR_UNSUPPORTED.  Partial tail
+ *               blocks are zero-padded to the next of 32 or 64 rows
+ *               (SiLU(0) = 0, so the pad adds nothing).
+ *   normalized  0: y = phi(q)^T S.  1: y = phi(q)^T S / phi(q)^T z.
+ *   gated       0: out = y.  1: out = RMSNorm(y) * w * sigmoid(x).
+ *   norm_group  RMSNorm width in features: 0 = H*d (whole token), or any
+ *               divisor of H*d that is a multiple of 64 (e.g. d = per head).
+ *   rms_eps     epsilon inside the square root (default 1e-6).
+ *   chunk_tokens tokens per independently scheduled chunk of one sequence
+ *               (multiple of 64); 0 = chosen by the library.  Changes fp32
+ *               rounding order only.                                          */
+typedef struct {
+    int32_t block_size;
+    int32_t normalized;
+    int32_t gated;
+    int32_t norm_group;
+    float rms_eps;
+    int32_t chunk_tokens;
+} la_options_t;
+
+la_options_t la_default_options(void);
+
+/* Prefill of a batch of Bt equal-length sequences.
+ *   q, k, v     [Bt, T, H, d]  in_dtype, pre-activation (SiLU applied inside)
+ *   x_gate      [Bt, T, H*d]   in_dtype gate pre-activation; required iff gated
+ *   rms_weight  [H*d] fp32 RMSNorm weight, or NULL for unit weight
+ *   state_in    [Bt, H, d, d] fp32 initial state (key feature i, value
+ *               feature j at [i*d + j]), or NULL for zeros
+ *   z_in        [Bt, H, d] fp32 initial normaliser, or NULL for zeros
+ *   out         [Bt, T, H*d]   out_dtype (feature index h*d + j)
+ *   state_out   [Bt, H, d, d] fp32 final state, or NULL
+ *   z_out       [Bt, H, d] fp32 final normaliser, or NULL
+ *   Bt >= 1, T >= 0 (T = 0 only copies state_in to state_out), H >= 1,
+ *   d in {64, 128}.  Total elements Bt*T*H*d must be < 2^31 * 64.
+ *   workspace   device scratch of at least
+ *               la_prefill_workspace_bytes(Bt, T, H, d, opt) bytes, 256-byte
+ *               aligned (may be NULL when that size is 0).                    */
+la_status_t la_prefill(const void* q, const void* k, const void* v,
+                       const void* x_gate, const float* rms_weight,
+                       const float* state_in, const float* z_in,
+                       void* out, float* state_out, float* z_out,
+                       int32_t Bt, int32_t T, int32_t H, int32_t d,
+                       la_dtype_t in_dtype, la_dtype_t out_dtype,
+                       const la_options_t* opt,
+                       void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Prefill of a packed batch of variable-length sequences; the state starts
+ * from state_in[s] (or zero) at each sequence start cu_seqlens[s].
+ *   q, k, v     [total_T, H, d] in_dtype, sequences back to back
+ *   x_gate      [total_T, H*d] | NULL;  rms_weight [H*d] | NULL
+ *   cu_seqlens  DEVICE int32 [num_seqs + 1]: 0 = c_0 <= c_1 <= ... = total_T.
+ *               Its contents are a precondition (they are not read on the
+ *               host); every length must be <= max_seqlen.
+ *   max_seqlen  upper bound of the sequence lengths (host value)
+ *   state_in/z_in/state_out/z_out  [num_seqs, H, d, d] / [num_seqs, H, d] | NULL
+ *   out         [total_T, H*d] out_dtype                                      */
+la_status_t la_prefill_varlen(const void* q, const void* k, const void* v,
+                              const void* x_gate, const float* rms_weight,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t total_T, int32_t max_seqlen,
+                              const float* state_in, const float* z_in,
+                              void* out, float* state_out, float* z_out,
+                              int32_t H, int32_t d,
+                              la_dtype_t in_dtype, la_dtype_t out_dtype,
+                              const la_options_t* opt,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* One decode token for each of N sequences ([Tut] 3: the new token only
+ * updates the state and reads its output from it; [Deploy] 6: decode is a
+ * call of its own).
+ *   q, k, v     [N, H, d] in_dtype, one pre-activation token per sequence
+ *   x_gate      [N, H*d] | NULL (required iff gated);  rms_weight [H*d] | NULL
+ *   state       [N, H, d, d] fp32, updated IN PLACE (S <- S + phi(k) phi(v)^T)
+ *   z           [N, H, d] fp32, updated in place; required iff normalized
+ *   out         [N, H*d] out_dtype, y read from the updated state
+ *   workspace   la_decode_workspace_bytes(N, H, d, opt) bytes (0 unless gated
+ *               with a bf16 output).                                          */
+la_status_t la_decode_step(const void* q, const void* k, const void* v,
+                           const void* x_gate, const float* rms_weight,
+                           float* state, float* z, void* out,
+                           int32_t N, int32_t H, int32_t d,
+                           la_dtype_t in_dtype, la_dtype_t out_dtype,
+                           const la_options_t* opt,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace sizes in bytes for the same arguments (0 means none needed);
+ * they return (size_t)-1 for arguments the matching call would reject. */
+size_t la_prefill_workspace_bytes(int32_t Bt, int32_t T, int32_t H, int32_t d,
+                                  la_dtype_t in_dtype, la_dtype_t out_dtype,
+                                  const la_options_t* opt);
+size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int32_t max_seqlen,
+                                         int32_t H, int32_t d,
+                                         la_dtype_t in_dtype, la_dtype_t out_dtype,
+                                         const la_options_t* opt);
+size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out_dtype,
+                                 const la_options_t* opt);
+
+/* Chunk length (tokens) the library would use for these arguments; for
+ * reporting and tests.  -1 on invalid arguments. */
+int32_t la_prefill_chunk_tokens(int32_t num_seqs, int32_t total_T, int32_t max_seqlen,
+                                int32_t H, int32_t d, la_dtype_t in_dtype,
+                                const la_options_t* opt);
+
+/* Static, NUL-terminated description of a status code. */
+const char* la_status_string(la_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for the linear-attention path.
+
+This module only draws random numbers and shapes them; it holds none of the
+method's arithmetic, so both the HIP path and the CPU oracle take their inputs
+from here.
+
+Recipe (every workload):
+  * a torch ``Generator`` seeded with ``seed * 1000 + index`` per tensor, in
+    the fixed order q=0, k=1, v=2, x=3, state=4, z=5 (decode steps use
+    index 100 + step);
+  * values drawn as fp32 standard normals, multiplied by the workload's
+    scale in fp32, then rounded to the input dtype (bf16 rounding is
+    round-to-nearest-even, torch's ``.to(torch.bfloat16)``);
+  * small workloads are drawn on the CPU; the 1M-token and packed workloads
+    are drawn on the GPU (``device="cuda"``) because CPU generation of 4e9
+    normals takes minutes.  The device is part of the recipe: the same seed
+    gives different values on CPU and GPU.
+  * variable lengths: numpy ``PCG64`` seeded with ``seed``, lengths
+    ``round(exp(U(ln 1024, ln 131072)))`` drawn until their sum reaches the
+    target; the last one is clipped to the remainder.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "prefill" | "varlen" | "decode"
+    seed: int
+    H: int
+    d: int
+    dtype: str           # "f32" | "bf16"
+    T: int = 0           # prefill: tokens per sequence
+    batch: int = 1       # prefill: sequences
+    total_T: int = 0     # varlen: packed tokens
+    N: int = 0           # decode: sequences
+    steps: int = 0       # decode: steps
+    scale: float = 1.0   # multiplier of the N(0,1) q, k, v draws
+    block: int = 64
+    gated: bool = False
+    normalized: bool = False
+    state_std: float = 0.0
+    gen_device: str = "cpu"
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+INV_SQRT128 = 1.0 / math.sqrt(128.0)
+
+WORKLOADS = {
+    # tiny fp32 case the oracle finishes in well under a second
+    "tiny_f32": Workload("tiny_f32", "prefill", 1001, H=2, d=64, dtype="f32", T=1024,
+                         block=64, note="fp32, B=1 T=1024 H=2 d=64, ungated"),
+    # bf16 prefill, 32K tokens, gated
+    "prefill_32k": Workload("prefill_32k", "prefill", 1002, H=8, d=128, dtype="bf16",
+                            T=32768, scale=INV_SQRT128, gated=True,
+                            note="bf16, B=1 T=32768 H=8 d=128, RMSNorm*sigmoid gate"),
+    # long-context prefill: one GPU's 8-head share of a 64-head layer
+    "prefill_1m": Workload("prefill_1m", "prefill", 1003, H=8, d=128, dtype="bf16",
+                           T=1048576, scale=INV_SQRT128, gated=True, gen_device="cuda",
+                           note="bf16, B=1 T=1048576 H=8 d=128, RMSNorm*sigmoid gate"),
+    # packed variable-length batch
+    "varlen_512k": Workload("varlen_512k", "varlen", 1004, H=8, d=128, dtype="bf16",
+                            total_T=524288, scale=INV_SQRT128, gated=True, gen_device="cuda",
+                            note="bf16 packed, lengths log-uniform in [1K,128K], sum 524288"),
+    # decode: 64 sequences x 64 heads, 1000 steps
+    "decode_64x64": Workload("decode_64x64", "decode", 1005, H=64, d=128, dtype="bf16",
+                             N=64, steps=1000, state_std=0.01, gen_device="cuda",
+                             note="decode, N=64 H=64 d=128, fp32 state N(0,0.01)"),
+}
+
+
+def _gen(seed: int, index: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000 + int(index))
+    return g
+
+
+def normal(shape, seed: int, index: int, scale: float = 1.0, dtype=torch.float32,
+           device="cpu") -> torch.Tensor:
+    """N(0,1) * scale drawn in fp32 on ``device`` with a per-tensor seed, then
+    rounded to ``dtype``."""
+    g = _gen(seed, index, device)
+    t = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if scale != 1.0:
+        t.mul_(float(scale))
+    return t.to(dtype)
+
+
+def varlen_lengths(seed: int, total: int, lo: int = 1024, hi: int = 131072) -> list:
+    """Lengths round(exp(U(ln lo, ln hi))) until they sum to ``total``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, acc = [], 0
+    while acc < total:
+        L = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        L = max(1, min(L, total - acc))
+        out.append(L)
+        acc += L
+    return out
+
+
+def cu_from_lengths(lengths) -> torch.Tensor:
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + int(L))
+    return torch.tensor(cu, dtype=torch.int32)
+
+
+def prefill_inputs(w: Workload, T: int | None = None, batch: int | None = None,
+                   device: str | None = None, with_gate: bool | None = None):
+    """q, k, v [batch, T, H, d] and x [batch, T, H*d] (or None) for a
+    prefill workload; ``T``/``batch`` override the workload's sizes."""
+    T = w.T if T is None else T
+    batch = w.batch if batch is None else batch
+    dev = w.gen_device if device is None else device
+    dt = DTYPES[w.dtype]
+    shape = (batch, T, w.H, w.d)
+    q = normal(shape, w.seed, 0, w.scale, dt, dev)
+    k = normal(shape, w.seed, 1, w.scale, dt, dev)
+    v = normal(shape, w.seed, 2, w.scale, dt, dev)
+    gate = w.gated if with_gate is None else with_gate
+    x = normal((batch, T, w.H * w.d), w.seed, 3, 1.0, dt, dev) if gate else None
+    return q, k, v, x
+
+
+def varlen_inputs(w: Workload, total_T: int | None = None, device: str | None = None):
+    """Packed q, k, v [total_T, H, d], x [total_T, H*d] and cu_seqlens (int32,
+    CPU) for a varlen workload."""
+    total = w.total_T if total_T is None else total_T
+    dev = w.gen_device if device is None else device
+    dt = DTYPES[w.dtype]
+    lengths = varlen_lengths(w.seed, total)
+    cu = cu_from_lengths(lengths)
+    shape = (total, w.H, w.d)
+    q = normal(shape, w.seed, 0, w.scale, dt, dev)
+    k = normal(shape, w.seed, 1, w.scale, dt, dev)
+    v = normal(shape, w.seed, 2, w.scale, dt, dev)
+    x = normal((total, w.H * w.d), w.seed, 3, 1.0, dt, dev) if w.gated else None
+    return q, k, v, x, cu
+
+
+def decode_state(w: Workload, N: int | None = None, H: int | None = None, device=None):
+    """Initial fp32 state S [N, H, d, d] and normaliser z [N, H, d], N(0, std)."""
+    N = w.N if N is None else N
+    H = w.H if H is None else H
+    dev = w.gen_device if device is None else device
+    S = normal((N, H, w.d, w.d), w.seed, 4, w.state_std, torch.float32, dev)
+    z = normal((N, H, w.d), w.seed, 5, w.state_std, torch.float32, dev)
+    return S, z
+
+
+def decode_token(w: Workload, step: int, N: int | None = None, H: int | None = None,
+                 device=None):
+    """Pre-activation q, k, v [N, H, d] of decode step ``step``."""
+    N = w.N if N is None else N
+    H = w.H if H is None else H
+    dev = w.gen_device if device is None else device
+    dt = DTYPES[w.dtype]
+    g = _gen(w.seed, 100 + step, dev)
+    t = torch.randn((3, N, H, w.d), generator=g, dtype=torch.float32, device=dev)
+    if w.scale != 1.0:
+        t.mul_(float(w.scale))
+    t = t.to(dt)
+    return t[0], t[1], t[2]
