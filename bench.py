@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning-Attention forward path on one MI355X.
+
+One step = one gated bf16 prefill of the long-context workload
+(B=1, T=1,048,576 tokens, 8 heads, head dim 128, RMSNorm*sigmoid gate):
+feature map, blocking, chunk states and prefix, intra- and inter-block
+products, state carry and the fused gate, i.e. every stage of the path, on
+seeded synthetic inputs already resident in HBM.  The same run also times
+the decode step (64 sequences x 64 heads x d=128, fp32 state, 1000 steps)
+and the CPU oracle on a bounded sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix-core peak, TFLOP/s
+METRIC = "Lightning-attn prefill tokens/s + % bf16 MFMA peak; decode HBM GB/s"
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw HIP events (libamdhip64) so the library can record them on its stream."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = ev.value
+        self.n = n
+
+    def ptr(self, offset: int = 0) -> ctypes.c_void_p:
+        return ctypes.c_void_p(ctypes.addressof(self.arr) + offset * ctypes.sizeof(ctypes.c_void_p))
+
+    def record(self, i: int, stream: int) -> None:
+        self.hip.hipEventRecord(ctypes.c_void_p(self.arr[i]), ctypes.c_void_p(stream))
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        self.hip.hipEventSynchronize(ctypes.c_void_p(self.arr[b]))
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.arr[a]),
+                                        ctypes.c_void_p(self.arr[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def bench_prefill(args, torch, lib, _lib, inputs):
+    w = inputs.WORKLOADS[args.workload]
+    T, H, d = w.T, w.H, w.d
+    log("generating %s inputs on the GPU (%s)" % (w.name, w.note))
+    q, k, v, x = inputs.prefill_inputs(w, device="cuda")
+    dev = q.device
+    out = torch.empty((1, T, H * d), dtype=torch.float32, device=dev)
+    state_out = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+    opt = _lib.options(block_size=64, gated=True)
+    nbytes = lib.la_prefill_workspace_bytes(1, T, H, d, _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32,
+                                            ctypes.byref(opt))
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+    chunk = lib.la_prefill_chunk_tokens(1, T, T, H, d, _lib.LA_DTYPE_BF16, ctypes.byref(opt))
+    chunked = T > chunk
+    names = (["chunk_state", "chunk_scan"] if chunked else []) + ["main", "gate"]
+    nk = len(names)
+    K, W = args.steps, args.warmup
+    ev = HipEvents(2 * nk * (K + W))
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        opt.timing_events = ev.ptr(2 * nk * i)
+        opt.n_timing = nk
+        st = lib.la_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), x.data_ptr(), None, None,
+                            None, out.data_ptr(), state_out.data_ptr(), None, 1, T, H, d,
+                            _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32, ctypes.byref(opt),
+                            ws.data_ptr(), ws.numel(), ctypes.c_void_p(stream))
+        _lib.check(st, "la_prefill")
+
+    log("prefill: chunk %d tokens, kernels %s; %d warmup + %d timed steps" % (chunk, names, W, K))
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    per_kernel = {}
+    for j, name in enumerate(names):
+        tot = 0.0
+        for i in range(W, W + K):
+            base = 2 * nk * i
+            tot += ev.elapsed_ms(base + 2 * j, base + 2 * j + 1)
+        per_kernel[name] = tot / K
+    log("prefill: %.3f ms/step; kernels (ms): %s" %
+        (ms_step, ", ".join("%s %.3f" % kv for kv in per_kernel.items())))
+    th = T * H
+    res = {
+        "T": T, "H": H, "d": d, "chunk": chunk, "ms_per_step": ms_step,
+        "tokens_per_s": T / (ms_step * 1e-3), "per_kernel_ms": per_kernel, "token_heads": th,
+    }
+    del q, k, v, x, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, torch, lib, _lib, inputs):
+    w = inputs.WORKLOADS["decode_64x64"]
+    N, H, d, steps = w.N, w.H, w.d, args.decode_steps
+    log("decode: generating state and %d steps of tokens on the GPU" % steps)
+    S, z = inputs.decode_state(w, device="cuda")
+    toks = [inputs.decode_token(w, s, device="cuda") for s in range(steps)]
+    out = torch.empty((N, H * d), dtype=torch.float32, device="cuda")
+    opt = _lib.options(block_size=64)
+    ev = HipEvents(2 * steps + 2)
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for normalized in (False, True):
+        opt.normalized = int(normalized)
+        zz = z if normalized else None
+
+        def call(s, timed):
+            qs, ks, vs = toks[s]
+            opt.timing_events = ev.ptr(2 * s) if timed else None
+            opt.n_timing = 1 if timed else 0
+            st = lib.la_decode_step(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), None, None,
+                                    S.data_ptr(), None if zz is None else zz.data_ptr(),
+                                    out.data_ptr(), N, H, d, _lib.LA_DTYPE_BF16,
+                                    _lib.LA_DTYPE_F32, ctypes.byref(opt), None, 0,
+                                    ctypes.c_void_p(stream))
+            _lib.check(st, "la_decode_step")
+
+        for s in range(min(10, steps)):
+            call(s, False)
+        torch.cuda.synchronize()
+        ev.record(2 * steps, stream)
+        t0 = time.perf_counter()
+        for s in range(steps):
+            call(s, True)
+        ev.record(2 * steps + 1, stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        kern = sum(ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)) / steps
+        loop = ev.elapsed_ms(2 * steps, 2 * steps + 1) / steps
+        # algorithmic bytes per step: S read + write, z read + write, q/k/v in, y out
+        nbytes = 2 * N * H * d * d * 4 + 3 * N * H * d * 2 + N * H * d * 4
+        if normalized:
+            nbytes += 2 * N * H * d * 4
+        key = "normalized" if normalized else "plain"
+        res[key] = {
+            "kernel_us": kern * 1e3, "loop_us_per_step": loop * 1e3,
+            "wall_us_per_step": (t1 - t0) * 1e6 / steps, "bytes_per_step": nbytes,
+            "GBps": nbytes / (kern * 1e-3) / 1e9, "hbm_frac": nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        log("decode %s: kernel %.1f us/step (%.0f GB/s), loop %.1f us/step" %
+            (key, kern * 1e3, res[key]["GBps"], loop * 1e3))
+    del toks, S, z
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, inputs):
+    """The oracle (plain fp64 C) on the first tokens of the same workload."""
+    import torch
+
+    from oracle import oracle as O
+
+    w = inputs.WORKLOADS[args.workload]
+    T = args.cpu_tokens
+    q, k, v, x = inputs.prefill_inputs(w, T=T, device="cuda")
+    q, k, v, x = (t.cpu() for t in (q, k, v, x))
+    torch.cuda.synchronize()
+    threads = min(os.cpu_count() or 1, w.H)
+    log("cpu baseline: oracle on %d tokens x %d heads with %d threads" % (T, w.H, threads))
+    t0 = time.perf_counter()
+    O.forward(q[0], k[0], v[0], x[0], gated=True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    log("cpu baseline: %.2f s -> %.0f tokens/s" % (dt, T / dt))
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d tokens of the %s workload, all %d heads, gated; fp64 "
+                      "token-by-token recurrence; %.1f s" % (T, w.name, w.H, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_1m", choices=["prefill_1m", "prefill_32k"])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=262144)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the path shards by head or sequence with no collective; see the design "
+              "notes).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_long_amd import _lib, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    lib = _lib.load()
+    log("device: %s" % torch.cuda.get_device_name(0))
+
+    pre = bench_prefill(args, torch, lib, _lib, inputs)
+    dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, inputs)
+
+    th = pre["token_heads"]
+    main_ms = pre["per_kernel_ms"]["main"]
+    # main pass: reads q, k, v (3 x 256 B bf16) and writes fp32 Y (512 B) per token-head
+    main_bytes = th * (3 * 256 + 512)
+    main_gbs = main_bytes / (main_ms * 1e-3) / 1e9
+    # whole path, minimal traffic: q, k, v, x in (bf16) and fp32 out = 1536 B per token-head
+    path_bytes = th * 1536
+    path_gbs = path_bytes / (pre["ms_per_step"] * 1e-3) / 1e9
+    # algorithmic flops per token-head at block 64, d 128: intra 2(B+1)d + inter 2d^2 + state 2d^2
+    B, d = 64, pre["d"]
+    flops = th * (2 * (B + 1) * d + 4 * d * d)
+    tflops = flops / (pre["ms_per_step"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: bf16 q/k/v N(0,1)/sqrt(128), B=1 T=%d H=%d d=%d, block 64, "
+                               "fp32 state carry, RMSNorm*sigmoid gate, fp32 out"
+                               % (args.workload, pre["T"], pre["H"], pre["d"]),
+                   "global_batch": 1, "seq_len": pre["T"], "heads": pre["H"], "head_dim": pre["d"],
+                   "block": 64, "chunk_tokens": pre["chunk"]},
+        "roofline": {"bound": "hbm", "kernel": "main pass (k_prefill_main)",
+                     "achieved": main_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": main_gbs / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+        "prefill": {"per_kernel_ms": pre["per_kernel_ms"], "path_min_bytes_GBps": path_gbs,
+                    "path_hbm_roofline_frac": path_gbs / HBM_PEAK_GBS,
+                    "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS},
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -80,7 +80,17 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *   rms_eps     epsilon inside the square root (default 1e-6).
  *   chunk_tokens tokens per independently scheduled chunk of one sequence
  *               (multiple of 64); 0 = chosen by the library.  Changes fp32
- *               rounding order only.                                          */
+ *               rounding order only.
+ *   timing_events, n_timing
+ *               instrumentation: NULL/0, or an array of 2*n_timing hipEvent_t
+ *               handles (created by the caller).  The library records
+ *               events[2i] just before and events[2i+1] just after the i-th
+ *               kernel it launches on hip_stream, for i < n_timing.  Launch
+ *               order of la_prefill / la_prefill_varlen: [chunk planner]
+ *               (varlen only), [state copy] (zero-length input, or varlen
+ *               whose sequences each fit one chunk), [chunk-state, chunk
+ *               scan] (when a sequence spans several chunks), main pass,
+ *               [gate] (gated).  la_decode_step: decode, [gate].             */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -88,6 +98,8 @@ typedef struct {
     int32_t norm_group;
     float rms_eps;
     int32_t chunk_tokens;
+    void* timing_events;
+    int32_t n_timing;
 } la_options_t;
 
 la_options_t la_default_options(void);
@@ -103,7 +115,7 @@ la_options_t la_default_options(void);
  *   state_out   [Bt, H, d, d] fp32 final state, or NULL
  *   z_out       [Bt, H, d] fp32 final normaliser, or NULL
  *   Bt >= 1, T >= 0 (T = 0 only copies state_in to state_out), H >= 1,
- *   d in {64, 128}.  Total elements Bt*T*H*d must be < 2^31 * 64.
+ *   d in {64, 128}, Bt*T < 2^31, H*d <= 2^20.
  *   workspace   device scratch of at least
  *               la_prefill_workspace_bytes(Bt, T, H, d, opt) bytes, 256-byte
  *               aligned (may be NULL when that size is 0).                    */

@@ -1,0 +1,122 @@
+"""ctypes view of liblinattn.so (the C ABI declared in include/la.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
+
+LA_OK = 0
+LA_ERR_INVALID_ARGUMENT = 1
+LA_ERR_UNSUPPORTED = 2
+LA_ERR_WORKSPACE_TOO_SMALL = 3
+LA_ERR_HIP = 4
+
+LA_DTYPE_F32 = 0
+LA_DTYPE_BF16 = 1
+
+# every extern "C" function declared in include/la.h
+EXPORTS = (
+    "la_default_options",
+    "la_prefill",
+    "la_prefill_varlen",
+    "la_decode_step",
+    "la_prefill_workspace_bytes",
+    "la_prefill_varlen_workspace_bytes",
+    "la_decode_workspace_bytes",
+    "la_prefill_chunk_tokens",
+    "la_status_string",
+)
+
+
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("block_size", ctypes.c_int32),
+        ("normalized", ctypes.c_int32),
+        ("gated", ctypes.c_int32),
+        ("norm_group", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("chunk_tokens", ctypes.c_int32),
+        ("timing_events", ctypes.c_void_p),
+        ("n_timing", ctypes.c_int32),
+    ]
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+_lock = threading.Lock()
+_lib = None
+
+_vp = ctypes.c_void_p
+_fp = ctypes.c_void_p  # float* passed as raw addresses
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_optp = ctypes.POINTER(Options)
+
+
+def load() -> ctypes.CDLL:
+    """Load liblinattn.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("liblinattn.so is not built (expected at %s); run "
+                               "`python -m linear_attention_long_amd.build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.la_default_options.restype = Options
+        lib.la_default_options.argtypes = []
+        lib.la_status_string.restype = ctypes.c_char_p
+        lib.la_status_string.argtypes = [ctypes.c_int]
+        lib.la_prefill.restype = ctypes.c_int
+        lib.la_prefill.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _fp,
+                                   _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
+                                   _optp, _vp, _sz, _vp]
+        lib.la_prefill_varlen.restype = ctypes.c_int
+        lib.la_prefill_varlen.argtypes = [_vp, _vp, _vp, _vp, _fp, _vp, _i32, _i32, _i32,
+                                          _fp, _fp, _vp, _fp, _fp, _i32, _i32, ctypes.c_int,
+                                          ctypes.c_int, _optp, _vp, _sz, _vp]
+        lib.la_decode_step.restype = ctypes.c_int
+        lib.la_decode_step.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _vp, _i32, _i32, _i32,
+                                       ctypes.c_int, ctypes.c_int, _optp, _vp, _sz, _vp]
+        lib.la_prefill_workspace_bytes.restype = _sz
+        lib.la_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, ctypes.c_int,
+                                                   ctypes.c_int, _optp]
+        lib.la_prefill_varlen_workspace_bytes.restype = _sz
+        lib.la_prefill_varlen_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32,
+                                                          ctypes.c_int, ctypes.c_int, _optp]
+        lib.la_decode_workspace_bytes.restype = _sz
+        lib.la_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, ctypes.c_int, _optp]
+        lib.la_prefill_chunk_tokens.restype = _i32
+        lib.la_prefill_chunk_tokens.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.c_int, _optp]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().la_status_string(int(status)).decode()
+    except Exception:  # library missing: still give a message
+        return "status %d" % status
+
+
+def options(block_size=64, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
+            chunk_tokens=0) -> Options:
+    o = load().la_default_options()
+    o.block_size = int(block_size)
+    o.normalized = int(bool(normalized))
+    o.gated = int(bool(gated))
+    o.norm_group = int(norm_group)
+    o.rms_eps = float(rms_eps)
+    o.chunk_tokens = int(chunk_tokens)
+    return o
+
+
+def check(status: int, where: str) -> None:
+    if status != LA_OK:
+        raise LAError(status, where)

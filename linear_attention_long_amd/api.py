@@ -1,0 +1,150 @@
+"""Python entry points with the names of the C ABI: argument marshalling only.
+
+Every step of the computation runs in liblinattn's HIP kernels; torch supplies
+device memory (outputs and workspace) and the current stream.  If the library
+is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.LA_DTYPE_F32, torch.bfloat16: _lib.LA_DTYPE_BF16}
+
+
+def _dtype(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError("dtype %s not supported (float32 or bfloat16)" % t)
+    return _DT[t]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == ctypes.c_size_t(-1).value:
+        return None
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=False,
+               block_size=64, norm_group=0, rms_eps=1e-6, chunk_tokens=0,
+               out_dtype=torch.float32, return_state=True, stream=None):
+    """Prefill of Bt equal-length sequences.
+
+    q, k, v: [Bt, T, H, d] (or [T, H, d]) pre-activation, float32 or bfloat16.
+    x: gate pre-activation [Bt, T, H*d] (same dtype) -> gated output, or None.
+    w: RMSNorm weight [H*d] float32 or None.  state_in [Bt, H, d, d], z_in
+    [Bt, H, d] float32 or None.  Returns (out [Bt, T, H*d], state_out, z_out).
+    """
+    lib = _lib.load()
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
+        if x is not None:
+            x = x.unsqueeze(0)
+        if state_in is not None and state_in.dim() == 3:
+            state_in = state_in.unsqueeze(0)
+        if z_in is not None and z_in.dim() == 2:
+            z_in = z_in.unsqueeze(0)
+    Bt, T, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same shape and dtype")
+    gated = x is not None
+    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens)
+    in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
+    dev = q.device
+    out = torch.empty((Bt, T, H * d), dtype=out_dtype, device=dev)
+    state_out = torch.empty((Bt, H, d, d), dtype=torch.float32, device=dev) if return_state else None
+    z_out = (torch.empty((Bt, H, d), dtype=torch.float32, device=dev)
+             if (return_state and normalized) else None)
+    nbytes = lib.la_prefill_workspace_bytes(Bt, T, H, d, in_dt, out_dt, ctypes.byref(opt))
+    ws = _workspace(nbytes, dev)
+    st = lib.la_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(state_in), _ptr(z_in),
+                        _ptr(out), _ptr(state_out), _ptr(z_out), Bt, T, H, d, in_dt, out_dt,
+                        ctypes.byref(opt), _ptr(ws), 0 if ws is None else ws.numel(),
+                        _stream(stream))
+    _lib.check(st, "la_prefill")
+    if squeeze:
+        out = out[0]
+        state_out = None if state_out is None else state_out[0]
+        z_out = None if z_out is None else z_out[0]
+    return out, state_out, z_out
+
+
+def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=None, z_in=None,
+                      *, normalized=False, block_size=64, norm_group=0, rms_eps=1e-6,
+                      chunk_tokens=0, out_dtype=torch.float32, return_state=True, stream=None):
+    """Prefill of a packed batch.  q, k, v: [total_T, H, d]; cu_seqlens: int32
+    [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
+    Returns (out [total_T, H*d], state_out [num_seqs, H, d, d], z_out)."""
+    lib = _lib.load()
+    total_T, H, d = q.shape
+    num_seqs = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    gated = x is not None
+    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens)
+    in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
+    dev = q.device
+    out = torch.empty((total_T, H * d), dtype=out_dtype, device=dev)
+    state_out = (torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=dev)
+                 if return_state else None)
+    z_out = (torch.empty((num_seqs, H, d), dtype=torch.float32, device=dev)
+             if (return_state and normalized) else None)
+    nbytes = lib.la_prefill_varlen_workspace_bytes(total_T, num_seqs, int(max_seqlen), H, d,
+                                                   in_dt, out_dt, ctypes.byref(opt))
+    ws = _workspace(nbytes, dev)
+    st = lib.la_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(cu_seqlens),
+                               num_seqs, total_T, int(max_seqlen), _ptr(state_in), _ptr(z_in),
+                               _ptr(out), _ptr(state_out), _ptr(z_out), H, d, in_dt, out_dt,
+                               ctypes.byref(opt), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(stream))
+    _lib.check(st, "la_prefill_varlen")
+    return out, state_out, z_out
+
+
+def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, norm_group=0,
+                   rms_eps=1e-6, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+    """One decode token per sequence.  q, k, v: [N, H, d]; state [N, H, d, d]
+    float32 and z [N, H, d] (normalised mode) are updated in place.
+    Returns out [N, H*d].  ``out``/``workspace`` may be passed to reuse buffers."""
+    lib = _lib.load()
+    N, H, d = q.shape
+    gated = x is not None
+    opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0)
+    in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
+    if out is None:
+        out = torch.empty((N, H * d), dtype=out_dtype, device=q.device)
+    if workspace is None:
+        nbytes = lib.la_decode_workspace_bytes(N, H, d, out_dt, ctypes.byref(opt))
+        workspace = _workspace(nbytes, q.device)
+    st = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(state), _ptr(z),
+                            _ptr(out), N, H, d, in_dt, out_dt, ctypes.byref(opt),
+                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            _stream(stream))
+    _lib.check(st, "la_decode_step")
+    return out
+
+
+# the same calls under short names
+prefill = la_prefill
+prefill_varlen = la_prefill_varlen
+decode_step = la_decode_step

@@ -1,0 +1,501 @@
+// la_api.hip -- the C ABI of liblinattn (declared in include/la.h): host-side
+// validation, planning of chunks and workspace, and kernel launches.
+//
+// Every argument check runs on the host before the first HIP call, so a
+// rejected call has no side effects.  The library allocates nothing.
+#include "la.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <type_traits>
+
+#include "la_kernels_aux.h"
+#include "la_kernels_mfma.h"
+#include "la_kernels_valu.h"
+
+using namespace la;
+
+namespace {
+
+constexpr int kDefaultBlock = 64;
+constexpr int kMinAutoChunk = 1024;
+constexpr int kMaxAutoChunk = 16384;
+constexpr int64_t kTargetItems = 1024;  // (chunk, head) workgroups aimed for: ~4 per CU
+
+struct Opts {
+    int block;
+    bool normalized;
+    bool gated;
+    int group;      // RMSNorm group width (features)
+    float eps;
+    int chunk;      // requested chunk tokens (0 = auto)
+    hipEvent_t* events;
+    int n_events;
+};
+
+// Records the caller's timing events around each launched kernel.
+struct Timer {
+    hipEvent_t* ev;
+    int n;
+    int i = 0;
+    hipStream_t st;
+    Timer(const Opts& o, hipStream_t s) : ev(o.events), n(o.n_events), st(s) {}
+    void before() {
+        if (ev && i < n) (void)hipEventRecord(ev[2 * i], st);
+    }
+    void after() {
+        if (ev && i < n) (void)hipEventRecord(ev[2 * i + 1], st);
+        ++i;
+    }
+};
+
+struct Plan {
+    bool mfma;         // bf16, d = 128, block 64: matrix-core kernels
+    bool chunked;      // some sequence spans more than one chunk
+    bool varlen;
+    int C;             // tokens per chunk
+    int64_t items;     // grid size bound in chunks
+    int64_t stride;    // floats per (item, head) in the state buffer
+    size_t off_chunk_off, off_buf, off_y, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+inline size_t dtype_size(la_dtype_t t) { return t == LA_DTYPE_BF16 ? 2 : 4; }
+inline bool dtype_ok(la_dtype_t t) { return t == LA_DTYPE_F32 || t == LA_DTYPE_BF16; }
+
+la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
+    const la_options_t def = la_default_options();
+    const la_options_t& x = opt ? *opt : def;
+    o.block = x.block_size == 0 ? kDefaultBlock : x.block_size;
+    if (o.block != 32 && o.block != 64 && o.block != 128 && o.block != 256) return LA_ERR_UNSUPPORTED;
+    if (x.normalized != 0 && x.normalized != 1) return LA_ERR_INVALID_ARGUMENT;
+    if (x.gated != 0 && x.gated != 1) return LA_ERR_INVALID_ARGUMENT;
+    o.normalized = x.normalized == 1;
+    o.gated = x.gated == 1;
+    const int F = H * d;
+    o.group = x.norm_group == 0 ? F : x.norm_group;
+    if (o.group <= 0 || o.group % 64 != 0 || F % o.group != 0) return LA_ERR_INVALID_ARGUMENT;
+    if (!(x.rms_eps >= 0.f) || !std::isfinite(x.rms_eps)) return LA_ERR_INVALID_ARGUMENT;
+    o.eps = x.rms_eps;
+    if (x.chunk_tokens < 0 || x.chunk_tokens % 64 != 0) return LA_ERR_INVALID_ARGUMENT;
+    o.chunk = x.chunk_tokens;
+    if (x.n_timing < 0 || (x.n_timing > 0 && !x.timing_events)) return LA_ERR_INVALID_ARGUMENT;
+    o.events = (hipEvent_t*)x.timing_events;
+    o.n_events = x.timing_events ? x.n_timing : 0;
+    return LA_OK;
+}
+
+la_status_t check_shape(int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype) {
+    if (H < 1 || d < 1) return LA_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if ((int64_t)H * d > (1 << 20)) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+int auto_chunk(int64_t total_T, int H, int max_seqlen, const Opts& o) {
+    if (o.chunk) return o.chunk;
+    int64_t C = (total_T * H + kTargetItems - 1) / kTargetItems;
+    C = (C + 63) / 64 * 64;
+    if (C < kMinAutoChunk) C = kMinAutoChunk;
+    if (C > kMaxAutoChunk) C = kMaxAutoChunk;
+    (void)max_seqlen;
+    return (int)C;
+}
+
+Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqlen, int H, int d,
+               la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o) {
+    Plan p{};
+    p.varlen = varlen;
+    p.mfma = in_dtype == LA_DTYPE_BF16 && d == 128 && o.block == 64;
+    p.C = auto_chunk(total_T, H, (int)max_seqlen, o);
+    p.chunked = max_seqlen > p.C;
+    if (!p.chunked) {
+        // one chunk per sequence: the chunk length only has to cover it
+        int64_t c = (max_seqlen + 63) / 64 * 64;
+        p.C = (int)(c < 64 ? 64 : c);
+    }
+    if (varlen) p.items = total_T / p.C + num_seqs;
+    else p.items = num_seqs * ((max_seqlen + p.C - 1) / p.C);
+    p.stride = (int64_t)d * d + (o.normalized ? d : 0);
+    size_t off = 0;
+    p.off_chunk_off = off;
+    if (varlen) off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    p.off_buf = off;
+    if (p.chunked) off += align256((size_t)p.items * H * p.stride * sizeof(float));
+    p.off_y = off;
+    if (o.gated && out_dtype != LA_DTYPE_F32) off += align256((size_t)total_T * H * d * sizeof(float));
+    p.total = off;
+    return p;
+}
+
+template <typename InT, typename OutT>
+la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, const void* k,
+                                 const void* v, const void* x, const float* w,
+                                 const int32_t* cu, int32_t nseq, int32_t T, int64_t total_T,
+                                 const float* state_in, const float* z_in, void* out,
+                                 float* state_out, float* z_out, int H, int d, char* ws,
+                                 hipStream_t st) {
+    Timer tm(o, st);
+    ItemMap map{};
+    map.nseq = nseq;
+    map.C = p.C;
+    if (p.varlen) {
+        map.cu = cu;
+        map.chunk_off = (int32_t*)(ws + p.off_chunk_off);
+        tm.before();
+        k_plan_chunks<<<1, 256, 0, st>>>(cu, nseq, p.C, (int32_t*)(ws + p.off_chunk_off));
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+    } else {
+        map.T = T;
+        map.cps = (T + p.C - 1) / p.C;
+    }
+    const int64_t nS = (int64_t)nseq * H * d * d, nz = (int64_t)nseq * H * d;
+    if (total_T == 0 || (p.varlen && !p.chunked)) {
+        // zero-length sequences keep their state; others are overwritten below
+        if (state_out || z_out) {
+            const int64_t n = nS;
+            tm.before();
+            k_fill_state<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+                state_in, z_in, state_out, o.normalized ? z_out : nullptr, nS, nz);
+            if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+            tm.after();
+        }
+        if (total_T == 0) return LA_OK;
+    }
+    const bool need_yws = o.gated && !std::is_same<OutT, float>::value;
+    float* ybuf_f = need_yws ? (float*)(ws + p.off_y) : nullptr;
+    float* buf = p.chunked ? (float*)(ws + p.off_buf) : nullptr;
+    const dim3 grid((unsigned)p.items, (unsigned)H);
+    const bool norm = o.normalized;
+
+    if (p.chunked) {
+        tm.before();
+        if (p.mfma) {
+            if (norm) mf::k_chunk_state<true><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            else mf::k_chunk_state<false><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+        } else if (d == 128) {
+            if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+            else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+        } else {
+            if (norm) vk::k_valu_state<64, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+            else vk::k_valu_state<64, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+        }
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+        const int E = (int)p.stride;
+        const int nblk = (E + 255) / 256;
+        tm.before();
+        k_chunk_scan<<<dim3((unsigned)nblk, (unsigned)H, (unsigned)nseq), 256, 0, st>>>(
+            buf, p.stride, map, H, d, E, state_in, norm ? z_in : nullptr, state_out,
+            norm ? z_out : nullptr);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+    }
+
+    // main pass: Y in the output dtype, or fp32 (out itself when fp32) when gated
+    void* ydst = o.gated ? (need_yws ? (void*)ybuf_f : out) : out;
+    const bool y_is_f32 = o.gated || std::is_same<OutT, float>::value;
+    tm.before();
+    if (p.mfma) {
+        const uint16_t* qb = (const uint16_t*)q;
+        const uint16_t* kb = (const uint16_t*)k;
+        const uint16_t* vb = (const uint16_t*)v;
+        if (y_is_f32) {
+            if (norm) mf::k_prefill_main<true, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out);
+            else mf::k_prefill_main<false, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, nullptr);
+        } else {
+            if (norm) mf::k_prefill_main<true, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out);
+            else mf::k_prefill_main<false, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, nullptr);
+        }
+    } else {
+#define LA_VALU_MAIN(DD, YT, NN)                                                                \
+    vk::k_valu_main<DD, InT, YT, NN><<<grid, vk::NT, 0, st>>>(                                  \
+        (const InT*)q, (const InT*)k, (const InT*)v, map, H, o.block, buf, p.stride, state_in,  \
+        z_in, (YT*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out)
+        if (d == 128) {
+            if (y_is_f32) { if (norm) LA_VALU_MAIN(128, float, true); else LA_VALU_MAIN(128, float, false); }
+            else { if (norm) LA_VALU_MAIN(128, uint16_t, true); else LA_VALU_MAIN(128, uint16_t, false); }
+        } else {
+            if (y_is_f32) { if (norm) LA_VALU_MAIN(64, float, true); else LA_VALU_MAIN(64, float, false); }
+            else { if (norm) LA_VALU_MAIN(64, uint16_t, true); else LA_VALU_MAIN(64, uint16_t, false); }
+        }
+#undef LA_VALU_MAIN
+    }
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    tm.after();
+
+    if (o.gated) {
+        const int F = H * d;
+        const int64_t units = total_T * (F / o.group);
+        const unsigned blocks = (unsigned)((units + 3) / 4);
+        const float* yf = need_yws ? ybuf_f : (const float*)out;
+        tm.before();
+        if (o.group % 256 == 0) k_gate4<InT, OutT><<<blocks, 256, 0, st>>>(yf, (const InT*)x, w, (OutT*)out, total_T, F, o.group, o.eps);
+        else k_gate<InT, OutT><<<blocks, 256, 0, st>>>(yf, (const InT*)x, w, (OutT*)out, total_T, F, o.group, o.eps);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+    }
+    return LA_OK;
+}
+
+la_status_t launch_prefill(const Plan& p, const Opts& o, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                           const void* q, const void* k, const void* v, const void* x,
+                           const float* w, const int32_t* cu, int32_t nseq, int32_t T,
+                           int64_t total_T, const float* state_in, const float* z_in, void* out,
+                           float* state_out, float* z_out, int H, int d, char* ws, hipStream_t st) {
+    if (in_dtype == LA_DTYPE_BF16) {
+        if (out_dtype == LA_DTYPE_BF16)
+            return launch_prefill_typed<uint16_t, uint16_t>(p, o, q, k, v, x, w, cu, nseq, T, total_T, state_in, z_in, out, state_out, z_out, H, d, ws, st);
+        return launch_prefill_typed<uint16_t, float>(p, o, q, k, v, x, w, cu, nseq, T, total_T, state_in, z_in, out, state_out, z_out, H, d, ws, st);
+    }
+    if (out_dtype == LA_DTYPE_BF16)
+        return launch_prefill_typed<float, uint16_t>(p, o, q, k, v, x, w, cu, nseq, T, total_T, state_in, z_in, out, state_out, z_out, H, d, ws, st);
+    return launch_prefill_typed<float, float>(p, o, q, k, v, x, w, cu, nseq, T, total_T, state_in, z_in, out, state_out, z_out, H, d, ws, st);
+}
+
+// Checks shared by both prefill entry points.
+la_status_t check_prefill_common(const void* q, const void* k, const void* v, const void* x_gate,
+                                 const float* rms_weight, const float* state_in, const float* z_in,
+                                 void* out, float* state_out, float* z_out, int64_t nseq,
+                                 int64_t total_T, int H, int d, la_dtype_t in_dtype,
+                                 la_dtype_t out_dtype, const Opts& o) {
+    if (!q || !k || !v || !out) return LA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return LA_ERR_INVALID_ARGUMENT;
+    if (o.gated && (!x_gate || !aligned(x_gate, 16))) return LA_ERR_INVALID_ARGUMENT;
+    if (rms_weight && !aligned(rms_weight, 16)) return LA_ERR_INVALID_ARGUMENT;
+    if (!o.normalized && (z_in || z_out)) return LA_ERR_INVALID_ARGUMENT;
+    const void* st_ptrs[4] = {state_in, z_in, state_out, z_out};
+    for (const void* sp : st_ptrs)
+        if (sp && !aligned(sp, 16)) return LA_ERR_INVALID_ARGUMENT;
+    const size_t in_bytes = (size_t)total_T * H * d * dtype_size(in_dtype);
+    const size_t out_bytes = (size_t)total_T * H * d * dtype_size(out_dtype);
+    const size_t s_bytes = (size_t)nseq * H * d * d * sizeof(float);
+    const size_t z_bytes = (size_t)nseq * H * d * sizeof(float);
+    const void* ins[4] = {q, k, v, o.gated ? x_gate : nullptr};
+    for (const void* ip : ins)
+        if (overlap(out, out_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
+    if (overlap(out, out_bytes, state_out, s_bytes) || overlap(out, out_bytes, state_in, s_bytes))
+        return LA_ERR_INVALID_ARGUMENT;
+    if (state_out && state_in && state_out != state_in && overlap(state_out, s_bytes, state_in, s_bytes))
+        return LA_ERR_INVALID_ARGUMENT;
+    if (z_out && z_in && z_out != z_in && overlap(z_out, z_bytes, z_in, z_bytes))
+        return LA_ERR_INVALID_ARGUMENT;
+    if (state_out && overlap(state_out, s_bytes, z_out, z_bytes)) return LA_ERR_INVALID_ARGUMENT;
+    return LA_OK;
+}
+
+la_status_t check_workspace(const Plan& p, void* ws, size_t ws_bytes) {
+    if (p.total == 0) return LA_OK;
+    if (!ws || !aligned(ws, 256)) return LA_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < p.total) return LA_ERR_WORKSPACE_TOO_SMALL;
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_options_t la_default_options(void) {
+    la_options_t o;
+    o.block_size = kDefaultBlock;
+    o.normalized = 0;
+    o.gated = 0;
+    o.norm_group = 0;
+    o.rms_eps = 1e-6f;
+    o.chunk_tokens = 0;
+    o.timing_events = nullptr;
+    o.n_timing = 0;
+    return o;
+}
+
+const char* la_status_string(la_status_t s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case LA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case LA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t la_prefill_workspace_bytes(int32_t Bt, int32_t T, int32_t H, int32_t d, la_dtype_t in_dtype,
+                                  la_dtype_t out_dtype, const la_options_t* opt) {
+    Opts o;
+    if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return (size_t)-1;
+    if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
+    if (parse_options(opt, H, d, o) != LA_OK) return (size_t)-1;
+    return make_plan(false, Bt, (int64_t)Bt * T, T, H, d, in_dtype, out_dtype, o).total;
+}
+
+size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int32_t max_seqlen,
+                                         int32_t H, int32_t d, la_dtype_t in_dtype,
+                                         la_dtype_t out_dtype, const la_options_t* opt) {
+    Opts o;
+    if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T) return (size_t)-1;
+    if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
+    if (parse_options(opt, H, d, o) != LA_OK) return (size_t)-1;
+    return make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o).total;
+}
+
+size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out_dtype,
+                                 const la_options_t* opt) {
+    Opts o;
+    if (N < 0) return (size_t)-1;
+    if (check_shape(H, d, LA_DTYPE_BF16, out_dtype) != LA_OK) return (size_t)-1;
+    if (parse_options(opt, H, d, o) != LA_OK) return (size_t)-1;
+    if (o.gated && out_dtype != LA_DTYPE_F32) return align256((size_t)N * H * d * sizeof(float));
+    return 0;
+}
+
+int32_t la_prefill_chunk_tokens(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
+                                int32_t d, la_dtype_t in_dtype, const la_options_t* opt) {
+    Opts o;
+    if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T) return -1;
+    if (check_shape(H, d, in_dtype, LA_DTYPE_F32) != LA_OK) return -1;
+    if (parse_options(opt, H, d, o) != LA_OK) return -1;
+    return make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, LA_DTYPE_F32, o).C;
+}
+
+la_status_t la_prefill(const void* q, const void* k, const void* v, const void* x_gate,
+                       const float* rms_weight, const float* state_in, const float* z_in,
+                       void* out, float* state_out, float* z_out, int32_t Bt, int32_t T, int32_t H,
+                       int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                       const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
+    if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return LA_ERR_INVALID_ARGUMENT;
+    Opts o;
+    s = parse_options(opt, H, d, o);
+    if (s != LA_OK) return s;
+    const int64_t total_T = (int64_t)Bt * T;
+    s = check_prefill_common(q, k, v, x_gate, rms_weight, state_in, z_in, out, state_out, z_out, Bt,
+                             total_T, H, d, in_dtype, out_dtype, o);
+    if (s != LA_OK) return s;
+    const Plan p = make_plan(false, Bt, total_T, T, H, d, in_dtype, out_dtype, o);
+    s = check_workspace(p, workspace, workspace_bytes);
+    if (s != LA_OK) return s;
+    return launch_prefill(p, o, in_dtype, out_dtype, q, k, v, x_gate, rms_weight, nullptr, Bt, T,
+                          total_T, state_in, z_in, out, state_out, z_out, H, d, (char*)workspace,
+                          (hipStream_t)hip_stream);
+}
+
+la_status_t la_prefill_varlen(const void* q, const void* k, const void* v, const void* x_gate,
+                              const float* rms_weight, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t total_T, int32_t max_seqlen, const float* state_in,
+                              const float* z_in, void* out, float* state_out, float* z_out,
+                              int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                              const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
+    if (!cu_seqlens || !aligned(cu_seqlens, 4) || num_seqs < 1 || total_T < 0 || max_seqlen < 0 ||
+        max_seqlen > total_T)
+        return LA_ERR_INVALID_ARGUMENT;
+    Opts o;
+    s = parse_options(opt, H, d, o);
+    if (s != LA_OK) return s;
+    s = check_prefill_common(q, k, v, x_gate, rms_weight, state_in, z_in, out, state_out, z_out,
+                             num_seqs, total_T, H, d, in_dtype, out_dtype, o);
+    if (s != LA_OK) return s;
+    const Plan p = make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o);
+    s = check_workspace(p, workspace, workspace_bytes);
+    if (s != LA_OK) return s;
+    return launch_prefill(p, o, in_dtype, out_dtype, q, k, v, x_gate, rms_weight, cu_seqlens,
+                          num_seqs, 0, total_T, state_in, z_in, out, state_out, z_out, H, d,
+                          (char*)workspace, (hipStream_t)hip_stream);
+}
+
+la_status_t la_decode_step(const void* q, const void* k, const void* v, const void* x_gate,
+                           const float* rms_weight, float* state, float* z, void* out, int32_t N,
+                           int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                           const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
+    if (N < 0) return LA_ERR_INVALID_ARGUMENT;
+    Opts o;
+    s = parse_options(opt, H, d, o);
+    if (s != LA_OK) return s;
+    if (!q || !k || !v || !state || !out) return LA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(out, 16))
+        return LA_ERR_INVALID_ARGUMENT;
+    if (o.normalized && (!z || !aligned(z, 16))) return LA_ERR_INVALID_ARGUMENT;
+    if (!o.normalized && z) return LA_ERR_INVALID_ARGUMENT;
+    if (o.gated && (!x_gate || !aligned(x_gate, 16))) return LA_ERR_INVALID_ARGUMENT;
+    if (rms_weight && !aligned(rms_weight, 16)) return LA_ERR_INVALID_ARGUMENT;
+    const size_t in_bytes = (size_t)N * H * d * dtype_size(in_dtype);
+    const size_t out_bytes = (size_t)N * H * d * dtype_size(out_dtype);
+    const size_t s_bytes = (size_t)N * H * d * d * sizeof(float);
+    const void* ins[4] = {q, k, v, o.gated ? x_gate : nullptr};
+    for (const void* ip : ins) {
+        if (overlap(out, out_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
+        if (overlap(state, s_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
+    }
+    if (overlap(out, out_bytes, state, s_bytes)) return LA_ERR_INVALID_ARGUMENT;
+    if (z && (overlap(out, out_bytes, z, (size_t)N * H * d * 4) || overlap(state, s_bytes, z, (size_t)N * H * d * 4)))
+        return LA_ERR_INVALID_ARGUMENT;
+    const size_t need = (o.gated && out_dtype != LA_DTYPE_F32) ? align256((size_t)N * H * d * sizeof(float)) : 0;
+    if (need) {
+        if (!workspace || !aligned(workspace, 256)) return LA_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < need) return LA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    if (N == 0) return LA_OK;
+    hipStream_t st = (hipStream_t)hip_stream;
+    Timer tm(o, st);
+    void* ydst = o.gated ? (need ? workspace : out) : out;
+    const bool yf32 = o.gated || out_dtype == LA_DTYPE_F32;
+    const unsigned grid = (unsigned)((int64_t)N * H);
+#define LA_DEC(DD, IT, OT, NN) \
+    k_decode<DD, IT, OT, NN><<<grid, 256, 0, st>>>((const IT*)q, (const IT*)k, (const IT*)v, state, z, (OT*)ydst)
+#define LA_DEC_OUT(DD, IT)                                                                  \
+    do {                                                                                    \
+        if (yf32) { if (o.normalized) LA_DEC(DD, IT, float, true); else LA_DEC(DD, IT, float, false); } \
+        else { if (o.normalized) LA_DEC(DD, IT, uint16_t, true); else LA_DEC(DD, IT, uint16_t, false); } \
+    } while (0)
+    tm.before();
+    if (in_dtype == LA_DTYPE_BF16) {
+        if (d == 128) LA_DEC_OUT(128, uint16_t); else LA_DEC_OUT(64, uint16_t);
+    } else {
+        if (d == 128) LA_DEC_OUT(128, float); else LA_DEC_OUT(64, float);
+    }
+#undef LA_DEC_OUT
+#undef LA_DEC
+    if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+    tm.after();
+    if (o.gated) {
+        const int F = H * d;
+        const int64_t units = (int64_t)N * (F / o.group);
+        const unsigned blocks = (unsigned)((units + 3) / 4);
+        const float* yf = (const float*)ydst;
+        tm.before();
+#define LA_GATE(XT, OT)                                                                                     \
+    do {                                                                                                    \
+        if (o.group % 256 == 0) k_gate4<XT, OT><<<blocks, 256, 0, st>>>(yf, (const XT*)x_gate, rms_weight, (OT*)out, N, F, o.group, o.eps); \
+        else k_gate<XT, OT><<<blocks, 256, 0, st>>>(yf, (const XT*)x_gate, rms_weight, (OT*)out, N, F, o.group, o.eps); \
+    } while (0)
+        if (in_dtype == LA_DTYPE_BF16) {
+            if (out_dtype == LA_DTYPE_BF16) LA_GATE(uint16_t, uint16_t); else LA_GATE(uint16_t, float);
+        } else {
+            if (out_dtype == LA_DTYPE_BF16) LA_GATE(float, uint16_t); else LA_GATE(float, float);
+        }
+#undef LA_GATE
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+    }
+    return LA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,215 @@
+// la_kernels_aux.h -- chunk planner, chunk-state prefix scan, output gate,
+// decode step and state fill.
+#pragma once
+
+#include "la_device.h"
+#include "la_items.h"
+
+namespace la {
+
+// chunk_off[s] = sum_{s' < s} ceil(len_s' / C) from device cu_seqlens, one
+// workgroup of 256 threads, no host round trip.
+__global__ __launch_bounds__(256) void k_plan_chunks(const int32_t* __restrict__ cu, int32_t nseq,
+                                                     int32_t C, int32_t* __restrict__ chunk_off) {
+    __shared__ int32_t part[257];
+    const int tid = threadIdx.x;
+    const int per = (nseq + 255) / 256;
+    const int s0 = min(nseq, tid * per), s1 = min(nseq, s0 + per);
+    int32_t local = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int32_t L = max(0, cu[s + 1] - cu[s]);
+        local += (L + C - 1) / C;
+    }
+    part[tid] = local;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t acc = 0;
+        for (int i = 0; i < 256; ++i) {
+            const int32_t x = part[i];
+            part[i] = acc;
+            acc += x;
+        }
+        part[256] = acc;
+        chunk_off[nseq] = acc;
+    }
+    __syncthreads();
+    int32_t acc = part[tid];
+    for (int s = s0; s < s1; ++s) {
+        chunk_off[s] = acc;
+        const int32_t L = max(0, cu[s + 1] - cu[s]);
+        acc += (L + C - 1) / C;
+    }
+}
+
+// Exclusive prefix over the chunks of each sequence, in increasing chunk order
+// (deterministic): buf[item] <- init + sum of the earlier chunks' increments;
+// the full sum goes to state_out / z_out.  E = D*D (+ D with the normaliser).
+__global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int64_t stride,
+                                                    ItemMap map, int H, int D, int E,
+                                                    const float* state_in, const float* z_in,
+                                                    float* state_out, float* z_out) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const int h = blockIdx.y, s = blockIdx.z;
+    int32_t first, count;
+    seq_items(map, s, first, count);
+    const int DD = D * D;
+    float acc;
+    if (e < DD) acc = state_in ? state_in[((size_t)s * H + h) * DD + e] : 0.f;
+    else acc = z_in ? z_in[((size_t)s * H + h) * D + (e - DD)] : 0.f;
+    for (int32_t i = 0; i < count; ++i) {
+        float* p = buf + ((size_t)(first + i) * H + h) * stride + e;
+        const float dlt = *p;
+        *p = acc;
+        acc += dlt;
+    }
+    if (e < DD) {
+        if (state_out) state_out[((size_t)s * H + h) * DD + e] = acc;
+    } else if (z_out) {
+        z_out[((size_t)s * H + h) * D + (e - DD)] = acc;
+    }
+}
+
+// state_out <- state_in (or zeros), z_out likewise: the zero-length case.
+__global__ __launch_bounds__(256) void k_fill_state(const float* state_in, const float* z_in,
+                                                    float* state_out, float* z_out, int64_t nS,
+                                                    int64_t nz) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (state_out && i < nS) state_out[i] = state_in ? state_in[i] : 0.f;
+    if (z_out && i < nz) z_out[i] = z_in ? z_in[i] : 0.f;
+}
+
+// Output gate (page "MiniMax-Text-01 405B MoE模型架构与训练策略解析" section 2.1):
+// per token and norm group of G features, r = 1/sqrt(mean(y^2) + eps), then
+// out = y * r * w * sigmoid(x).  One wave per (token, group); y and out may be
+// the same buffer.
+template <typename XT, typename OutT>
+__global__ __launch_bounds__(256) void k_gate(const float* y, const XT* __restrict__ x,
+                                              const float* __restrict__ w, OutT* out, int64_t ntok,
+                                              int F, int G, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int ngroups = F / G;
+    const int64_t tok = unit / ngroups;
+    if (tok >= ntok) return;
+    const int grp = (int)(unit - tok * ngroups);
+    const size_t base = (size_t)tok * F + (size_t)grp * G;
+    float ss = 0.f;
+    for (int f = lane; f < G; f += 64) {
+        const float a = y[base + f];
+        ss += a * a;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss / (float)G + eps);
+    for (int f = lane; f < G; f += 64) {
+        const float a = y[base + f];
+        const float wf = w ? w[grp * G + f] : 1.f;
+        store_from_f32<OutT>(out + base + f, a * r * wf * sigmoid(load_as_f32<XT>(x + base + f)));
+    }
+}
+
+// Vectorised gate for G % 256 == 0: each lane handles 4 consecutive features.
+template <typename XT, typename OutT>
+__global__ __launch_bounds__(256) void k_gate4(const float* y, const XT* __restrict__ x,
+                                               const float* __restrict__ w, OutT* out, int64_t ntok,
+                                               int F, int G, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int ngroups = F / G;
+    const int64_t tok = unit / ngroups;
+    if (tok >= ntok) return;
+    const int grp = (int)(unit - tok * ngroups);
+    const size_t base = (size_t)tok * F + (size_t)grp * G;
+    float ss = 0.f;
+    for (int f = 4 * lane; f < G; f += 256) {
+        const float4 a = *(const float4*)(y + base + f);
+        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss / (float)G + eps);
+    for (int f = 4 * lane; f < G; f += 256) {
+        const float4 a = *(const float4*)(y + base + f);
+        float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float wf = w ? w[grp * G + f + e] : 1.f;
+            store_from_f32<OutT>(out + base + f + e,
+                                 av[e] * r * wf * sigmoid(load_as_f32<XT>(x + base + f + e)));
+        }
+    }
+}
+
+// Decode step (page "六十四：MiniMax-01" section 3: a new token updates only S
+// and z, and reads its output from them).  One workgroup per (sequence,
+// head) streams the d x d state once: S += phi(k) phi(v)^T in place, then
+// y = phi(q)^T S (read after the update), optionally / phi(q).z.
+template <int D, typename InT, typename OutT, bool NORM>
+__global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const InT* __restrict__ k,
+                                                const InT* __restrict__ v, float* __restrict__ S,
+                                                float* __restrict__ z, OutT* __restrict__ y) {
+    constexpr int CQ = D / 4;      // threads per state row (float4 each)
+    constexpr int RG = 256 / CQ;   // row groups
+    constexpr int M = D / RG;      // rows per thread
+    __shared__ float fq[D], fk[D], fv[D];
+    __shared__ float4 part[RG][CQ];
+    __shared__ float dpart[4];
+    const int tid = threadIdx.x;
+    const size_t pair = blockIdx.x;  // sequence * H + head
+    const size_t vb = pair * D;
+    if (tid < D) {
+        fq[tid] = silu(load_as_f32<InT>(q + vb + tid));
+        fk[tid] = silu(load_as_f32<InT>(k + vb + tid));
+        fv[tid] = silu(load_as_f32<InT>(v + vb + tid));
+    }
+    __syncthreads();
+    float den_part = 0.f;
+    if (NORM && tid < D) {
+        const float zn = z[vb + tid] + fk[tid];
+        z[vb + tid] = zn;
+        den_part = fq[tid] * zn;
+    }
+    const int cq = tid % CQ, rg = tid / CQ;
+    const float4 v4 = make_float4(fv[4 * cq], fv[4 * cq + 1], fv[4 * cq + 2], fv[4 * cq + 3]);
+    float4* S4 = (float4*)(S + pair * D * D);
+    float4 s[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) s[m] = S4[(rg + RG * m) * CQ + cq];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        const int i = rg + RG * m;
+        const float kk = fk[i], qq = fq[i];
+        float4 t = s[m];
+        t.x += kk * v4.x;
+        t.y += kk * v4.y;
+        t.z += kk * v4.z;
+        t.w += kk * v4.w;
+        S4[i * CQ + cq] = t;
+        acc.x += qq * t.x;
+        acc.y += qq * t.y;
+        acc.z += qq * t.z;
+        acc.w += qq * t.w;
+    }
+    part[rg][cq] = acc;
+    if (NORM) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) den_part += __shfl_xor(den_part, m, 64);
+        if ((tid & 63) == 0) dpart[tid >> 6] = den_part;
+    }
+    __syncthreads();
+    if (tid < D) {
+        const int c4 = tid >> 2, e = tid & 3;
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const float4 p = part[r][c4];
+            a += e == 0 ? p.x : e == 1 ? p.y : e == 2 ? p.z : p.w;
+        }
+        if (NORM) a /= (dpart[0] + dpart[1] + dpart[2] + dpart[3]);
+        store_from_f32<OutT>(y + vb + tid, a);
+    }
+}
+
+}  // namespace la

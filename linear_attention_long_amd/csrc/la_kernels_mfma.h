@@ -1,0 +1,452 @@
+// la_kernels_mfma.h -- bf16 matrix-core (MFMA) kernels for head dim 128.
+//
+// Method (page "MiniMax-Text-01 405B MoE模型架构与训练策略解析" section 2.1 and
+// page "六十四：MiniMax-01" section 3): per head, phi = SiLU on q, k, v;
+// y_t = phi(q_t)^T S_t with S_t = S_{t-1} + phi(k_t) phi(v_t)^T, the sum
+// including token t.  Evaluated in blocks of 64 tokens: inside a block the
+// masked quadratic form (phi(Q) phi(K)^T (.) M) phi(V), M = lower triangle
+// with the diagonal; across blocks phi(Q) S_prev with the fp32 state carried
+// in registers; after the block S += phi(K)^T phi(V).
+//
+// gfx950 design:
+//  * one workgroup = 4 waves = one (chunk, head); wave w owns value columns
+//    [32w, 32w+32) of the state (128 x 32 fp32 = 64 accumulator registers per
+//    lane) and of the output, so the state never leaves registers;
+//  * q, k, v of a 64-token block are staged once into LDS as bf16 hi/lo pairs
+//    of phi(x) (hi = RNE(phi), lo = RNE(phi - hi)), row-major;
+//    contractions over d read row fragments, contractions over tokens read
+//    transposed fragments with ds_read_b64_tr_b16, so no transposed copies;
+//  * every product takes three bf16 MFMAs (hi*hi + hi*lo + lo*hi), which
+//    carries ~16 significant bits of each operand: with single bf16 operands
+//    the intra-block term alone (all of y for short sequences) is off by
+//    ~1.5e-2 of rms;
+//  * outputs are produced transposed (Y^T = V^T P^T + S^T Q^T) so each lane
+//    holds 4 consecutive output features and stores 16 bytes;
+//  * the next block's raw q, k, v are loaded into registers while the
+//    current block computes.
+#pragma once
+
+#include "la_device.h"
+#include "la_items.h"
+
+namespace la {
+namespace mf {
+
+constexpr int D = 128;   // head dim
+constexpr int TB = 64;   // tokens per block
+constexpr int NT = 256;  // threads per workgroup
+constexpr int LS = 136;  // LDS row stride of q/k/v tiles (bf16 elements)
+constexpr int PS = 72;   // LDS row stride of the P tile
+
+struct SmemMain {
+    uint16_t qh[TB * LS];
+    uint16_t ql[TB * LS];
+    uint16_t kh[TB * LS];
+    uint16_t kl[TB * LS];
+    uint16_t vh[TB * LS];
+    uint16_t vl[TB * LS];
+    uint16_t ph[TB * PS];  // P[query][key], bf16 hi
+    uint16_t pl[TB * PS];  // P[query][key], bf16 lo
+    float denp[4 * TB];    // normalised mode: row sums of P per 16-key tile
+    float zq[TB];          // normalised mode: phi(q) . z_prev per row
+    float zpart[16 * D];   // normalised mode: column sums of phi(k) per row group
+    float z[D];            // normalised mode: running normaliser
+};
+
+struct SmemState {
+    uint16_t kh[TB * LS];
+    uint16_t kl[TB * LS];
+    uint16_t vh[TB * LS];
+    uint16_t vl[TB * LS];
+    float zpart[16 * D];
+};
+
+// Thread tid loads rows (tid>>4) + 16j, j = 0..3, columns (tid&15)*8 .. +7 of
+// a 64 x 128 bf16 tile of one head; rows at or past nvalid read as zero.
+__device__ __forceinline__ void load_tile(uint4 (&dst)[4], const uint16_t* __restrict__ src,
+                                          int64_t t0, int nvalid, int H, int h, int tid) {
+    const int col = (tid & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (tid >> 4) + 16 * j;
+        if (r < nvalid) {
+            dst[j] = *(const uint4*)(src + ((size_t)(t0 + r) * H + h) * D + col);
+        } else {
+            dst[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+__device__ __forceinline__ void silu8(const uint4& w, float (&f)[8]) {
+    f[0] = silu(bf16_lo_to_f32(w.x));
+    f[1] = silu(bf16_hi_to_f32(w.x));
+    f[2] = silu(bf16_lo_to_f32(w.y));
+    f[3] = silu(bf16_hi_to_f32(w.y));
+    f[4] = silu(bf16_lo_to_f32(w.z));
+    f[5] = silu(bf16_hi_to_f32(w.z));
+    f[6] = silu(bf16_lo_to_f32(w.w));
+    f[7] = silu(bf16_hi_to_f32(w.w));
+}
+
+__device__ __forceinline__ void store_split8(const float (&f)[8], uint16_t* dh, uint16_t* dl) {
+    uint4 hi, lo;
+    split2(f[0], f[1], hi.x, lo.x);
+    split2(f[2], f[3], hi.y, lo.y);
+    split2(f[4], f[5], hi.z, lo.z);
+    split2(f[6], f[7], hi.w, lo.w);
+    *(uint4*)dh = hi;
+    *(uint4*)dl = lo;
+}
+
+// phi(k) and phi(v) of the block into LDS (hi/lo); with NORM, per-thread
+// column sums of phi(k) over its 4 rows into zpart[tid>>4][col..col+7].
+template <bool NORM>
+__device__ __forceinline__ void stage_kv(const uint4 (&rk)[4], const uint4 (&rv)[4], uint16_t* kh,
+                                         uint16_t* kl, uint16_t* vh, uint16_t* vl, float* zpart,
+                                         int tid) {
+    const int col = (tid & 15) * 8;
+    float zs[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zs[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = (tid >> 4) + 16 * j;
+        float f[8];
+        silu8(rk[j], f);
+        store_split8(f, kh + r * LS + col, kl + r * LS + col);
+        if (NORM) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zs[e] += f[e];
+        }
+        silu8(rv[j], f);
+        store_split8(f, vh + r * LS + col, vl + r * LS + col);
+    }
+    if (NORM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zpart[(tid >> 4) * D + col + e] = zs[e];
+    }
+}
+
+// State update S[dk][dv] += sum_t phi(k_t)[dk] phi(v_t)[dv] over the first
+// nks*32 rows of the staged block (rows past the data are zero).
+// S[dkt][dvt]: C-layout tile, lane (g, c) holds dv = 32*wave + 16*dvt + c,
+// dk = 16*dkt + 4*g + i.
+__device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t* kh,
+                                             const uint16_t* kl, const uint16_t* vh,
+                                             const uint16_t* vl, int nks, int wave, int g, int c) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks < nks) {
+            const int r0 = 32 * ks + 8 * g;
+            bf16x8_t Vh[2], Vl[2];
+#pragma unroll
+            for (int dvt = 0; dvt < 2; ++dvt) {
+                const int c0 = 32 * wave + 16 * dvt;
+                Vh[dvt] = as_bf16x8(lds_read_tr4(vh, LS, r0, c0, c), lds_read_tr4(vh, LS, r0 + 4, c0, c));
+                Vl[dvt] = as_bf16x8(lds_read_tr4(vl, LS, r0, c0, c), lds_read_tr4(vl, LS, r0 + 4, c0, c));
+            }
+#pragma unroll
+            for (int dkt = 0; dkt < 8; ++dkt) {
+                const int c0 = 16 * dkt;
+                const bf16x8_t Kh = as_bf16x8(lds_read_tr4(kh, LS, r0, c0, c), lds_read_tr4(kh, LS, r0 + 4, c0, c));
+                const bf16x8_t Kl = as_bf16x8(lds_read_tr4(kl, LS, r0, c0, c), lds_read_tr4(kl, LS, r0 + 4, c0, c));
+#pragma unroll
+                for (int dvt = 0; dvt < 2; ++dvt) {
+                    S[dkt][dvt] = mfma16x16x32(Kh, Vh[dvt], S[dkt][dvt]);
+                    S[dkt][dvt] = mfma16x16x32(Kh, Vl[dvt], S[dkt][dvt]);
+                    S[dkt][dvt] = mfma16x16x32(Kl, Vh[dvt], S[dkt][dvt]);
+                }
+            }
+        }
+    }
+}
+
+// Per-chunk state increment dS = sum_{t in chunk} phi(k_t) phi(v_t)^T (and
+// dz = sum phi(k_t)), written to buf[item][h] = [dS (D*D) | dz (D)].
+template <bool NORM>
+__global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v, ItemMap map,
+                                                       int H, float* __restrict__ buf,
+                                                       int64_t buf_stride) {
+    __shared__ SmemState sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.y;
+    Item it;
+    if (!decode_item(map, blockIdx.x, it)) return;
+
+    f32x4_t S[8][2];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) S[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float zacc = 0.f;
+
+    const int ntiles = (it.len + TB - 1) / TB;
+    uint4 rk[4], rv[4];
+    load_tile(rk, k, it.t0, min(TB, it.len), H, h, tid);
+    load_tile(rv, v, it.t0, min(TB, it.len), H, h, tid);
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int nvalid = min(TB, it.len - ti * TB);
+        __syncthreads();
+        stage_kv<NORM>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+        if (ti + 1 < ntiles) {
+            const int64_t t1 = it.t0 + (int64_t)(ti + 1) * TB;
+            const int nv1 = min(TB, it.len - (ti + 1) * TB);
+            load_tile(rk, k, t1, nv1, H, h, tid);
+            load_tile(rv, v, t1, nv1, H, h, tid);
+        }
+        __syncthreads();
+        if (NORM && tid < D) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s += sm.zpart[i * D + tid];
+            zacc += s;
+        }
+        state_update(S, sm.kh, sm.kl, sm.vh, sm.vl, nvalid <= 32 ? 1 : 2, wave, g, c);
+    }
+    float* dst = buf + ((size_t)blockIdx.x * H + h) * buf_stride;
+#pragma unroll
+    for (int dkt = 0; dkt < 8; ++dkt)
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] = S[dkt][dvt][i];
+    if (NORM && tid < D) dst[D * D + tid] = zacc;
+}
+
+template <typename OutT> __device__ __forceinline__ void store4(OutT* p, f32x4_t v, float s);
+template <> __device__ __forceinline__ void store4<float>(float* p, f32x4_t v, float s) {
+    *(float4*)p = make_float4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+}
+template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4_t v, float s) {
+    uint2 u;
+    u.x = pack_bf16x2(v[0] * s, v[1] * s);
+    u.y = pack_bf16x2(v[2] * s, v[3] * s);
+    *(uint2*)p = u;
+}
+
+// Main pass over one (chunk, head).  Starting state: prefix[item][h] if
+// prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
+// chunk is a whole sequence (no prefix), the final state is written to
+// state_out/z_out (if given).  Y goes to y[t][h*D + j].
+template <bool NORM, typename OutT>
+__global__ __launch_bounds__(NT, 1) void k_prefill_main(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
+    const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
+    float* state_out, float* z_out) {
+    __shared__ SmemMain sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.y;
+    Item it;
+    if (!decode_item(map, blockIdx.x, it)) return;
+
+    // P tiles above the diagonal are read by the P.V product but never written.
+    for (int i = tid; i < TB * PS / 2; i += NT) {
+        ((uint32_t*)sm.ph)[i] = 0u;
+        ((uint32_t*)sm.pl)[i] = 0u;
+    }
+    if (NORM)
+        for (int i = tid; i < 4 * TB; i += NT) sm.denp[i] = 0.f;
+
+    const float* s0 = nullptr;
+    const float* z0 = nullptr;
+    if (prefix) {
+        s0 = prefix + ((size_t)blockIdx.x * H + h) * prefix_stride;
+        z0 = s0 + D * D;
+    } else {
+        if (state_in) s0 = state_in + ((size_t)it.seq * H + h) * D * D;
+        if (z_in) z0 = z_in + ((size_t)it.seq * H + h) * D;
+    }
+    f32x4_t S[8][2];
+#pragma unroll
+    for (int dkt = 0; dkt < 8; ++dkt)
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[dkt][dvt][i] = s0 ? s0[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] : 0.f;
+    if (NORM && tid < D) sm.z[tid] = z0 ? z0[tid] : 0.f;
+
+    const int ntiles = (it.len + TB - 1) / TB;
+    uint4 rq[4], rk[4], rv[4];
+    load_tile(rq, q, it.t0, min(TB, it.len), H, h, tid);
+    load_tile(rk, k, it.t0, min(TB, it.len), H, h, tid);
+    load_tile(rv, v, it.t0, min(TB, it.len), H, h, tid);
+
+    for (int ti = 0; ti < ntiles; ++ti) {
+        const int64_t tt0 = it.t0 + (int64_t)ti * TB;
+        const int nvalid = min(TB, it.len - ti * TB);
+        const int nks = nvalid <= 32 ? 1 : 2;  // tail pad: 32 or 64 rows
+        const int nqt = 2 * nks;
+
+        __syncthreads();  // previous block's LDS reads and z update are done
+        {
+            const int col = (tid & 15) * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = (tid >> 4) + 16 * j;
+                float f[8];
+                silu8(rq[j], f);
+                store_split8(f, sm.qh + r * LS + col, sm.ql + r * LS + col);
+                if (NORM) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) part += f[e] * sm.z[col + e];
+                    part += __shfl_xor(part, 1, 64);
+                    part += __shfl_xor(part, 2, 64);
+                    part += __shfl_xor(part, 4, 64);
+                    part += __shfl_xor(part, 8, 64);
+                    if ((tid & 15) == 0) sm.zq[r] = part;
+                }
+            }
+            stage_kv<NORM>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+        }
+        if (ti + 1 < ntiles) {
+            const int64_t t1 = tt0 + TB;
+            const int nv1 = min(TB, it.len - (ti + 1) * TB);
+            load_tile(rq, q, t1, nv1, H, h, tid);
+            load_tile(rk, k, t1, nv1, H, h, tid);
+            load_tile(rv, v, t1, nv1, H, h, tid);
+        }
+        __syncthreads();
+        if (NORM && tid < D) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s += sm.zpart[i * D + tid];
+            sm.z[tid] += s;  // read again only after the next block's first barrier
+        }
+
+        // ---- P^T tiles (16 keys x 16 queries), causal, shared through LDS ----
+        {
+            const int ntau = nks == 2 ? 10 : 3;
+            for (int tau = wave; tau < ntau; tau += 4) {
+                const int qt = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
+                const int kt = tau - qt * (qt + 1) / 2;
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int ko = (16 * kt + c) * LS + 32 * s + 8 * g;
+                    const int qo = (16 * qt + c) * LS + 32 * s + 8 * g;
+                    const bf16x8_t ah = as_bf16x8(*(const uint4*)&sm.kh[ko]);
+                    const bf16x8_t al = as_bf16x8(*(const uint4*)&sm.kl[ko]);
+                    const bf16x8_t bh = as_bf16x8(*(const uint4*)&sm.qh[qo]);
+                    const bf16x8_t bl = as_bf16x8(*(const uint4*)&sm.ql[qo]);
+                    acc = mfma16x16x32(ah, bh, acc);
+                    acc = mfma16x16x32(ah, bl, acc);
+                    acc = mfma16x16x32(al, bh, acc);
+                }
+                // acc[i]: key 16kt + 4g + i, query 16qt + c; keep key <= query
+                if (kt == qt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (4 * g + i > c) acc[i] = 0.f;
+                }
+                uint2 pkh, pkl;
+                split2(acc[0], acc[1], pkh.x, pkl.x);
+                split2(acc[2], acc[3], pkh.y, pkl.y);
+                *(uint2*)&sm.ph[(16 * qt + c) * PS + 16 * kt + 4 * g] = pkh;
+                *(uint2*)&sm.pl[(16 * qt + c) * PS + 16 * kt + 4 * g] = pkl;
+                if (NORM) {
+                    float rs = acc[0] + acc[1] + acc[2] + acc[3];
+                    rs += __shfl_xor(rs, 16, 64);
+                    rs += __shfl_xor(rs, 32, 64);
+                    if (g == 0) sm.denp[kt * TB + 16 * qt + c] = rs;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- Y^T = V^T P^T (intra) + S^T Q^T (inter), this wave's 32 columns ----
+        f32x4_t acc[2][4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt) {
+            const int c0 = 32 * wave + 16 * dvt;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks < nks) {
+                    const int r0 = 32 * ks + 8 * g;
+                    const bf16x8_t ah = as_bf16x8(lds_read_tr4(sm.vh, LS, r0, c0, c),
+                                                  lds_read_tr4(sm.vh, LS, r0 + 4, c0, c));
+                    const bf16x8_t al = as_bf16x8(lds_read_tr4(sm.vl, LS, r0, c0, c),
+                                                  lds_read_tr4(sm.vl, LS, r0 + 4, c0, c));
+#pragma unroll
+                    for (int qt = 0; qt < 4; ++qt) {
+                        if (qt < nqt && (ks == 0 || qt >= 2)) {
+                            const int po = (16 * qt + c) * PS + 32 * ks + 8 * g;
+                            const bf16x8_t bh = as_bf16x8(*(const uint4*)&sm.ph[po]);
+                            const bf16x8_t bl = as_bf16x8(*(const uint4*)&sm.pl[po]);
+                            acc[dvt][qt] = mfma16x16x32(ah, bh, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(ah, bl, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(al, bh, acc[dvt][qt]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                uint4 ah, al;
+                split2(S[2 * s][dvt][0], S[2 * s][dvt][1], ah.x, al.x);
+                split2(S[2 * s][dvt][2], S[2 * s][dvt][3], ah.y, al.y);
+                split2(S[2 * s + 1][dvt][0], S[2 * s + 1][dvt][1], ah.z, al.z);
+                split2(S[2 * s + 1][dvt][2], S[2 * s + 1][dvt][3], ah.w, al.w);
+                const bf16x8_t Ah = as_bf16x8(ah), Al = as_bf16x8(al);
+#pragma unroll
+                for (int qt = 0; qt < 4; ++qt) {
+                    if (qt < nqt) {
+                        const int o = (16 * qt + c) * LS + 32 * s + 4 * g;
+                        const bf16x8_t Bh = as_bf16x8(*(const i16x4_t*)&sm.qh[o], *(const i16x4_t*)&sm.qh[o + 16]);
+                        const bf16x8_t Bl = as_bf16x8(*(const i16x4_t*)&sm.ql[o], *(const i16x4_t*)&sm.ql[o + 16]);
+                        acc[dvt][qt] = mfma16x16x32(Ah, Bh, acc[dvt][qt]);
+                        acc[dvt][qt] = mfma16x16x32(Ah, Bl, acc[dvt][qt]);
+                        acc[dvt][qt] = mfma16x16x32(Al, Bh, acc[dvt][qt]);
+                    }
+                }
+            }
+        }
+        // acc[dvt][qt][i]: query 16qt + c, feature 32*wave + 16*dvt + 4g + i
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+            const int row = 16 * qt + c;
+            if (qt < nqt && row < nvalid) {
+                float sc = 1.f;
+                if (NORM) {
+                    float den = sm.zq[row];
+                    for (int kt = 0; kt <= qt; ++kt) den += sm.denp[kt * TB + row];
+                    sc = 1.f / den;
+                }
+                OutT* dst = y + ((size_t)(tt0 + row) * H + h) * D + 32 * wave + 4 * g;
+#pragma unroll
+                for (int dvt = 0; dvt < 2; ++dvt) store4<OutT>(dst + 16 * dvt, acc[dvt][qt], sc);
+            }
+        }
+
+        // ---- S += phi(K)^T phi(V) ----
+        state_update(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+    }
+
+    if (!prefix) {
+        if (state_out) {
+            float* dst = state_out + ((size_t)it.seq * H + h) * D * D;
+#pragma unroll
+            for (int dkt = 0; dkt < 8; ++dkt)
+#pragma unroll
+                for (int dvt = 0; dvt < 2; ++dvt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dst[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] = S[dkt][dvt][i];
+        }
+        if (NORM && z_out) {
+            __syncthreads();
+            if (tid < D) z_out[((size_t)it.seq * H + h) * D + tid] = sm.z[tid];
+        }
+    }
+}
+
+}  // namespace mf
+}  // namespace la

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/la.h declares, and rejects invalid calls on the host.
+
+Every call below fails host validation, so none of them reaches a HIP call;
+the fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_long_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+F32, BF16 = _lib.LA_DTYPE_F32, _lib.LA_DTYPE_BF16
+INVALID, UNSUPPORTED, WS_SMALL = (_lib.LA_ERR_INVALID_ARGUMENT, _lib.LA_ERR_UNSUPPORTED,
+                                  _lib.LA_ERR_WORKSPACE_TOO_SMALL)
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+# fake, 256-byte aligned, never dereferenced "device" addresses
+A = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(12)]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from linear_attention_long_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+[\s\*]+(la_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_python_export_list():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_default_options(lib):
+    o = lib.la_default_options()
+    assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (64, 0, 0, 0, 0)
+    assert abs(o.rms_eps - 1e-6) < 1e-12
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.la_status_string(s)
+    assert lib.la_status_string(99) == b"unknown status"
+
+
+def opt(**kw):
+    o = _lib.options()
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def test_workspace_queries(lib):
+    o = opt()
+    # one chunk per sequence, ungated: nothing needed
+    assert lib.la_prefill_workspace_bytes(1, 1024, 2, 64, F32, F32, ctypes.byref(o)) == 0
+    # 1M tokens x 8 heads: chunked, chunk 8192 -> 128 chunks x 8 heads x d^2 floats
+    assert lib.la_prefill_chunk_tokens(1, 1 << 20, 1 << 20, 8, 128, BF16, ctypes.byref(o)) == 8192
+    nb = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, F32, ctypes.byref(o))
+    assert nb == 128 * 8 * 128 * 128 * 4
+    # gated with a bf16 output adds an fp32 Y buffer
+    g = opt(gated=1)
+    nb2 = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, BF16, ctypes.byref(g))
+    assert nb2 == nb + (1 << 20) * 8 * 128 * 4
+    assert lib.la_decode_workspace_bytes(64, 64, 128, F32, ctypes.byref(g)) == 0
+    assert lib.la_decode_workspace_bytes(64, 64, 128, BF16, ctypes.byref(g)) == 64 * 64 * 128 * 4
+    # rejected arguments report SIZE_MAX
+    assert lib.la_prefill_workspace_bytes(1, 16, 2, 96, F32, F32, ctypes.byref(o)) == SIZE_MAX
+    assert lib.la_prefill_workspace_bytes(0, 16, 2, 64, F32, F32, ctypes.byref(o)) == SIZE_MAX
+    assert lib.la_prefill_varlen_workspace_bytes(10, 2, 11, 2, 64, F32, F32, ctypes.byref(o)) == SIZE_MAX
+
+
+def prefill(lib, q=A[0], k=A[1], v=A[2], x=None, w=None, si=None, zi=None, out=A[3], so=None,
+            zo=None, Bt=1, T=64, H=2, d=64, idt=F32, odt=F32, o=None, ws=None, wsb=0):
+    o = o or opt()
+    return lib.la_prefill(q, k, v, x, w, si, zi, out, so, zo, Bt, T, H, d, idt, odt,
+                          ctypes.byref(o), ws, wsb, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert prefill(lib, q=None) == INVALID
+    assert prefill(lib, out=None) == INVALID
+    assert prefill(lib, q=ctypes.c_void_p(0x10000004)) == INVALID          # misaligned
+    assert prefill(lib, d=96) == UNSUPPORTED
+    assert prefill(lib, d=0) == INVALID
+    assert prefill(lib, H=0) == INVALID
+    assert prefill(lib, T=-1) == INVALID
+    assert prefill(lib, Bt=0) == INVALID
+    assert prefill(lib, idt=7) == INVALID
+    assert prefill(lib, o=opt(block_size=48)) == UNSUPPORTED
+    assert prefill(lib, o=opt(normalized=2)) == INVALID
+    assert prefill(lib, o=opt(gated=1)) == INVALID                         # no gate input
+    assert prefill(lib, o=opt(norm_group=100)) == INVALID
+    assert prefill(lib, o=opt(rms_eps=-1.0)) == INVALID
+    assert prefill(lib, o=opt(chunk_tokens=100)) == INVALID
+    assert prefill(lib, zi=A[5]) == INVALID                               # z without normalised mode
+    # out overlapping an input
+    assert prefill(lib, out=A[0]) == INVALID
+    # state_out partly overlapping state_in
+    assert prefill(lib, si=A[6], so=ctypes.c_void_p(A[6].value + 256)) == INVALID
+    # chunked plan needs a workspace
+    o = opt(chunk_tokens=64)
+    assert prefill(lib, T=4096, o=o) == INVALID                          # NULL workspace
+    need = lib.la_prefill_workspace_bytes(1, 4096, 2, 64, F32, F32, ctypes.byref(o))
+    assert need > 0
+    assert prefill(lib, T=4096, o=o, ws=A[8], wsb=need - 1) == WS_SMALL
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    o = opt()
+
+    def call(cu=A[9], nseq=2, total=100, maxlen=60, **kw):
+        return lib.la_prefill_varlen(A[0], A[1], A[2], None, None, cu, nseq, total, maxlen,
+                                     None, None, A[3], None, None, kw.get("H", 2), kw.get("d", 64),
+                                     F32, F32, ctypes.byref(kw.get("o", o)), None, 0, None)
+
+    assert call(cu=None) == INVALID
+    assert call(nseq=0) == INVALID
+    assert call(total=-1) == INVALID
+    assert call(maxlen=101) == INVALID
+    assert call(d=32) == UNSUPPORTED
+    # varlen always needs the chunk table in the workspace
+    assert call() == INVALID
+
+
+def test_decode_rejects_bad_arguments(lib):
+    def call(q=A[0], state=A[4], z=None, out=A[3], x=None, N=4, H=2, d=64, o=None, ws=None, wsb=0,
+             odt=F32):
+        o = o or opt()
+        return lib.la_decode_step(q, A[1], A[2], x, None, state, z, out, N, H, d, F32, odt,
+                                  ctypes.byref(o), ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(state=None) == INVALID
+    assert call(N=-1) == INVALID
+    assert call(d=256) == UNSUPPORTED
+    assert call(o=opt(normalized=1)) == INVALID          # normalised mode needs z
+    assert call(z=A[5]) == INVALID                       # z without normalised mode
+    assert call(o=opt(gated=1)) == INVALID               # gate input missing
+    assert call(out=A[4]) == INVALID                     # out overlaps the state
+    g = opt(gated=1)
+    assert call(o=g, x=A[6], odt=BF16) == INVALID        # bf16 gated output needs workspace
+    assert call(o=g, x=A[6], odt=BF16, ws=A[7], wsb=16) == WS_SMALL

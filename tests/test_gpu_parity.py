@@ -1,0 +1,322 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (max|err| / rms(ref), over every element compared):
+  * fp32 inputs: 1e-5 -- fp32 arithmetic throughout;
+  * bf16 inputs: 1e-2 -- bf16 matrix-core operands (hi/lo split on the
+    inter-block and state products), fp32 accumulation, fp32 output.
+The oracle runs in fp64 on the same (bf16- or fp32-valued) inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_long_amd import api, inputs
+from oracle import oracle as O
+from tests._util import banner, np64, randn, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 1e-2
+DEV = "cuda"
+
+
+def run_prefill(q, k, v, x=None, **kw):
+    out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV),
+                               None if x is None else x.to(DEV), **kw)
+    torch.cuda.synchronize()
+    return out, S, z
+
+
+def oracle_forward(q, k, v, x=None, state_in=None, z_in=None, normalized=False, norm_group=0):
+    """Oracle on [Bt, T, H, d] inputs -> out [Bt, T, H*d], S [Bt, H, d, d], z."""
+    Bt, T, H, d = q.shape
+    outs, Ss, zs = [], [], []
+    for b in range(Bt):
+        o, S, z = O.forward(q[b], k[b], v[b], None if x is None else x[b], None,
+                            state_in=None if state_in is None else state_in[b:b + 1],
+                            z_in=None if z_in is None else z_in[b:b + 1],
+                            normalized=normalized, gated=x is not None, norm_group=norm_group)
+        outs.append(o)
+        Ss.append(S[0])
+        zs.append(z[0])
+    return np.stack(outs), np.stack(Ss), np.stack(zs)
+
+
+# ---------------------------------------------------------------- fp32 path --
+
+def test_tiny_f32_workload():
+    """fp32, B=1 T=1024 H=2 d=64, block 64, ungated, unnormalised."""
+    w = inputs.WORKLOADS["tiny_f32"]
+    banner("tiny_f32 workload")
+    q, k, v, _ = inputs.prefill_inputs(w)
+    out, S, _ = run_prefill(q, k, v, block_size=w.block)
+    ref, Sref, _ = oracle_forward(q, k, v)
+    assert rel_err(np64(out), ref.reshape(out.shape)) <= TOL_F32
+    assert rel_err(np64(S), Sref) <= TOL_F32
+
+
+@pytest.mark.parametrize("block", [32, 64, 128, 256])
+@pytest.mark.parametrize("T,chunk", [(1000, 0), (1000, 256), (1, 0), (33, 0), (300, 64)])
+def test_f32_block_sizes_and_tails(block, T, chunk):
+    banner("f32 block=%d T=%d chunk=%d" % (block, T, chunk))
+    H, d = 2, 64
+    q, k, v = (randn((1, T, H, d), 10 + i) for i in range(3))
+    out, S, _ = run_prefill(q, k, v, block_size=block, chunk_tokens=chunk)
+    ref, Sref, _ = oracle_forward(q, k, v)
+    assert rel_err(np64(out), ref.reshape(out.shape)) <= TOL_F32
+    assert rel_err(np64(S), Sref) <= TOL_F32
+
+
+def test_f32_d128_gated_normalized_with_state():
+    banner("f32 d=128 gated normalised with state")
+    Bt, T, H, d = 2, 200, 2, 128
+    q, k = (randn((Bt, T, H, d), 20 + i, 0.5, 1.0) for i in range(2))
+    v = randn((Bt, T, H, d), 22)
+    x = randn((Bt, T, H * d), 23)
+    S0 = randn((Bt, H, d, d), 24, 0.01).abs()
+    z0 = randn((Bt, H, d), 25, 0.1).abs() + 1.0
+    out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), None, S0.to(DEV),
+                               z0.to(DEV), normalized=True, chunk_tokens=64)
+    ref, Sref, zref = oracle_forward(q, k, v, x, S0, z0, normalized=True)
+    assert rel_err(np64(out), ref) <= TOL_F32
+    assert rel_err(np64(S), Sref) <= TOL_F32
+    assert rel_err(np64(z), zref) <= TOL_F32
+
+
+# ---------------------------------------------------- bf16 matrix-core path --
+
+@pytest.mark.parametrize("T", [1, 17, 32, 33, 64, 100, 1000, 2085])
+@pytest.mark.parametrize("gated", [False, True])
+def test_bf16_short_sequences(T, gated):
+    banner("bf16 T=%d gated=%s" % (T, gated))
+    H, d = 2, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 30 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((1, T, H * d), 33, dtype=torch.bfloat16) if gated else None
+    out, S, _ = run_prefill(q, k, v, x)
+    ref, Sref, _ = oracle_forward(q, k, v, x)
+    assert rel_err(np64(out), ref) <= TOL_BF16
+    assert rel_err(np64(S), Sref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [64, 1024])
+def test_bf16_chunked_with_state_in(chunk):
+    banner("bf16 chunked chunk=%d" % chunk)
+    Bt, T, H, d = 2, 3000, 4, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((Bt, T, H, d), 40 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((Bt, T, H * d), 43, dtype=torch.bfloat16)
+    S0 = randn((Bt, H, d, d), 44, 0.05)
+    out, S, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), None, S0.to(DEV),
+                               chunk_tokens=chunk)
+    ref, Sref, _ = oracle_forward(q, k, v, x, S0)
+    assert rel_err(np64(out), ref) <= TOL_BF16
+    assert rel_err(np64(S), Sref) <= TOL_BF16
+
+
+def test_bf16_normalized():
+    banner("bf16 normalised")
+    Bt, T, H, d = 1, 1500, 2, 128
+    q, k = (randn((Bt, T, H, d), 50 + i, 0.5, 1.0, dtype=torch.bfloat16) for i in range(2))
+    v = randn((Bt, T, H, d), 52, dtype=torch.bfloat16)
+    z0 = torch.ones((Bt, H, d))
+    for chunk in (0, 512):
+        out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), None, None, None, z0.to(DEV),
+                                   normalized=True, chunk_tokens=chunk)
+        ref, Sref, zref = oracle_forward(q, k, v, None, None, z0, normalized=True)
+        assert rel_err(np64(out), ref.reshape(out.shape)) <= TOL_BF16
+        assert rel_err(np64(z), zref) <= 1e-4
+
+
+def test_bf16_out_dtype_and_weight():
+    banner("bf16 output, rms weight, per-head norm group")
+    T, H, d = 700, 4, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 60 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((1, T, H * d), 63, dtype=torch.bfloat16)
+    w = randn((H * d,), 64, 0.2, 1.0)
+    for group in (0, d):
+        out, _, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), w.to(DEV),
+                                   norm_group=group, out_dtype=torch.float32)
+        ref, _, _ = O.forward(q[0], k[0], v[0], x[0], w, gated=True, norm_group=group)
+        assert rel_err(np64(out[0]), ref) <= TOL_BF16
+        outb, _, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), w.to(DEV),
+                                    norm_group=group, out_dtype=torch.bfloat16)
+        # bf16 storage adds up to half an ulp (<= 2^-8 of |value|, 8 significant bits)
+        # on top of the fp32-output error bound
+        rms = np.sqrt(np.mean(ref ** 2))
+        err = np.abs(np64(outb[0]) - ref)
+        assert (err <= 2.0 ** -8 * np.abs(ref) + TOL_BF16 * rms).all()
+
+
+def test_prefill_32k_workload():
+    """bf16, T=32768, H=8, d=128, gated: every output and the final state."""
+    w = inputs.WORKLOADS["prefill_32k"]
+    banner("prefill_32k workload")
+    q, k, v, x = inputs.prefill_inputs(w)
+    out, S, _ = run_prefill(q, k, v, x)
+    ref, Sref, _ = oracle_forward(q, k, v, x)
+    e_out, e_S = rel_err(np64(out), ref), rel_err(np64(S), Sref)
+    print("prefill_32k rel err out %.3e state %.3e" % (e_out, e_S))
+    assert e_out <= TOL_BF16 and e_S <= TOL_BF16
+
+
+# ------------------------------------------------------------------- varlen --
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("chunk", [0, 128])
+def test_varlen_matches_oracle(dtype, d, chunk):
+    banner("varlen dtype=%s d=%d chunk=%d" % (dtype, d, chunk))
+    lengths = [1, 0, 100, 64, 1500, 33, 0, 257]
+    cu = inputs.cu_from_lengths(lengths)
+    total, H = int(cu[-1]), 2
+    s = 1.0 / np.sqrt(d) if dtype == torch.bfloat16 else 1.0
+    q, k, v = (randn((total, H, d), 70 + i, s, dtype=dtype) for i in range(3))
+    x = randn((total, H * d), 73, dtype=dtype)
+    S0 = randn((len(lengths), H, d, d), 74, 0.05)
+    out, S, _ = api.la_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lengths),
+                                      x.to(DEV), None, S0.to(DEV), chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(q, k, v, x, None, cu_seqlens=cu.numpy(), state_in=S0, gated=True)
+    tol = TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+    assert rel_err(np64(out), ref) <= tol
+    assert rel_err(np64(S), Sref) <= tol
+    # empty sequences hand their state through unchanged
+    assert torch.equal(S[1].cpu(), S0[1]) and torch.equal(S[6].cpu(), S0[6])
+
+
+# ------------------------------------------------------------------- decode --
+
+@pytest.mark.parametrize("normalized", [False, True])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_decode_steps(normalized, dtype, d):
+    banner("decode normalized=%s dtype=%s d=%d" % (normalized, dtype, d))
+    N, H, steps = 3, 4, 12
+    S0 = randn((N, H, d, d), 80, 0.01)
+    z0 = randn((N, H, d), 81, 0.01).abs() + 1.0 if normalized else None
+    S_dev = S0.clone().to(DEV)
+    z_dev = None if z0 is None else z0.clone().to(DEV)
+    S_ref, z_ref = S0.numpy().astype(np.float64), None if z0 is None else z0.numpy().astype(np.float64)
+    shift = 1.0 if normalized else 0.0
+    for t in range(steps):
+        q, k, v = (randn((N, H, d), 100 * t + i, 1.0, shift if i < 2 else 0.0, dtype=dtype)
+                   for i in range(3))
+        y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S_dev, z_dev, normalized=normalized)
+        yr, S_ref, z_new = O.decode_step(q, k, v, S_ref, z_ref, normalized)
+        if normalized:
+            z_ref = z_new
+        tol = TOL_BF16 if dtype == torch.bfloat16 else TOL_F32
+        assert rel_err(np64(y), yr.reshape(N, H * d)) <= tol
+    assert rel_err(np64(S_dev), S_ref) <= 1e-5
+
+
+def test_decode_gated():
+    banner("decode gated")
+    N, H, d = 4, 8, 128
+    S0 = randn((N, H, d, d), 90, 0.01)
+    q, k, v = (randn((N, H, d), 91 + i, dtype=torch.bfloat16) for i in range(3))
+    x = randn((N, H * d), 94, dtype=torch.bfloat16)
+    for odt in (torch.float32, torch.bfloat16):
+        S_dev = S0.clone().to(DEV)
+        y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S_dev, None, x.to(DEV),
+                               out_dtype=odt)
+        yr, _, _ = O.decode_step(q, k, v, S0, None, False)
+        ref = O.gate(yr.reshape(N, H * d), x, None, 0, 1e-6)
+        if odt == torch.float32:
+            assert rel_err(np64(y), ref) <= TOL_BF16
+        else:
+            rms = np.sqrt(np.mean(ref ** 2))
+            assert (np.abs(np64(y) - ref) <= 2.0 ** -8 * np.abs(ref) + TOL_BF16 * rms).all()
+
+
+def test_decode_workload_steps():
+    """64 sequences x 64 heads x d=128, fp32 state N(0, 0.01): 10 steps, both modes."""
+    w = inputs.WORKLOADS["decode_64x64"]
+    for normalized in (False, True):
+        banner("decode_64x64 normalized=%s" % normalized)
+        S0, z0 = inputs.decode_state(w, device="cpu")
+        S_dev, z_dev = S0.to(DEV), z0.to(DEV) if normalized else None
+        S_ref, z_ref = S0.numpy().astype(np.float64), z0.numpy().astype(np.float64)
+        for step in range(10):
+            q, k, v = inputs.decode_token(w, step, device="cpu")
+            y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S_dev, z_dev,
+                                   normalized=normalized)
+            yr, S_ref, z_new = O.decode_step(q, k, v, S_ref, z_ref if normalized else None,
+                                             normalized)
+            yr = yr.reshape(w.N, w.H * w.d)
+            got = np64(y)
+            if normalized:
+                z_ref = z_new
+                # the unguarded denominator phi(q).z can pass near zero; judge
+                # rows whose |den| >= 0.5 and check the rest are finite
+                a = q.float().numpy().astype(np.float64)
+                a = a / (1 + np.exp(-a))
+                den = np.einsum("nhd,nhd->nh", a, z_ref)
+                keep = (np.abs(den) >= 0.5).repeat(w.d, axis=1).reshape(w.N, w.H * w.d)
+                assert rel_err(got[keep], yr[keep]) <= TOL_BF16
+            else:
+                assert rel_err(got, yr) <= TOL_BF16
+        assert rel_err(np64(S_dev), S_ref) <= 1e-5
+
+
+# ------------------------------------------------------------- invariances --
+
+def test_prefill_equals_decode_and_chaining():
+    banner("prefill == decode, chaining")
+    T, H, d = 40, 2, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 110 + i, s, dtype=torch.bfloat16).to(DEV) for i in range(3))
+    out, S, _ = api.la_prefill(q, k, v)
+    # the same tokens one at a time through the decode entry point
+    Sd = torch.zeros((1, H, d, d), device=DEV)
+    ys = [api.la_decode_step(q[:, t], k[:, t], v[:, t], Sd) for t in range(T)]
+    yd = torch.stack(ys, dim=1)
+    assert rel_err(np64(yd), np64(out)) <= TOL_BF16
+    assert rel_err(np64(Sd), np64(S)) <= 1e-3
+    # chunked prefill through state_out -> state_in
+    out1, S1, _ = api.la_prefill(q[:, :25], k[:, :25], v[:, :25])
+    out2, S2, _ = api.la_prefill(q[:, 25:], k[:, 25:], v[:, 25:], None, None, S1)
+    assert rel_err(np64(torch.cat([out1, out2], dim=1)), np64(out)) <= TOL_BF16
+    assert rel_err(np64(S2), np64(S)) <= 1e-3
+
+
+def test_deterministic_and_fully_written():
+    banner("determinism")
+    T, H, d = 5000, 4, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 120 + i, s, dtype=torch.bfloat16).to(DEV) for i in range(3))
+    x = randn((1, T, H * d), 123, dtype=torch.bfloat16).to(DEV)
+    a, Sa, _ = api.la_prefill(q, k, v, x, chunk_tokens=1024)
+    b, Sb, _ = api.la_prefill(q, k, v, x, chunk_tokens=1024)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(Sa, Sb)
+    assert torch.isfinite(a).all() and torch.isfinite(Sa).all()
+
+
+def test_state_alias_in_place():
+    banner("state_out aliasing state_in")
+    T, H, d = 300, 2, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 130 + i, s, dtype=torch.bfloat16) for i in range(3))
+    S0 = randn((1, H, d, d), 133, 0.05)
+    ref, Sref, _ = oracle_forward(q, k, v, None, S0)
+    import ctypes
+
+    from linear_attention_long_amd import _lib
+    lib = _lib.load()
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    S = S0.clone().to(DEV)
+    out = torch.empty((1, T, H * d), device=DEV)
+    for chunk in (0, 64):
+        S.copy_(S0.to(DEV))
+        opt = _lib.options(chunk_tokens=chunk)
+        nb = lib.la_prefill_workspace_bytes(1, T, H, d, 1, 0, ctypes.byref(opt))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=DEV)
+        st = lib.la_prefill(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), None, None, S.data_ptr(),
+                            None, out.data_ptr(), S.data_ptr(), None, 1, T, H, d, 1, 0,
+                            ctypes.byref(opt), ws.data_ptr(), nb, None)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert rel_err(np64(out), ref) <= TOL_BF16
+        assert rel_err(np64(S), Sref) <= TOL_BF16
