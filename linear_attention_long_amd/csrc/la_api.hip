@@ -212,11 +212,11 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const uint16_t* kb = (const uint16_t*)k;
         const uint16_t* vb = (const uint16_t*)v;
         if (y_is_f32) {
-            if (norm) mf::k_prefill_main<true, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out);
-            else mf::k_prefill_main<false, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, nullptr);
+            if (norm) mf::k_prefill_main<true, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out, 16);
+            else mf::k_prefill_main<false, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, nullptr, 16);
         } else {
-            if (norm) mf::k_prefill_main<true, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out);
-            else mf::k_prefill_main<false, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, nullptr);
+            if (norm) mf::k_prefill_main<true, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out, 16);
+            else mf::k_prefill_main<false, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, nullptr, 16);
         }
     } else {
 #define LA_VALU_MAIN(DD, YT, NN)                                                                \

@@ -22,9 +22,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_floa
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // phi = SiLU(x) = x * sigmoid(x)  (feature map on q, k and v)
 __device__ __forceinline__ float silu(float x) {
@@ -34,13 +31,22 @@ __device__ __forceinline__ float sigmoid(float x) {
     return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// Split an fp32 value into bf16 hi + bf16 lo with hi = RNE(x), lo = RNE(x - hi);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (RNE), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return cvt_pk_bf16(a, b); }
+
+// Split two fp32 values into bf16 hi + bf16 lo with hi = RNE(x), lo = RNE(x - hi);
 // hi*hi' + hi*lo' + lo*hi' then carries ~16 significant bits of each product.
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-    const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
-    const float r0 = x0 - bf16_to_f32(h0), r1 = x1 - bf16_to_f32(h1);
-    hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo = pack_bf16x2(r0, r1);
+    hi = cvt_pk_bf16(x0, x1);
+    lo = cvt_pk_bf16(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
 }
 
 template <typename T> __device__ __forceinline__ float load_as_f32(const T* p);
@@ -70,6 +76,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(i16x4_t lo, i16x4_t hi) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// 8-byte LDS read.
+__device__ __forceinline__ i16x4_t lds_read8(const uint16_t* p) { return *(const i16x4_t*)p; }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  For a row-major bf16 tile with
 // row stride `stride` elements, returns for this lane's 16-lane group the

@@ -14,12 +14,20 @@
 //    lane) and of the output, so the state never leaves registers;
 //  * q, k, v of a 64-token block are staged once into LDS as bf16 hi/lo pairs
 //    of phi(x) (hi = RNE(phi), lo = RNE(phi - hi)), row-major;
-//    contractions over d read row fragments, contractions over tokens read
-//    transposed fragments with ds_read_b64_tr_b16, so no transposed copies;
 //  * every product takes three bf16 MFMAs (hi*hi + hi*lo + lo*hi), which
 //    carries ~16 significant bits of each operand: with single bf16 operands
 //    the intra-block term alone (all of y for short sequences) is off by
 //    ~1.5e-2 of rms;
+//  * LDS traffic is arranged to be free of bank conflicts (measured with the
+//    SQ_LDS_BANK_CONFLICT counter on gfx950): contractions over tokens read
+//    transposed fragments with ds_read_b64_tr_b16 from row-major K, V and P^T
+//    tiles at a row stride of 144 (K, V) or 80 (P^T) elements, each 16-lane
+//    group covering four consecutive rows; contractions over the head dim
+//    read two 8-byte pieces per lane (never 16-byte row reads, which conflict)
+//    from Q and K rows.  The k index of every MFMA is permuted so that a
+//    lane's 8 slots are {32s + 4g + i, 32s + 16 + 4g + i}, i < 4, which is
+//    also the order in which a lane holds the fp32 state (C layout), so the
+//    state feeds the inter-block product straight from registers;
 //  * outputs are produced transposed (Y^T = V^T P^T + S^T Q^T) so each lane
 //    holds 4 consecutive output features and stores 16 bytes;
 //  * the next block's raw q, k, v are loaded into registers while the
@@ -35,29 +43,37 @@ namespace mf {
 constexpr int D = 128;   // head dim
 constexpr int TB = 64;   // tokens per block
 constexpr int NT = 256;  // threads per workgroup
-constexpr int LS = 136;  // LDS row stride of q/k/v tiles (bf16 elements)
-constexpr int PS = 72;   // LDS row stride of the P tile
+constexpr int QS = 136;  // LDS row stride of the Q tile (bf16 elements)
+constexpr int KS = 144;  // LDS row stride of the K and V tiles
+constexpr int PS = 80;   // LDS row stride of the P^T tile ([key][query])
+// 16 bytes after each LDS array: neighbouring hi/lo arrays then are not a
+// multiple of 512 bytes apart, so the compiler cannot fuse a read of one with
+// a read of the other into a ds_read2st64 that lands both halves in the same
+// banks.
+constexpr int APAD = 8;
 
-struct SmemMain {
-    uint16_t qh[TB * LS];
-    uint16_t ql[TB * LS];
-    uint16_t kh[TB * LS];
-    uint16_t kl[TB * LS];
-    uint16_t vh[TB * LS];
-    uint16_t vl[TB * LS];
-    uint16_t ph[TB * PS];  // P[query][key], bf16 hi
-    uint16_t pl[TB * PS];  // P[query][key], bf16 lo
+struct __attribute__((aligned(16))) SmemMain {
+    __attribute__((aligned(16))) uint16_t qh[TB * QS + APAD];
+    __attribute__((aligned(16))) uint16_t ql[TB * QS + APAD];
+    __attribute__((aligned(16))) uint16_t kh[TB * KS + APAD];
+    __attribute__((aligned(16))) uint16_t kl[TB * KS + APAD];
+    __attribute__((aligned(16))) uint16_t vh[TB * KS + APAD];
+    __attribute__((aligned(16))) uint16_t vl[TB * KS + APAD];
+    __attribute__((aligned(16))) uint16_t ph[TB * PS + APAD];  // P^T[key][query], bf16 hi
+    __attribute__((aligned(16))) uint16_t pl[TB * PS + APAD];  // P^T[key][query], bf16 lo
     float denp[4 * TB];    // normalised mode: row sums of P per 16-key tile
     float zq[TB];          // normalised mode: phi(q) . z_prev per row
     float zpart[16 * D];   // normalised mode: column sums of phi(k) per row group
     float z[D];            // normalised mode: running normaliser
 };
 
-struct SmemState {
-    uint16_t kh[TB * LS];
-    uint16_t kl[TB * LS];
-    uint16_t vh[TB * LS];
-    uint16_t vl[TB * LS];
+// (only transposing reads, which are never fused: no padding, so two
+// workgroups fit in one CU's 160 KB)
+struct __attribute__((aligned(16))) SmemState {
+    __attribute__((aligned(16))) uint16_t kh[TB * KS];
+    __attribute__((aligned(16))) uint16_t kl[TB * KS];
+    __attribute__((aligned(16))) uint16_t vh[TB * KS];
+    __attribute__((aligned(16))) uint16_t vl[TB * KS];
     float zpart[16 * D];
 };
 
@@ -113,18 +129,36 @@ __device__ __forceinline__ void stage_kv(const uint4 (&rk)[4], const uint4 (&rv)
         const int r = (tid >> 4) + 16 * j;
         float f[8];
         silu8(rk[j], f);
-        store_split8(f, kh + r * LS + col, kl + r * LS + col);
+        store_split8(f, kh + r * KS + col, kl + r * KS + col);
         if (NORM) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) zs[e] += f[e];
         }
         silu8(rv[j], f);
-        store_split8(f, vh + r * LS + col, vl + r * LS + col);
+        store_split8(f, vh + r * KS + col, vl + r * KS + col);
     }
     if (NORM) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) zpart[(tid >> 4) * D + col + e] = zs[e];
     }
+}
+
+// Operand over 32 tokens (rows of a row-major tile) for the permuted k
+// order: slots {r0 + 4g + i, r0 + 16 + 4g + i}; lane (g, c) gets column c0 + c.
+__device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* tile, int stride, int r0, int c0,
+                                               int g, int c) {
+    return as_bf16x8(lds_read_tr4(tile, stride, r0 + 4 * g, c0, c),
+                     lds_read_tr4(tile, stride, r0 + 16 + 4 * g, c0, c));
+}
+
+// Operand over 32 columns (head-dim features) of one row for the permuted k
+// order: columns {k0 + 4g + i, k0 + 16 + 4g + i} of row `row`.  `k16` is 16
+// at run time; passing it as a value keeps the two 8-byte reads separate
+// (a merged 2 x 8-byte read conflicts on LDS banks, two single ones do not).
+__device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, int stride, int row, int k0,
+                                                int g, int k16) {
+    const uint16_t* p = tile + row * stride + k0 + 4 * g;
+    return as_bf16x8(lds_read8(p), lds_read8(p + k16));
 }
 
 // State update S[dk][dv] += sum_t phi(k_t)[dk] phi(v_t)[dv] over the first
@@ -137,19 +171,17 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         if (ks < nks) {
-            const int r0 = 32 * ks + 8 * g;
             bf16x8_t Vh[2], Vl[2];
 #pragma unroll
             for (int dvt = 0; dvt < 2; ++dvt) {
                 const int c0 = 32 * wave + 16 * dvt;
-                Vh[dvt] = as_bf16x8(lds_read_tr4(vh, LS, r0, c0, c), lds_read_tr4(vh, LS, r0 + 4, c0, c));
-                Vl[dvt] = as_bf16x8(lds_read_tr4(vl, LS, r0, c0, c), lds_read_tr4(vl, LS, r0 + 4, c0, c));
+                Vh[dvt] = tr_operand(vh, KS, 32 * ks, c0, g, c);
+                Vl[dvt] = tr_operand(vl, KS, 32 * ks, c0, g, c);
             }
 #pragma unroll
             for (int dkt = 0; dkt < 8; ++dkt) {
-                const int c0 = 16 * dkt;
-                const bf16x8_t Kh = as_bf16x8(lds_read_tr4(kh, LS, r0, c0, c), lds_read_tr4(kh, LS, r0 + 4, c0, c));
-                const bf16x8_t Kl = as_bf16x8(lds_read_tr4(kl, LS, r0, c0, c), lds_read_tr4(kl, LS, r0 + 4, c0, c));
+                const bf16x8_t Kh = tr_operand(kh, KS, 32 * ks, 16 * dkt, g, c);
+                const bf16x8_t Kl = tr_operand(kl, KS, 32 * ks, 16 * dkt, g, c);
 #pragma unroll
                 for (int dvt = 0; dvt < 2; ++dvt) {
                     S[dkt][dvt] = mfma16x16x32(Kh, Vh[dvt], S[dkt][dvt]);
@@ -229,20 +261,21 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4_
 // Main pass over one (chunk, head).  Starting state: prefix[item][h] if
 // prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
 // chunk is a whole sequence (no prefix), the final state is written to
-// state_out/z_out (if given).  Y goes to y[t][h*D + j].
+// state_out/z_out (if given).  Y goes to y[t][h*D + j].  k16 must be 16.
 template <bool NORM, typename OutT>
 __global__ __launch_bounds__(NT, 1) void k_prefill_main(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
     const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
-    float* state_out, float* z_out) {
+    float* state_out, float* z_out, int k16) {
     __shared__ SmemMain sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
     const int h = blockIdx.y;
     Item it;
     if (!decode_item(map, blockIdx.x, it)) return;
 
-    // P tiles above the diagonal are read by the P.V product but never written.
+    // P^T tiles with key tile > query tile are read by the P.V product but
+    // never written: they stay zero.
     for (int i = tid; i < TB * PS / 2; i += NT) {
         ((uint32_t*)sm.ph)[i] = 0u;
         ((uint32_t*)sm.pl)[i] = 0u;
@@ -289,7 +322,7 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
                 const int r = (tid >> 4) + 16 * j;
                 float f[8];
                 silu8(rq[j], f);
-                store_split8(f, sm.qh + r * LS + col, sm.ql + r * LS + col);
+                store_split8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
                 if (NORM) {
                     float part = 0.f;
 #pragma unroll
@@ -318,7 +351,8 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
             sm.z[tid] += s;  // read again only after the next block's first barrier
         }
 
-        // ---- P^T tiles (16 keys x 16 queries), causal, shared through LDS ----
+        // ---- P = phi(Q) phi(K)^T on 16 x 16 tiles (query tile qt >= key tile kt),
+        //      causal mask, stored transposed as P^T[key][query] ----
         {
             const int ntau = nks == 2 ? 10 : 3;
             for (int tau = wave; tau < ntau; tau += 4) {
@@ -327,32 +361,37 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const int ko = (16 * kt + c) * LS + 32 * s + 8 * g;
-                    const int qo = (16 * qt + c) * LS + 32 * s + 8 * g;
-                    const bf16x8_t ah = as_bf16x8(*(const uint4*)&sm.kh[ko]);
-                    const bf16x8_t al = as_bf16x8(*(const uint4*)&sm.kl[ko]);
-                    const bf16x8_t bh = as_bf16x8(*(const uint4*)&sm.qh[qo]);
-                    const bf16x8_t bl = as_bf16x8(*(const uint4*)&sm.ql[qo]);
+                    const bf16x8_t ah = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
+                    const bf16x8_t al = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
+                    const bf16x8_t bh = row_operand(sm.kh, KS, 16 * kt + c, 32 * s, g, k16);
+                    const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 32 * s, g, k16);
                     acc = mfma16x16x32(ah, bh, acc);
                     acc = mfma16x16x32(ah, bl, acc);
                     acc = mfma16x16x32(al, bh, acc);
                 }
-                // acc[i]: key 16kt + 4g + i, query 16qt + c; keep key <= query
+                // acc[i]: query 16qt + 4g + i, key 16kt + c; keep key <= query
                 if (kt == qt) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (4 * g + i > c) acc[i] = 0.f;
+                        if (c > 4 * g + i) acc[i] = 0.f;
                 }
                 uint2 pkh, pkl;
                 split2(acc[0], acc[1], pkh.x, pkl.x);
                 split2(acc[2], acc[3], pkh.y, pkl.y);
-                *(uint2*)&sm.ph[(16 * qt + c) * PS + 16 * kt + 4 * g] = pkh;
-                *(uint2*)&sm.pl[(16 * qt + c) * PS + 16 * kt + 4 * g] = pkl;
+                const int po = (16 * kt + c) * PS + 16 * qt + 4 * g;
+                *(uint2*)&sm.ph[po] = pkh;
+                *(uint2*)&sm.pl[po] = pkl;
                 if (NORM) {
-                    float rs = acc[0] + acc[1] + acc[2] + acc[3];
-                    rs += __shfl_xor(rs, 16, 64);
-                    rs += __shfl_xor(rs, 32, 64);
-                    if (g == 0) sm.denp[kt * TB + 16 * qt + c] = rs;
+                    // row sums over this tile's 16 keys (the 16 lanes of a group)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float rs = acc[i];
+                        rs += __shfl_xor(rs, 1, 64);
+                        rs += __shfl_xor(rs, 2, 64);
+                        rs += __shfl_xor(rs, 4, 64);
+                        rs += __shfl_xor(rs, 8, 64);
+                        if (c == 0) sm.denp[kt * TB + 16 * qt + 4 * g + i] = rs;
+                    }
                 }
             }
         }
@@ -370,17 +409,13 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks < nks) {
-                    const int r0 = 32 * ks + 8 * g;
-                    const bf16x8_t ah = as_bf16x8(lds_read_tr4(sm.vh, LS, r0, c0, c),
-                                                  lds_read_tr4(sm.vh, LS, r0 + 4, c0, c));
-                    const bf16x8_t al = as_bf16x8(lds_read_tr4(sm.vl, LS, r0, c0, c),
-                                                  lds_read_tr4(sm.vl, LS, r0 + 4, c0, c));
+                    const bf16x8_t ah = tr_operand(sm.vh, KS, 32 * ks, c0, g, c);
+                    const bf16x8_t al = tr_operand(sm.vl, KS, 32 * ks, c0, g, c);
 #pragma unroll
                     for (int qt = 0; qt < 4; ++qt) {
                         if (qt < nqt && (ks == 0 || qt >= 2)) {
-                            const int po = (16 * qt + c) * PS + 32 * ks + 8 * g;
-                            const bf16x8_t bh = as_bf16x8(*(const uint4*)&sm.ph[po]);
-                            const bf16x8_t bl = as_bf16x8(*(const uint4*)&sm.pl[po]);
+                            const bf16x8_t bh = tr_operand(sm.ph, PS, 32 * ks, 16 * qt, g, c);
+                            const bf16x8_t bl = tr_operand(sm.pl, PS, 32 * ks, 16 * qt, g, c);
                             acc[dvt][qt] = mfma16x16x32(ah, bh, acc[dvt][qt]);
                             acc[dvt][qt] = mfma16x16x32(ah, bl, acc[dvt][qt]);
                             acc[dvt][qt] = mfma16x16x32(al, bh, acc[dvt][qt]);
@@ -399,9 +434,8 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
 #pragma unroll
                 for (int qt = 0; qt < 4; ++qt) {
                     if (qt < nqt) {
-                        const int o = (16 * qt + c) * LS + 32 * s + 4 * g;
-                        const bf16x8_t Bh = as_bf16x8(*(const i16x4_t*)&sm.qh[o], *(const i16x4_t*)&sm.qh[o + 16]);
-                        const bf16x8_t Bl = as_bf16x8(*(const i16x4_t*)&sm.ql[o], *(const i16x4_t*)&sm.ql[o + 16]);
+                        const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
+                        const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
                         acc[dvt][qt] = mfma16x16x32(Ah, Bh, acc[dvt][qt]);
                         acc[dvt][qt] = mfma16x16x32(Ah, Bl, acc[dvt][qt]);
                         acc[dvt][qt] = mfma16x16x32(Al, Bh, acc[dvt][qt]);
