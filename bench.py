@@ -75,7 +75,7 @@ def bench_prefill(args, torch, lib, _lib, inputs):
     dev = q.device
     out = torch.empty((1, T, H * d), dtype=torch.float32, device=dev)
     state_out = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
-    opt = _lib.options(block_size=64, gated=True)
+    opt = _lib.options(block_size=args.block, gated=True)
     nbytes = lib.la_prefill_workspace_bytes(1, T, H, d, _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32,
                                             ctypes.byref(opt))
     ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
@@ -212,6 +212,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=262144)
+    ap.add_argument("--block", type=int, default=0, help="block size (0 = library default)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -105,7 +105,7 @@ def status_string(status: int) -> str:
         return "status %d" % status
 
 
-def options(block_size=64, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
+def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
             chunk_tokens=0) -> Options:
     o = load().la_default_options()
     o.block_size = int(block_size)

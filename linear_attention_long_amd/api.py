@@ -45,7 +45,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
 
 
 def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=False,
-               block_size=64, norm_group=0, rms_eps=1e-6, chunk_tokens=0,
+               block_size=0, norm_group=0, rms_eps=1e-6, chunk_tokens=0,
                out_dtype=torch.float32, return_state=True, stream=None):
     """Prefill of Bt equal-length sequences.
 
@@ -90,7 +90,7 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
 
 
 def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=None, z_in=None,
-                      *, normalized=False, block_size=64, norm_group=0, rms_eps=1e-6,
+                      *, normalized=False, block_size=0, norm_group=0, rms_eps=1e-6,
                       chunk_tokens=0, out_dtype=torch.float32, return_state=True, stream=None):
     """Prefill of a packed batch.  q, k, v: [total_T, H, d]; cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.

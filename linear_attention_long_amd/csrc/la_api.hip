@@ -20,10 +20,12 @@ using namespace la;
 
 namespace {
 
-constexpr int kDefaultBlock = 64;
-constexpr int kMinAutoChunk = 1024;
+constexpr int kMfmaDefaultBlock = 32;   // bf16 d=128: two workgroups per CU
+constexpr int kValuDefaultBlock = 64;
+constexpr int kStateTile = 64;          // tile of the chunk-state kernel (any block size)
+constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
-constexpr int64_t kTargetItems = 1024;  // (chunk, head) workgroups aimed for: ~4 per CU
+constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
 
 struct Opts {
     int block;
@@ -53,7 +55,8 @@ struct Timer {
 };
 
 struct Plan {
-    bool mfma;         // bf16, d = 128, block 64: matrix-core kernels
+    int block;         // resolved block size
+    bool mfma;         // bf16, d = 128, block 32 or 64: matrix-core kernels
     bool chunked;      // some sequence spans more than one chunk
     bool varlen;
     int C;             // tokens per chunk
@@ -75,8 +78,9 @@ inline bool dtype_ok(la_dtype_t t) { return t == LA_DTYPE_F32 || t == LA_DTYPE_B
 la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
     const la_options_t def = la_default_options();
     const la_options_t& x = opt ? *opt : def;
-    o.block = x.block_size == 0 ? kDefaultBlock : x.block_size;
-    if (o.block != 32 && o.block != 64 && o.block != 128 && o.block != 256) return LA_ERR_UNSUPPORTED;
+    o.block = x.block_size;
+    if (o.block != 0 && o.block != 32 && o.block != 64 && o.block != 128 && o.block != 256)
+        return LA_ERR_UNSUPPORTED;
     if (x.normalized != 0 && x.normalized != 1) return LA_ERR_INVALID_ARGUMENT;
     if (x.gated != 0 && x.gated != 1) return LA_ERR_INVALID_ARGUMENT;
     o.normalized = x.normalized == 1;
@@ -116,7 +120,9 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
                la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o) {
     Plan p{};
     p.varlen = varlen;
-    p.mfma = in_dtype == LA_DTYPE_BF16 && d == 128 && o.block == 64;
+    p.block = o.block;
+    if (p.block == 0) p.block = (in_dtype == LA_DTYPE_BF16 && d == 128) ? kMfmaDefaultBlock : kValuDefaultBlock;
+    p.mfma = in_dtype == LA_DTYPE_BF16 && d == 128 && (p.block == 32 || p.block == 64);
     p.C = auto_chunk(total_T, H, (int)max_seqlen, o);
     p.chunked = max_seqlen > p.C;
     if (!p.chunked) {
@@ -136,6 +142,20 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
     if (o.gated && out_dtype != LA_DTYPE_F32) off += align256((size_t)total_T * H * d * sizeof(float));
     p.total = off;
     return p;
+}
+
+// Gate kernel choice: registers-resident groups of 256/512/1024/2048 features,
+// else the general loop.
+template <typename XT, typename OT>
+void launch_gate(unsigned blocks, hipStream_t st, const float* y, const XT* x, const float* w,
+                 OT* out, int64_t ntok, int F, int G, float eps) {
+    switch (G) {
+        case 256: k_gate4<XT, OT, 1><<<blocks, 256, 0, st>>>(y, x, w, out, ntok, F, G, eps); break;
+        case 512: k_gate4<XT, OT, 2><<<blocks, 256, 0, st>>>(y, x, w, out, ntok, F, G, eps); break;
+        case 1024: k_gate4<XT, OT, 4><<<blocks, 256, 0, st>>>(y, x, w, out, ntok, F, G, eps); break;
+        case 2048: k_gate4<XT, OT, 8><<<blocks, 256, 0, st>>>(y, x, w, out, ntok, F, G, eps); break;
+        default: k_gate<XT, OT><<<blocks, 256, 0, st>>>(y, x, w, out, ntok, F, G, eps); break;
+    }
 }
 
 template <typename InT, typename OutT>
@@ -182,8 +202,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     if (p.chunked) {
         tm.before();
         if (p.mfma) {
-            if (norm) mf::k_chunk_state<true><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
-            else mf::k_chunk_state<false><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            if (norm) mf::k_chunk_state<true, kStateTile><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            else mf::k_chunk_state<false, kStateTile><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
         } else if (d == 128) {
             if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
             else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
@@ -211,17 +231,22 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const uint16_t* qb = (const uint16_t*)q;
         const uint16_t* kb = (const uint16_t*)k;
         const uint16_t* vb = (const uint16_t*)v;
-        if (y_is_f32) {
-            if (norm) mf::k_prefill_main<true, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out, 16);
-            else mf::k_prefill_main<false, float><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (float*)ydst, p.chunked ? nullptr : state_out, nullptr, 16);
+        float* so = p.chunked ? nullptr : state_out;
+        float* zo = p.chunked ? nullptr : z_out;
+#define LA_MF_MAIN(NN, YT, TBV) \
+    mf::k_prefill_main<NN, YT, TBV><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
+        if (p.block == 32) {
+            if (y_is_f32) { if (norm) LA_MF_MAIN(true, float, 32); else LA_MF_MAIN(false, float, 32); }
+            else { if (norm) LA_MF_MAIN(true, uint16_t, 32); else LA_MF_MAIN(false, uint16_t, 32); }
         } else {
-            if (norm) mf::k_prefill_main<true, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out, 16);
-            else mf::k_prefill_main<false, uint16_t><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (uint16_t*)ydst, p.chunked ? nullptr : state_out, nullptr, 16);
+            if (y_is_f32) { if (norm) LA_MF_MAIN(true, float, 64); else LA_MF_MAIN(false, float, 64); }
+            else { if (norm) LA_MF_MAIN(true, uint16_t, 64); else LA_MF_MAIN(false, uint16_t, 64); }
         }
+#undef LA_MF_MAIN
     } else {
 #define LA_VALU_MAIN(DD, YT, NN)                                                                \
     vk::k_valu_main<DD, InT, YT, NN><<<grid, vk::NT, 0, st>>>(                                  \
-        (const InT*)q, (const InT*)k, (const InT*)v, map, H, o.block, buf, p.stride, state_in,  \
+        (const InT*)q, (const InT*)k, (const InT*)v, map, H, p.block, buf, p.stride, state_in,  \
         z_in, (YT*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out)
         if (d == 128) {
             if (y_is_f32) { if (norm) LA_VALU_MAIN(128, float, true); else LA_VALU_MAIN(128, float, false); }
@@ -241,8 +266,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const unsigned blocks = (unsigned)((units + 3) / 4);
         const float* yf = need_yws ? ybuf_f : (const float*)out;
         tm.before();
-        if (o.group % 256 == 0) k_gate4<InT, OutT><<<blocks, 256, 0, st>>>(yf, (const InT*)x, w, (OutT*)out, total_T, F, o.group, o.eps);
-        else k_gate<InT, OutT><<<blocks, 256, 0, st>>>(yf, (const InT*)x, w, (OutT*)out, total_T, F, o.group, o.eps);
+        launch_gate<InT, OutT>(blocks, st, yf, (const InT*)x, w, (OutT*)out, total_T, F, o.group, o.eps);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
     }
@@ -308,7 +332,7 @@ extern "C" {
 
 la_options_t la_default_options(void) {
     la_options_t o;
-    o.block_size = kDefaultBlock;
+    o.block_size = 0;
     o.normalized = 0;
     o.gated = 0;
     o.norm_group = 0;
@@ -483,8 +507,7 @@ la_status_t la_decode_step(const void* q, const void* k, const void* v, const vo
         tm.before();
 #define LA_GATE(XT, OT)                                                                                     \
     do {                                                                                                    \
-        if (o.group % 256 == 0) k_gate4<XT, OT><<<blocks, 256, 0, st>>>(yf, (const XT*)x_gate, rms_weight, (OT*)out, N, F, o.group, o.eps); \
-        else k_gate<XT, OT><<<blocks, 256, 0, st>>>(yf, (const XT*)x_gate, rms_weight, (OT*)out, N, F, o.group, o.eps); \
+        launch_gate<XT, OT>(blocks, st, yf, (const XT*)x_gate, rms_weight, (OT*)out, N, F, o.group, o.eps); \
     } while (0)
         if (in_dtype == LA_DTYPE_BF16) {
             if (out_dtype == LA_DTYPE_BF16) LA_GATE(uint16_t, uint16_t); else LA_GATE(uint16_t, float);

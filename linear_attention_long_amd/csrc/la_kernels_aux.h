@@ -109,8 +109,32 @@ __global__ __launch_bounds__(256) void k_gate(const float* y, const XT* __restri
     }
 }
 
-// Vectorised gate for G % 256 == 0: each lane handles 4 consecutive features.
-template <typename XT, typename OutT>
+template <typename XT> struct Vec4In;
+template <> struct Vec4In<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+        const float4 t = *(const float4*)p;
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    }
+};
+template <> struct Vec4In<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[4]) {
+        const uint2 t = *(const uint2*)p;
+        v[0] = bf16_lo_to_f32(t.x); v[1] = bf16_hi_to_f32(t.x);
+        v[2] = bf16_lo_to_f32(t.y); v[3] = bf16_hi_to_f32(t.y);
+    }
+};
+template <typename OutT> __device__ __forceinline__ void store_vec4(OutT* p, const float (&v)[4]);
+template <> __device__ __forceinline__ void store_vec4<float>(float* p, const float (&v)[4]) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store_vec4<uint16_t>(uint16_t* p, const float (&v)[4]) {
+    *(uint2*)p = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+// Gate for groups of G = 256 * NC features: one wave per (token, group), each
+// lane holds 4 * NC features in registers between the sum of squares and the
+// scaling, and issues all of its loads before using any of them.
+template <typename XT, typename OutT, int NC>
 __global__ __launch_bounds__(256) void k_gate4(const float* y, const XT* __restrict__ x,
                                                const float* __restrict__ w, OutT* out, int64_t ntok,
                                                int F, int G, float eps) {
@@ -120,24 +144,28 @@ __global__ __launch_bounds__(256) void k_gate4(const float* y, const XT* __restr
     const int64_t tok = unit / ngroups;
     if (tok >= ntok) return;
     const int grp = (int)(unit - tok * ngroups);
-    const size_t base = (size_t)tok * F + (size_t)grp * G;
+    const size_t base = (size_t)tok * F + (size_t)grp * G + 4 * lane;
+    float yv[NC][4], xv[NC][4];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) Vec4In<float>::load(y + base + 256 * j, yv[j]);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) Vec4In<XT>::load(x + base + 256 * j, xv[j]);
     float ss = 0.f;
-    for (int f = 4 * lane; f < G; f += 256) {
-        const float4 a = *(const float4*)(y + base + f);
-        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
-    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += yv[j][e] * yv[j][e];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
     const float r = 1.0f / sqrtf(ss / (float)G + eps);
-    for (int f = 4 * lane; f < G; f += 256) {
-        const float4 a = *(const float4*)(y + base + f);
-        float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float wf = w ? w[grp * G + f + e] : 1.f;
-            store_from_f32<OutT>(out + base + f + e,
-                                 av[e] * r * wf * sigmoid(load_as_f32<XT>(x + base + f + e)));
-        }
+    for (int j = 0; j < NC; ++j) {
+        float wv[4] = {1.f, 1.f, 1.f, 1.f};
+        if (w) Vec4In<float>::load(w + (size_t)grp * G + 4 * lane + 256 * j, wv);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = yv[j][e] * r * wv[e] * sigmoid(xv[j][e]);
+        store_vec4<OutT>(out + base + 256 * j, o);
     }
 }
 

@@ -3,16 +3,18 @@
 // Method (page "MiniMax-Text-01 405B MoE模型架构与训练策略解析" section 2.1 and
 // page "六十四：MiniMax-01" section 3): per head, phi = SiLU on q, k, v;
 // y_t = phi(q_t)^T S_t with S_t = S_{t-1} + phi(k_t) phi(v_t)^T, the sum
-// including token t.  Evaluated in blocks of 64 tokens: inside a block the
+// including token t.  Evaluated in blocks of TB = 32 or 64 tokens: inside a block the
 // masked quadratic form (phi(Q) phi(K)^T (.) M) phi(V), M = lower triangle
 // with the diagonal; across blocks phi(Q) S_prev with the fp32 state carried
 // in registers; after the block S += phi(K)^T phi(V).
 //
 // gfx950 design:
-//  * one workgroup = 4 waves = one (chunk, head); wave w owns value columns
+//  * one workgroup = 4 waves = one (chunk, head); with TB = 32 the LDS of a
+//    workgroup is ~64 KB and two workgroups share a CU, so one's SiLU/split
+//    VALU work overlaps the other's matrix-core work; wave w owns value columns
 //    [32w, 32w+32) of the state (128 x 32 fp32 = 64 accumulator registers per
 //    lane) and of the output, so the state never leaves registers;
-//  * q, k, v of a 64-token block are staged once into LDS as bf16 hi/lo pairs
+//  * q, k, v of a block are staged once into LDS as bf16 hi/lo pairs
 //    of phi(x) (hi = RNE(phi), lo = RNE(phi - hi)), row-major;
 //  * every product takes three bf16 MFMAs (hi*hi + hi*lo + lo*hi), which
 //    carries ~16 significant bits of each operand: with single bf16 operands
@@ -21,7 +23,7 @@
 //  * LDS traffic is arranged to be free of bank conflicts (measured with the
 //    SQ_LDS_BANK_CONFLICT counter on gfx950): contractions over tokens read
 //    transposed fragments with ds_read_b64_tr_b16 from row-major K, V and P^T
-//    tiles at a row stride of 144 (K, V) or 80 (P^T) elements, each 16-lane
+//    tiles at a row stride of 144 (K, V) or TB + 16 (P^T) elements, each 16-lane
 //    group covering four consecutive rows; contractions over the head dim
 //    read two 8-byte pieces per lane (never 16-byte row reads, which conflict)
 //    from Q and K rows.  The k index of every MFMA is permuted so that a
@@ -41,17 +43,26 @@ namespace la {
 namespace mf {
 
 constexpr int D = 128;   // head dim
-constexpr int TB = 64;   // tokens per block
 constexpr int NT = 256;  // threads per workgroup
 constexpr int QS = 136;  // LDS row stride of the Q tile (bf16 elements)
 constexpr int KS = 144;  // LDS row stride of the K and V tiles
-constexpr int PS = 80;   // LDS row stride of the P^T tile ([key][query])
 // 16 bytes after each LDS array: neighbouring hi/lo arrays then are not a
 // multiple of 512 bytes apart, so the compiler cannot fuse a read of one with
 // a read of the other into a ds_read2st64 that lands both halves in the same
 // banks.
 constexpr int APAD = 8;
 
+template <int TB>
+struct Tile {
+    static_assert(TB == 32 || TB == 64, "block of 32 or 64 tokens");
+    static constexpr int PS = TB + 16;   // LDS row stride of P^T ([key][query])
+    static constexpr int NJ = TB / 16;   // staged rows per thread
+    static constexpr int NQT = TB / 16;  // 16-row query tiles
+    static constexpr int NKS = TB / 32;  // 32-key steps
+    static constexpr int WG_PER_CU = TB == 32 ? 2 : 1;
+};
+
+template <int TB>
 struct __attribute__((aligned(16))) SmemMain {
     __attribute__((aligned(16))) uint16_t qh[TB * QS + APAD];
     __attribute__((aligned(16))) uint16_t ql[TB * QS + APAD];
@@ -59,31 +70,32 @@ struct __attribute__((aligned(16))) SmemMain {
     __attribute__((aligned(16))) uint16_t kl[TB * KS + APAD];
     __attribute__((aligned(16))) uint16_t vh[TB * KS + APAD];
     __attribute__((aligned(16))) uint16_t vl[TB * KS + APAD];
-    __attribute__((aligned(16))) uint16_t ph[TB * PS + APAD];  // P^T[key][query], bf16 hi
-    __attribute__((aligned(16))) uint16_t pl[TB * PS + APAD];  // P^T[key][query], bf16 lo
-    float denp[4 * TB];    // normalised mode: row sums of P per 16-key tile
-    float zq[TB];          // normalised mode: phi(q) . z_prev per row
-    float zpart[16 * D];   // normalised mode: column sums of phi(k) per row group
-    float z[D];            // normalised mode: running normaliser
+    __attribute__((aligned(16))) uint16_t ph[TB * Tile<TB>::PS + APAD];  // P^T[key][query], hi
+    __attribute__((aligned(16))) uint16_t pl[TB * Tile<TB>::PS + APAD];  // P^T[key][query], lo
+    float denp[Tile<TB>::NQT * TB];  // normalised mode: row sums of P per 16-key tile
+    float zq[TB];                    // normalised mode: phi(q) . z_prev per row
+    float zpart[4 * D];              // normalised mode: column sums of phi(k) per wave
+    float z[D];                      // normalised mode: running normaliser
 };
 
-// (only transposing reads, which are never fused: no padding, so two
-// workgroups fit in one CU's 160 KB)
+// (only transposing reads, which are never fused: no padding)
+template <int TB>
 struct __attribute__((aligned(16))) SmemState {
     __attribute__((aligned(16))) uint16_t kh[TB * KS];
     __attribute__((aligned(16))) uint16_t kl[TB * KS];
     __attribute__((aligned(16))) uint16_t vh[TB * KS];
     __attribute__((aligned(16))) uint16_t vl[TB * KS];
-    float zpart[16 * D];
+    float zpart[4 * D];
 };
 
-// Thread tid loads rows (tid>>4) + 16j, j = 0..3, columns (tid&15)*8 .. +7 of
-// a 64 x 128 bf16 tile of one head; rows at or past nvalid read as zero.
-__device__ __forceinline__ void load_tile(uint4 (&dst)[4], const uint16_t* __restrict__ src,
+// Thread tid loads rows (tid>>4) + 16j, j < NJ, columns (tid&15)*8 .. +7 of
+// a 16*NJ x 128 bf16 tile of one head; rows at or past nvalid read as zero.
+template <int NJ>
+__device__ __forceinline__ void load_tile(uint4 (&dst)[NJ], const uint16_t* __restrict__ src,
                                           int64_t t0, int nvalid, int H, int h, int tid) {
     const int col = (tid & 15) * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int r = (tid >> 4) + 16 * j;
         if (r < nvalid) {
             dst[j] = *(const uint4*)(src + ((size_t)(t0 + r) * H + h) * D + col);
@@ -114,18 +126,18 @@ __device__ __forceinline__ void store_split8(const float (&f)[8], uint16_t* dh, 
     *(uint4*)dl = lo;
 }
 
-// phi(k) and phi(v) of the block into LDS (hi/lo); with NORM, per-thread
-// column sums of phi(k) over its 4 rows into zpart[tid>>4][col..col+7].
-template <bool NORM>
-__device__ __forceinline__ void stage_kv(const uint4 (&rk)[4], const uint4 (&rv)[4], uint16_t* kh,
-                                         uint16_t* kl, uint16_t* vh, uint16_t* vl, float* zpart,
-                                         int tid) {
+// phi(k) and phi(v) of the block into LDS (hi/lo); with NORM, column sums of
+// phi(k) over the wave's rows into zpart[wave][col..col+7].
+template <bool NORM, int NJ>
+__device__ __forceinline__ void stage_kv(const uint4 (&rk)[NJ], const uint4 (&rv)[NJ],
+                                         uint16_t* kh, uint16_t* kl, uint16_t* vh, uint16_t* vl,
+                                         float* zpart, int tid) {
     const int col = (tid & 15) * 8;
     float zs[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zs[e] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
         const int r = (tid >> 4) + 16 * j;
         float f[8];
         silu8(rk[j], f);
@@ -139,7 +151,14 @@ __device__ __forceinline__ void stage_kv(const uint4 (&rk)[4], const uint4 (&rv)
     }
     if (NORM) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zpart[(tid >> 4) * D + col + e] = zs[e];
+        for (int e = 0; e < 8; ++e) {
+            zs[e] += __shfl_xor(zs[e], 16, 64);
+            zs[e] += __shfl_xor(zs[e], 32, 64);
+        }
+        if ((tid & 63) < 16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zpart[(tid >> 6) * D + col + e] = zs[e];
+        }
     }
 }
 
@@ -165,11 +184,12 @@ __device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, int stride
 // nks*32 rows of the staged block (rows past the data are zero).
 // S[dkt][dvt]: C-layout tile, lane (g, c) holds dv = 32*wave + 16*dvt + c,
 // dk = 16*dkt + 4*g + i.
+template <int NKS>
 __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t* kh,
                                              const uint16_t* kl, const uint16_t* vh,
                                              const uint16_t* vl, int nks, int wave, int g, int c) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
         if (ks < nks) {
             bf16x8_t Vh[2], Vl[2];
 #pragma unroll
@@ -195,12 +215,13 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
 
 // Per-chunk state increment dS = sum_{t in chunk} phi(k_t) phi(v_t)^T (and
 // dz = sum phi(k_t)), written to buf[item][h] = [dS (D*D) | dz (D)].
-template <bool NORM>
+template <bool NORM, int TB>
 __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, ItemMap map,
                                                        int H, float* __restrict__ buf,
                                                        int64_t buf_stride) {
-    __shared__ SmemState sm;
+    using L = Tile<TB>;
+    __shared__ SmemState<TB> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
     const int h = blockIdx.y;
     Item it;
@@ -214,27 +235,23 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     float zacc = 0.f;
 
     const int ntiles = (it.len + TB - 1) / TB;
-    uint4 rk[4], rv[4];
-    load_tile(rk, k, it.t0, min(TB, it.len), H, h, tid);
-    load_tile(rv, v, it.t0, min(TB, it.len), H, h, tid);
+    uint4 rk[L::NJ], rv[L::NJ];
+    load_tile<L::NJ>(rk, k, it.t0, min(TB, it.len), H, h, tid);
+    load_tile<L::NJ>(rv, v, it.t0, min(TB, it.len), H, h, tid);
     for (int ti = 0; ti < ntiles; ++ti) {
         const int nvalid = min(TB, it.len - ti * TB);
         __syncthreads();
-        stage_kv<NORM>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+        stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         if (ti + 1 < ntiles) {
             const int64_t t1 = it.t0 + (int64_t)(ti + 1) * TB;
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
-            load_tile(rk, k, t1, nv1, H, h, tid);
-            load_tile(rv, v, t1, nv1, H, h, tid);
+            load_tile<L::NJ>(rk, k, t1, nv1, H, h, tid);
+            load_tile<L::NJ>(rv, v, t1, nv1, H, h, tid);
         }
         __syncthreads();
-        if (NORM && tid < D) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s += sm.zpart[i * D + tid];
-            zacc += s;
-        }
-        state_update(S, sm.kh, sm.kl, sm.vh, sm.vl, nvalid <= 32 ? 1 : 2, wave, g, c);
+        if (NORM && tid < D)
+            zacc += (sm.zpart[tid] + sm.zpart[D + tid]) + (sm.zpart[2 * D + tid] + sm.zpart[3 * D + tid]);
+        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nvalid <= 32 ? 1 : L::NKS, wave, g, c);
     }
     float* dst = buf + ((size_t)blockIdx.x * H + h) * buf_stride;
 #pragma unroll
@@ -262,13 +279,15 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4_
 // prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
 // chunk is a whole sequence (no prefix), the final state is written to
 // state_out/z_out (if given).  Y goes to y[t][h*D + j].  k16 must be 16.
-template <bool NORM, typename OutT>
-__global__ __launch_bounds__(NT, 1) void k_prefill_main(
+template <bool NORM, typename OutT, int TB>
+__global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
     const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
     float* state_out, float* z_out, int k16) {
-    __shared__ SmemMain sm;
+    using L = Tile<TB>;
+    constexpr int PS = L::PS;
+    __shared__ SmemMain<TB> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
     const int h = blockIdx.y;
     Item it;
@@ -281,7 +300,7 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
         ((uint32_t*)sm.pl)[i] = 0u;
     }
     if (NORM)
-        for (int i = tid; i < 4 * TB; i += NT) sm.denp[i] = 0.f;
+        for (int i = tid; i < L::NQT * TB; i += NT) sm.denp[i] = 0.f;
 
     const float* s0 = nullptr;
     const float* z0 = nullptr;
@@ -303,22 +322,22 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
     if (NORM && tid < D) sm.z[tid] = z0 ? z0[tid] : 0.f;
 
     const int ntiles = (it.len + TB - 1) / TB;
-    uint4 rq[4], rk[4], rv[4];
-    load_tile(rq, q, it.t0, min(TB, it.len), H, h, tid);
-    load_tile(rk, k, it.t0, min(TB, it.len), H, h, tid);
-    load_tile(rv, v, it.t0, min(TB, it.len), H, h, tid);
+    uint4 rq[L::NJ], rk[L::NJ], rv[L::NJ];
+    load_tile<L::NJ>(rq, q, it.t0, min(TB, it.len), H, h, tid);
+    load_tile<L::NJ>(rk, k, it.t0, min(TB, it.len), H, h, tid);
+    load_tile<L::NJ>(rv, v, it.t0, min(TB, it.len), H, h, tid);
 
     for (int ti = 0; ti < ntiles; ++ti) {
         const int64_t tt0 = it.t0 + (int64_t)ti * TB;
         const int nvalid = min(TB, it.len - ti * TB);
-        const int nks = nvalid <= 32 ? 1 : 2;  // tail pad: 32 or 64 rows
+        const int nks = nvalid <= 32 ? 1 : L::NKS;  // tail pad: 32 or 64 rows
         const int nqt = 2 * nks;
 
         __syncthreads();  // previous block's LDS reads and z update are done
         {
             const int col = (tid & 15) * 8;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < L::NJ; ++j) {
                 const int r = (tid >> 4) + 16 * j;
                 float f[8];
                 silu8(rq[j], f);
@@ -334,22 +353,18 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
                     if ((tid & 15) == 0) sm.zq[r] = part;
                 }
             }
-            stage_kv<NORM>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+            stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         }
         if (ti + 1 < ntiles) {
             const int64_t t1 = tt0 + TB;
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
-            load_tile(rq, q, t1, nv1, H, h, tid);
-            load_tile(rk, k, t1, nv1, H, h, tid);
-            load_tile(rv, v, t1, nv1, H, h, tid);
+            load_tile<L::NJ>(rq, q, t1, nv1, H, h, tid);
+            load_tile<L::NJ>(rk, k, t1, nv1, H, h, tid);
+            load_tile<L::NJ>(rv, v, t1, nv1, H, h, tid);
         }
         __syncthreads();
-        if (NORM && tid < D) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s += sm.zpart[i * D + tid];
-            sm.z[tid] += s;  // read again only after the next block's first barrier
-        }
+        if (NORM && tid < D)  // read again only after the next block's first barrier
+            sm.z[tid] += (sm.zpart[tid] + sm.zpart[D + tid]) + (sm.zpart[2 * D + tid] + sm.zpart[3 * D + tid]);
 
         // ---- P = phi(Q) phi(K)^T on 16 x 16 tiles (query tile qt >= key tile kt),
         //      causal mask, stored transposed as P^T[key][query] ----
@@ -398,54 +413,69 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
         __syncthreads();
 
         // ---- Y^T = V^T P^T (intra) + S^T Q^T (inter), this wave's 32 columns ----
-        f32x4_t acc[2][4];
+        f32x4_t acc[2][L::NQT];
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < L::NQT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // intra: key steps outer, both value tiles per P^T operand
 #pragma unroll
-        for (int dvt = 0; dvt < 2; ++dvt) {
-            const int c0 = 32 * wave + 16 * dvt;
+        for (int ks = 0; ks < L::NKS; ++ks) {
+            if (ks < nks) {
+                bf16x8_t Ah[2], Al[2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks < nks) {
-                    const bf16x8_t ah = tr_operand(sm.vh, KS, 32 * ks, c0, g, c);
-                    const bf16x8_t al = tr_operand(sm.vl, KS, 32 * ks, c0, g, c);
+                for (int dvt = 0; dvt < 2; ++dvt) {
+                    const int c0 = 32 * wave + 16 * dvt;
+                    Ah[dvt] = tr_operand(sm.vh, KS, 32 * ks, c0, g, c);
+                    Al[dvt] = tr_operand(sm.vl, KS, 32 * ks, c0, g, c);
+                }
 #pragma unroll
-                    for (int qt = 0; qt < 4; ++qt) {
-                        if (qt < nqt && (ks == 0 || qt >= 2)) {
-                            const bf16x8_t bh = tr_operand(sm.ph, PS, 32 * ks, 16 * qt, g, c);
-                            const bf16x8_t bl = tr_operand(sm.pl, PS, 32 * ks, 16 * qt, g, c);
-                            acc[dvt][qt] = mfma16x16x32(ah, bh, acc[dvt][qt]);
-                            acc[dvt][qt] = mfma16x16x32(ah, bl, acc[dvt][qt]);
-                            acc[dvt][qt] = mfma16x16x32(al, bh, acc[dvt][qt]);
+                for (int qt = 0; qt < L::NQT; ++qt) {
+                    if (qt < nqt && (ks == 0 || qt >= 2)) {
+                        const bf16x8_t bh = tr_operand(sm.ph, PS, 32 * ks, 16 * qt, g, c);
+                        const bf16x8_t bl = tr_operand(sm.pl, PS, 32 * ks, 16 * qt, g, c);
+#pragma unroll
+                        for (int dvt = 0; dvt < 2; ++dvt) {
+                            acc[dvt][qt] = mfma16x16x32(Ah[dvt], bh, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(Ah[dvt], bl, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(Al[dvt], bh, acc[dvt][qt]);
                         }
                     }
                 }
             }
+        }
+        // inter: head-dim steps outer; the state's split for both value tiles,
+        // then each Q^T operand feeds both
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t Ah[2], Al[2];
+#pragma unroll
+            for (int dvt = 0; dvt < 2; ++dvt) {
                 uint4 ah, al;
                 split2(S[2 * s][dvt][0], S[2 * s][dvt][1], ah.x, al.x);
                 split2(S[2 * s][dvt][2], S[2 * s][dvt][3], ah.y, al.y);
                 split2(S[2 * s + 1][dvt][0], S[2 * s + 1][dvt][1], ah.z, al.z);
                 split2(S[2 * s + 1][dvt][2], S[2 * s + 1][dvt][3], ah.w, al.w);
-                const bf16x8_t Ah = as_bf16x8(ah), Al = as_bf16x8(al);
+                Ah[dvt] = as_bf16x8(ah);
+                Al[dvt] = as_bf16x8(al);
+            }
 #pragma unroll
-                for (int qt = 0; qt < 4; ++qt) {
-                    if (qt < nqt) {
-                        const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
-                        const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
-                        acc[dvt][qt] = mfma16x16x32(Ah, Bh, acc[dvt][qt]);
-                        acc[dvt][qt] = mfma16x16x32(Ah, Bl, acc[dvt][qt]);
-                        acc[dvt][qt] = mfma16x16x32(Al, Bh, acc[dvt][qt]);
+            for (int qt = 0; qt < L::NQT; ++qt) {
+                if (qt < nqt) {
+                    const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
+                    const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
+#pragma unroll
+                    for (int dvt = 0; dvt < 2; ++dvt) {
+                        acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bh, acc[dvt][qt]);
+                        acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bl, acc[dvt][qt]);
+                        acc[dvt][qt] = mfma16x16x32(Al[dvt], Bh, acc[dvt][qt]);
                     }
                 }
             }
         }
         // acc[dvt][qt][i]: query 16qt + c, feature 32*wave + 16*dvt + 4g + i
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
+        for (int qt = 0; qt < L::NQT; ++qt) {
             const int row = 16 * qt + c;
             if (qt < nqt && row < nvalid) {
                 float sc = 1.f;
@@ -461,7 +491,7 @@ __global__ __launch_bounds__(NT, 1) void k_prefill_main(
         }
 
         // ---- S += phi(K)^T phi(V) ----
-        state_update(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
     }
 
     if (!prefix) {

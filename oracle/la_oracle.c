@@ -77,6 +77,7 @@ static void recurrent_token(const double* qt, const double* kt, const double* vt
 
 typedef struct {
     const double *q, *k, *v;
+    const float *qf, *kf, *vf;  /* float inputs (widened exactly) instead of q, k, v */
     const int64_t* cu;
     int32_t nseq, H, d, normalized;
     const double *state_in, *z_in;
@@ -109,10 +110,13 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
     double* b = (double*)malloc((size_t)d * sizeof(double));
     double* c = (double*)malloc((size_t)d * sizeof(double));
     double* yt = (double*)malloc((size_t)d * sizeof(double));
-    if (!S || !z || !a || !b || !c || !yt) {
-        free(S); free(z); free(a); free(b); free(c); free(yt);
+    double* qt = (double*)malloc((size_t)3 * d * sizeof(double));
+    if (!S || !z || !a || !b || !c || !yt || !qt) {
+        free(S); free(z); free(a); free(b); free(c); free(yt); free(qt);
         return -1;
     }
+    double* kt = qt + d;
+    double* vt = qt + 2 * d;
     if (J->state_in)
         memcpy(S, J->state_in + ((size_t)s * H + h) * d * d, (size_t)d * d * sizeof(double));
     if (J->z_in)
@@ -128,7 +132,16 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
         } else if (si < J->nsample && J->sample_idx[si] == t) {
             dst = yt;
         }
-        recurrent_token(J->q + off, J->k + off, J->v + off, d, J->normalized, S, z, a, b, c, dst);
+        if (J->qf) {
+            for (int i = 0; i < d; i++) {
+                qt[i] = (double)J->qf[off + i];
+                kt[i] = (double)J->kf[off + i];
+                vt[i] = (double)J->vf[off + i];
+            }
+            recurrent_token(qt, kt, vt, d, J->normalized, S, z, a, b, c, dst);
+        } else {
+            recurrent_token(J->q + off, J->k + off, J->v + off, d, J->normalized, S, z, a, b, c, dst);
+        }
         if (J->sample_idx && dst) {
             /* several equal sample indices all receive this token's output */
             while (si < J->nsample && J->sample_idx[si] == t) {
@@ -141,7 +154,7 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
         memcpy(J->state_out + ((size_t)s * H + h) * d * d, S, (size_t)d * d * sizeof(double));
     if (J->z_out)
         memcpy(J->z_out + ((size_t)s * H + h) * d, z, (size_t)d * sizeof(double));
-    free(S); free(z); free(a); free(b); free(c); free(yt);
+    free(S); free(z); free(a); free(b); free(c); free(yt); free(qt);
     return 0;
 }
 
@@ -300,7 +313,27 @@ int lao_prefill(const double* q, const double* k, const double* v,
             if (i && sample_idx[i] < sample_idx[i - 1]) return -1;
         }
     }
-    job_t J = {q, k, v, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+               y, state_out, z_out, sample_idx, nsample, nthreads, 0, 0};
+    return run_job(&J);
+}
+
+/* Same as lao_prefill with float inputs (bf16 or fp32 values), each widened
+ * exactly to double as it is used: for inputs too large to hold in double. */
+int lao_prefill_f32in(const float* q, const float* k, const float* v,
+                      const int64_t* cu_seqlens, int32_t nseq, int32_t H, int32_t d,
+                      const double* state_in, const double* z_in, int32_t normalized,
+                      double* y, double* state_out, double* z_out,
+                      const int64_t* sample_idx, int64_t nsample, int32_t nthreads)
+{
+    if (!q || !k || !v || !y || H < 1 || d < 1 || check_cu(cu_seqlens, nseq)) return -1;
+    if (sample_idx) {
+        for (int64_t i = 0; i < nsample; i++) {
+            if (sample_idx[i] < 0 || sample_idx[i] >= cu_seqlens[nseq]) return -1;
+            if (i && sample_idx[i] < sample_idx[i - 1]) return -1;
+        }
+    }
+    job_t J = {NULL, NULL, NULL, q, k, v, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
                y, state_out, z_out, sample_idx, nsample, nthreads, 0, 0};
     return run_job(&J);
 }
@@ -314,7 +347,7 @@ int lao_prefill_blocked(const double* q, const double* k, const double* v,
                         int32_t block, int32_t fp32, int32_t nthreads)
 {
     if (!q || !k || !v || !y || H < 1 || d < 1 || block < 1 || check_cu(cu_seqlens, nseq)) return -1;
-    job_t J = {q, k, v, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
                y, state_out, z_out, NULL, 0, nthreads, block, fp32 ? 1 : 0};
     return run_job(&J);
 }

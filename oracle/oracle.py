@@ -35,6 +35,7 @@ _lock = threading.Lock()
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
+_fp32 = ctypes.POINTER(ctypes.c_float)
 _i64p = ctypes.POINTER(ctypes.c_int64)
 
 
@@ -60,6 +61,11 @@ def _load():
             lib.lao_prefill.argtypes = [_dp, _dp, _dp, _i64p, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _dp, _dp, ctypes.c_int32, _dp, _dp, _dp,
                                         _i64p, ctypes.c_int64, ctypes.c_int32]
+            lib.lao_prefill_f32in.restype = ctypes.c_int
+            lib.lao_prefill_f32in.argtypes = [_fp32, _fp32, _fp32, _i64p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, _dp, _dp,
+                                              ctypes.c_int32, _dp, _dp, _dp, _i64p, ctypes.c_int64,
+                                              ctypes.c_int32]
             lib.lao_prefill_blocked.restype = ctypes.c_int
             lib.lao_prefill_blocked.argtypes = [_dp, _dp, _dp, _i64p, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.c_int32, _dp, _dp,
@@ -205,6 +211,41 @@ def forward(q, k, v, x=None, w=None, cu_seqlens=None, state_in=None, z_in=None,
     y = y.reshape(total, H * d)
     if gated:
         y = gate(y, _f64(x).reshape(total, H * d), w, norm_group, eps)
+    return y, so, zo
+
+
+def _f32(a):
+    """Float inputs as a C-contiguous float32 numpy array (bf16 widens exactly)."""
+    if hasattr(a, "detach"):
+        import torch
+
+        a = a.detach().to("cpu")
+        if a.dtype != torch.float32:
+            a = a.to(torch.float32)
+        return np.ascontiguousarray(a.numpy())
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def prefill_sampled_f32(q, k, v, sample_idx, cu_seqlens=None, state_in=None, z_in=None,
+                        normalized=False, nthreads=None):
+    """:func:`prefill` at the listed tokens for float32-valued inputs (bf16 or
+    fp32 values), widened to double one token at a time inside the oracle."""
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    total, H, d = q.shape
+    cu = _cu_array(cu_seqlens, total)
+    nseq = len(cu) - 1
+    sample_idx = np.ascontiguousarray(np.asarray(sample_idx, dtype=np.int64))
+    y = np.zeros((len(sample_idx), H, d))
+    so = np.zeros((nseq, H, d, d))
+    zo = np.zeros((nseq, H, d))
+    fp = lambda a: a.ctypes.data_as(_fp32)
+    rc = lib.lao_prefill_f32in(fp(q), fp(k), fp(v), cu.ctypes.data_as(_i64p), nseq, H, d,
+                               _ptr(_f64(state_in)), _ptr(_f64(z_in)), int(bool(normalized)),
+                               _ptr(y), _ptr(so), _ptr(zo), sample_idx.ctypes.data_as(_i64p),
+                               len(sample_idx), _nthreads(nthreads))
+    if rc != 0:
+        raise ValueError("lao_prefill_f32in rejected its arguments")
     return y, so, zo
 
 

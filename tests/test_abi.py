@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_default_options(lib):
     o = lib.la_default_options()
-    assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (64, 0, 0, 0, 0)
+    assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (0, 0, 0, 0, 0)
     assert abs(o.rms_eps - 1e-6) < 1e-12
 
 
@@ -69,11 +69,13 @@ def opt(**kw):
 def test_workspace_queries(lib):
     o = opt()
     # one chunk per sequence, ungated: nothing needed
-    assert lib.la_prefill_workspace_bytes(1, 1024, 2, 64, F32, F32, ctypes.byref(o)) == 0
-    # 1M tokens x 8 heads: chunked, chunk 8192 -> 128 chunks x 8 heads x d^2 floats
-    assert lib.la_prefill_chunk_tokens(1, 1 << 20, 1 << 20, 8, 128, BF16, ctypes.byref(o)) == 8192
+    assert lib.la_prefill_workspace_bytes(1, 512, 2, 64, F32, F32, ctypes.byref(o)) == 0
+    # two 512-token chunks x 2 heads x d^2 floats
+    assert lib.la_prefill_workspace_bytes(1, 1024, 2, 64, F32, F32, ctypes.byref(o)) == 2 * 2 * 64 * 64 * 4
+    # 1M tokens x 8 heads: chunked, chunk 4096 -> 256 chunks x 8 heads x d^2 floats
+    assert lib.la_prefill_chunk_tokens(1, 1 << 20, 1 << 20, 8, 128, BF16, ctypes.byref(o)) == 4096
     nb = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, F32, ctypes.byref(o))
-    assert nb == 128 * 8 * 128 * 128 * 4
+    assert nb == 256 * 8 * 128 * 128 * 4
     # gated with a bf16 output adds an fp32 Y buffer
     g = opt(gated=1)
     nb2 = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, BF16, ctypes.byref(g))

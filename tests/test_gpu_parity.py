@@ -88,42 +88,45 @@ def test_f32_d128_gated_normalized_with_state():
 
 @pytest.mark.parametrize("T", [1, 17, 32, 33, 64, 100, 1000, 2085])
 @pytest.mark.parametrize("gated", [False, True])
-def test_bf16_short_sequences(T, gated):
-    banner("bf16 T=%d gated=%s" % (T, gated))
+@pytest.mark.parametrize("block", [32, 64])
+def test_bf16_short_sequences(T, gated, block):
+    banner("bf16 T=%d gated=%s block=%d" % (T, gated, block))
     H, d = 2, 128
     s = 1.0 / np.sqrt(d)
     q, k, v = (randn((1, T, H, d), 30 + i, s, dtype=torch.bfloat16) for i in range(3))
     x = randn((1, T, H * d), 33, dtype=torch.bfloat16) if gated else None
-    out, S, _ = run_prefill(q, k, v, x)
+    out, S, _ = run_prefill(q, k, v, x, block_size=block)
     ref, Sref, _ = oracle_forward(q, k, v, x)
     assert rel_err(np64(out), ref) <= TOL_BF16
     assert rel_err(np64(S), Sref) <= TOL_BF16
 
 
 @pytest.mark.parametrize("chunk", [64, 1024])
-def test_bf16_chunked_with_state_in(chunk):
-    banner("bf16 chunked chunk=%d" % chunk)
+@pytest.mark.parametrize("block", [32, 64])
+def test_bf16_chunked_with_state_in(chunk, block):
+    banner("bf16 chunked chunk=%d block=%d" % (chunk, block))
     Bt, T, H, d = 2, 3000, 4, 128
     s = 1.0 / np.sqrt(d)
     q, k, v = (randn((Bt, T, H, d), 40 + i, s, dtype=torch.bfloat16) for i in range(3))
     x = randn((Bt, T, H * d), 43, dtype=torch.bfloat16)
     S0 = randn((Bt, H, d, d), 44, 0.05)
     out, S, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), None, S0.to(DEV),
-                               chunk_tokens=chunk)
+                               chunk_tokens=chunk, block_size=block)
     ref, Sref, _ = oracle_forward(q, k, v, x, S0)
     assert rel_err(np64(out), ref) <= TOL_BF16
     assert rel_err(np64(S), Sref) <= TOL_BF16
 
 
-def test_bf16_normalized():
-    banner("bf16 normalised")
+@pytest.mark.parametrize("block", [32, 64])
+def test_bf16_normalized(block):
+    banner("bf16 normalised block=%d" % block)
     Bt, T, H, d = 1, 1500, 2, 128
     q, k = (randn((Bt, T, H, d), 50 + i, 0.5, 1.0, dtype=torch.bfloat16) for i in range(2))
     v = randn((Bt, T, H, d), 52, dtype=torch.bfloat16)
     z0 = torch.ones((Bt, H, d))
     for chunk in (0, 512):
         out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), None, None, None, z0.to(DEV),
-                                   normalized=True, chunk_tokens=chunk)
+                                   normalized=True, chunk_tokens=chunk, block_size=block)
         ref, Sref, zref = oracle_forward(q, k, v, None, None, z0, normalized=True)
         assert rel_err(np64(out), ref.reshape(out.shape)) <= TOL_BF16
         assert rel_err(np64(z), zref) <= 1e-4
