@@ -79,9 +79,8 @@ def bench_prefill(args, torch, lib, _lib, inputs):
     nbytes = lib.la_prefill_workspace_bytes(1, T, H, d, _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32,
                                             ctypes.byref(opt))
     ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
-    chunk = lib.la_prefill_chunk_tokens(1, T, T, H, d, _lib.LA_DTYPE_BF16, ctypes.byref(opt))
-    chunked = T > chunk
-    names = (["chunk_state", "chunk_scan"] if chunked else []) + ["main", "gate"]
+    plan = _lib.plan(False, 1, T, T, H, d, _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32, opt)
+    chunk, names = plan.chunk_tokens, plan.kernel_names()
     nk = len(names)
     K, W = args.steps, args.warmup
     ev = HipEvents(2 * nk * (K + W))
@@ -117,7 +116,9 @@ def bench_prefill(args, torch, lib, _lib, inputs):
         (ms_step, ", ".join("%s %.3f" % kv for kv in per_kernel.items())))
     th = T * H
     res = {
-        "T": T, "H": H, "d": d, "chunk": chunk, "ms_per_step": ms_step,
+        "T": T, "H": H, "d": d, "chunk": chunk, "block": plan.block_size,
+        "fused_gate": bool(plan.fused_gate), "main_workgroups": plan.main_workgroups,
+        "ms_per_step": ms_step,
         "tokens_per_s": T / (ms_step * 1e-3), "per_kernel_ms": per_kernel, "token_heads": th,
     }
     del q, k, v, x, out, ws
@@ -238,15 +239,22 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, inputs)
 
     th = pre["token_heads"]
-    main_ms = pre["per_kernel_ms"]["main"]
-    # main pass: reads q, k, v (3 x 256 B bf16) and writes fp32 Y (512 B) per token-head
-    main_bytes = th * (3 * 256 + 512)
+    if pre["fused_gate"]:
+        # main pass with the gate fused: reads q, k, v, x (4 x 256 B bf16) and
+        # writes the fp32 output (512 B) per token-head
+        main_name, main_kernel, main_unit = "main_gated", "main pass + gate (k_prefill_fused)", 4 * 256 + 512
+    else:
+        # main pass alone: reads q, k, v (3 x 256 B bf16), writes fp32 Y (512 B)
+        main_name, main_kernel, main_unit = "main", "main pass (k_prefill_main)", 3 * 256 + 512
+    main_ms = pre["per_kernel_ms"][main_name]
+    main_bytes = th * main_unit
     main_gbs = main_bytes / (main_ms * 1e-3) / 1e9
     # whole path, minimal traffic: q, k, v, x in (bf16) and fp32 out = 1536 B per token-head
     path_bytes = th * 1536
     path_gbs = path_bytes / (pre["ms_per_step"] * 1e-3) / 1e9
-    # algorithmic flops per token-head at block 64, d 128: intra 2(B+1)d + inter 2d^2 + state 2d^2
-    B, d = 64, pre["d"]
+    # algorithmic flops per token-head at block B, head dim d: intra 2(B+1)d
+    # (causal half of the block for phi(Q)phi(K)^T and P.V), inter 2d^2, state 2d^2
+    B, d = pre["block"], pre["d"]
     flops = th * (2 * (B + 1) * d + 4 * d * d)
     tflops = flops / (pre["ms_per_step"] * 1e-3) / 1e12
     line = {
@@ -262,14 +270,17 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: bf16 q/k/v N(0,1)/sqrt(128), B=1 T=%d H=%d d=%d, block 64, "
+        "config": {"workload": "%s: bf16 q/k/v N(0,1)/sqrt(128), B=1 T=%d H=%d d=%d, block %d, "
                                "fp32 state carry, RMSNorm*sigmoid gate, fp32 out"
-                               % (args.workload, pre["T"], pre["H"], pre["d"]),
+                               % (args.workload, pre["T"], pre["H"], pre["d"], pre["block"]),
                    "global_batch": 1, "seq_len": pre["T"], "heads": pre["H"], "head_dim": pre["d"],
-                   "block": 64, "chunk_tokens": pre["chunk"]},
-        "roofline": {"bound": "hbm", "kernel": "main pass (k_prefill_main)",
+                   "block": pre["block"], "chunk_tokens": pre["chunk"],
+                   "fused_gate": pre["fused_gate"]},
+        "roofline": {"bound": "hbm", "kernel": main_kernel,
                      "achieved": main_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": main_gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": main_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": main_bytes,
+                     "avg_launch_ms": main_ms},
         "cpu_baseline": cpu,
         "prefill": {"per_kernel_ms": pre["per_kernel_ms"], "path_min_bytes_GBps": path_gbs,
                     "path_hbm_roofline_frac": path_gbs / HBM_PEAK_GBS,

@@ -42,6 +42,8 @@
  *     `z_out` may equal `z_in` (exact aliasing only).
  *   - No C++ exception crosses this interface; no global mutable state, so
  *     calls on distinct streams with distinct buffers may run concurrently.
+ *     (A prefill whose plan fuses the gate is a cooperative launch: the HIP
+ *     runtime may serialise it against other cooperative launches.)
  */
 #ifndef LA_H
 #define LA_H
@@ -68,29 +70,29 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               use the masked quadratic form, inter-block terms the carried
  *               state ([Arch] 2.1, [Deploy] 3).  Mathematically every block
  *               size gives the same result; it changes fp32 rounding order
- *               only.  0 = library default (64).  The bf16 d=128 matrix-core
- *               path implements 64; the fp32 path implements 32, 64, 128
- *               and 256.  Other values: LA_ERR_UNSUPPORTED.  Partial tail
- *               blocks are zero-padded to the next of 32 or 64 rows
- *               (SiLU(0) = 0, so the pad adds nothing).
+ *               only.  0 = library default: 32 for bf16 inputs with d = 128
+ *               (matrix-core path), 64 otherwise.  The bf16 d=128
+ *               matrix-core path implements 32 and 64; the fp32 path
+ *               implements 32, 64, 128 and 256.  Other values:
+ *               LA_ERR_UNSUPPORTED.  Partial tail blocks are zero-padded to
+ *               the next of 32 or 64 rows (SiLU(0) = 0, so the pad adds
+ *               nothing).
  *   normalized  0: y = phi(q)^T S.  1: y = phi(q)^T S / phi(q)^T z.
  *   gated       0: out = y.  1: out = RMSNorm(y) * w * sigmoid(x).
  *   norm_group  RMSNorm width in features: 0 = H*d (whole token), or any
  *               divisor of H*d that is a multiple of 64 (e.g. d = per head).
  *   rms_eps     epsilon inside the square root (default 1e-6).
  *   chunk_tokens tokens per independently scheduled chunk of one sequence
- *               (multiple of 64); 0 = chosen by the library.  Changes fp32
- *               rounding order only.
+ *               (multiple of 64); 0 = chosen by the library (la_prefill_plan
+ *               reports it).  Changes fp32 rounding order only.
  *   timing_events, n_timing
  *               instrumentation: NULL/0, or an array of 2*n_timing hipEvent_t
  *               handles (created by the caller).  The library records
  *               events[2i] just before and events[2i+1] just after the i-th
- *               kernel it launches on hip_stream, for i < n_timing.  Launch
- *               order of la_prefill / la_prefill_varlen: [chunk planner]
- *               (varlen only), [state copy] (zero-length input, or varlen
- *               whose sequences each fit one chunk), [chunk-state, chunk
- *               scan] (when a sequence spans several chunks), main pass,
- *               [gate] (gated).  la_decode_step: decode, [gate].             */
+ *               kernel it launches on hip_stream, for i < n_timing.  The
+ *               kernels of a prefill call, in launch order, are listed by
+ *               la_prefill_plan; la_decode_step launches decode, then [gate]
+ *               when gated.                                                  */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -179,11 +181,46 @@ size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int3
 size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out_dtype,
                                  const la_options_t* opt);
 
-/* Chunk length (tokens) the library would use for these arguments; for
- * reporting and tests.  -1 on invalid arguments. */
-int32_t la_prefill_chunk_tokens(int32_t num_seqs, int32_t total_T, int32_t max_seqlen,
-                                int32_t H, int32_t d, la_dtype_t in_dtype,
-                                const la_options_t* opt);
+/* Kernels of a prefill call (la_plan_t.kernels, in launch order). */
+typedef enum {
+    LA_KERNEL_CHUNK_TABLE = 1,     /* varlen: chunk offsets from cu_seqlens */
+    LA_KERNEL_STATE_COPY = 2,      /* state_in -> state_out for sequences the
+                                      main pass does not finish (T = 0, or a
+                                      varlen batch held in one chunk each) */
+    LA_KERNEL_CHUNK_STATE = 3,     /* per-chunk increments of S (and z) */
+    LA_KERNEL_CHUNK_SCAN = 4,      /* exclusive prefix of the increments over
+                                      each sequence's chunks; final states */
+    LA_KERNEL_EXCHANGE_CLEAR = 5,  /* fused gate: clears its exchange buffer */
+    LA_KERNEL_MAIN = 6,            /* main pass: y of every token */
+    LA_KERNEL_MAIN_GATED = 7,      /* main pass with the gate fused in */
+    LA_KERNEL_GATE = 8             /* RMSNorm * w * sigmoid(x) gate */
+} la_kernel_t;
+
+/* What a prefill call with given sizes and options will do. */
+typedef struct {
+    int64_t main_workgroups;  /* (chunk, head) workgroups of the main pass
+                                 (an upper bound for varlen batches) */
+    int32_t chunk_tokens;     /* tokens per chunk */
+    int32_t block_size;       /* resolved block size */
+    int32_t fused_gate;       /* 1: the gate runs inside the main pass */
+    int32_t n_kernels;        /* kernels launched, <= 8 */
+    int32_t kernels[8];       /* la_kernel_t values, launch order */
+} la_plan_t;
+
+/* Fills *plan for a la_prefill (varlen = 0: num_seqs = Bt, total_T = Bt*T,
+ * max_seqlen = T) or la_prefill_varlen (varlen = 1) call with these sizes,
+ * dtypes and options; has_state_out says whether state_out or z_out will be
+ * given.  The plan depends on the current HIP device: the fused gate is
+ * chosen when the main pass's (chunk, head) workgroups can all be resident
+ * on it at once (bf16 d=128, block 32, H <= 8, norm_group = H*d), and it
+ * then fixes the chunk length.  Query the workspace size, and call, with the
+ * same device current.  Returns LA_ERR_INVALID_ARGUMENT or
+ * LA_ERR_UNSUPPORTED where the call would, else LA_OK.  Host only. */
+la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T,
+                            int32_t max_seqlen, int32_t H, int32_t d,
+                            la_dtype_t in_dtype, la_dtype_t out_dtype,
+                            int32_t has_state_out, const la_options_t* opt,
+                            la_plan_t* plan);
 
 /* Static, NUL-terminated description of a status code. */
 const char* la_status_string(la_status_t status);

@@ -25,7 +25,7 @@ EXPORTS = (
     "la_prefill_workspace_bytes",
     "la_prefill_varlen_workspace_bytes",
     "la_decode_workspace_bytes",
-    "la_prefill_chunk_tokens",
+    "la_prefill_plan",
     "la_status_string",
 )
 
@@ -41,6 +41,33 @@ class Options(ctypes.Structure):
         ("timing_events", ctypes.c_void_p),
         ("n_timing", ctypes.c_int32),
     ]
+
+
+# la_kernel_t: kernels of a prefill call, as listed by la_prefill_plan
+KERNEL_NAMES = {
+    1: "chunk_table",
+    2: "state_copy",
+    3: "chunk_state",
+    4: "chunk_scan",
+    5: "exchange_clear",
+    6: "main",
+    7: "main_gated",
+    8: "gate",
+}
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("main_workgroups", ctypes.c_int64),
+        ("chunk_tokens", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("fused_gate", ctypes.c_int32),
+        ("n_kernels", ctypes.c_int32),
+        ("kernels", ctypes.c_int32 * 8),
+    ]
+
+    def kernel_names(self):
+        return [KERNEL_NAMES[self.kernels[i]] for i in range(self.n_kernels)]
 
 
 class LAError(RuntimeError):
@@ -92,8 +119,9 @@ def load() -> ctypes.CDLL:
                                                           ctypes.c_int, ctypes.c_int, _optp]
         lib.la_decode_workspace_bytes.restype = _sz
         lib.la_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, ctypes.c_int, _optp]
-        lib.la_prefill_chunk_tokens.restype = _i32
-        lib.la_prefill_chunk_tokens.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.c_int, _optp]
+        lib.la_prefill_plan.restype = ctypes.c_int
+        lib.la_prefill_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                        ctypes.c_int, _i32, _optp, ctypes.POINTER(Plan)]
         _lib = lib
         return lib
 
@@ -115,6 +143,16 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     o.rms_eps = float(rms_eps)
     o.chunk_tokens = int(chunk_tokens)
     return o
+
+
+def plan(varlen, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, opt,
+         has_state_out=True) -> Plan:
+    """What a prefill call with these sizes will launch (la_prefill_plan)."""
+    r = Plan()
+    check(load().la_prefill_plan(int(bool(varlen)), num_seqs, total_T, max_seqlen, H, d,
+                                 in_dtype, out_dtype, int(bool(has_state_out)),
+                                 ctypes.byref(opt), ctypes.byref(r)), "la_prefill_plan")
+    return r
 
 
 def check(status: int, where: str) -> None:

@@ -26,6 +26,19 @@ constexpr int kStateTile = 64;          // tile of the chunk-state kernel (any b
 constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
 constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
+constexpr int kSpinLimit = 1 << 22;     // bounded waits of the fused gate (~seconds)
+
+// Workgroups of `kernel` (256 threads) the current device keeps resident at
+// once, or 0 when cooperative launch is unavailable.
+int64_t resident_capacity(const void* kernel) {
+    int dev = 0, ncu = 0, coop = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop)
+        return 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess) return 0;
+    return (int64_t)per_cu * ncu;
+}
 
 struct Opts {
     int block;
@@ -55,6 +68,9 @@ struct Timer {
 };
 
 struct Plan {
+    bool fuse_ok;      // gated bf16 d=128 block 32 with H <= 8: gate fused into the main pass
+    int64_t xbuf_words;  // exchange buffer of the fused gate (64-bit words)
+    size_t off_xbuf;
     int block;         // resolved block size
     bool mfma;         // bf16, d = 128, block 32 or 64: matrix-core kernels
     bool chunked;      // some sequence spans more than one chunk
@@ -116,6 +132,10 @@ int auto_chunk(int64_t total_T, int H, int max_seqlen, const Opts& o) {
     return (int)C;
 }
 
+int64_t items_for(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqlen, int64_t C) {
+    return varlen ? total_T / C + num_seqs : num_seqs * ((max_seqlen + C - 1) / C);
+}
+
 Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqlen, int H, int d,
                la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o) {
     Plan p{};
@@ -123,23 +143,57 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
     p.block = o.block;
     if (p.block == 0) p.block = (in_dtype == LA_DTYPE_BF16 && d == 128) ? kMfmaDefaultBlock : kValuDefaultBlock;
     p.mfma = in_dtype == LA_DTYPE_BF16 && d == 128 && (p.block == 32 || p.block == 64);
-    p.C = auto_chunk(total_T, H, (int)max_seqlen, o);
+    p.stride = (int64_t)d * d + (o.normalized ? d : 0);
+    // Fused gate: every (chunk, head) workgroup must be resident at once, so the
+    // chunk length is chosen for (chunks x H) <= the device's capacity.
+    p.fuse_ok = false;
+    // (the fused gate normalises over all H*d features of a token)
+    const bool fusable = o.gated && o.group == H * d && p.mfma && p.block == 32 &&
+                         H <= mf::FUSE_HMAX && total_T > 0;
+    const void* fk = o.normalized ? (const void*)mf::k_prefill_fused<true, float, 32>
+                                  : (const void*)mf::k_prefill_fused<false, float, 32>;
+    const int64_t cap = fusable ? resident_capacity(fk) : 0;
+    if (cap >= H) {
+        const int64_t teams = cap / H;
+        int64_t C;
+        if (o.chunk) {
+            C = o.chunk;
+        } else if (varlen) {
+            C = teams > num_seqs ? (total_T + (teams - num_seqs) - 1) / (teams - num_seqs) : 0;
+        } else {
+            const int64_t per_seq = teams / num_seqs;
+            C = per_seq > 0 ? (max_seqlen + per_seq - 1) / per_seq : 0;
+        }
+        C = (C + 63) / 64 * 64;
+        if (C > 0 && C < (int64_t)1 << 30) {
+            if (!o.chunk && C < kMinAutoChunk) C = kMinAutoChunk;
+            if (max_seqlen <= C) C = max_seqlen <= 64 ? 64 : (max_seqlen + 63) / 64 * 64;
+            const int64_t items = items_for(varlen, num_seqs, total_T, max_seqlen, C);
+            if (items <= teams) {
+                p.fuse_ok = true;
+                p.C = (int)C;
+            }
+        }
+    }
+    if (!p.fuse_ok) p.C = auto_chunk(total_T, H, (int)max_seqlen, o);
     p.chunked = max_seqlen > p.C;
     if (!p.chunked) {
         // one chunk per sequence: the chunk length only has to cover it
         int64_t c = (max_seqlen + 63) / 64 * 64;
         p.C = (int)(c < 64 ? 64 : c);
     }
-    if (varlen) p.items = total_T / p.C + num_seqs;
-    else p.items = num_seqs * ((max_seqlen + p.C - 1) / p.C);
-    p.stride = (int64_t)d * d + (o.normalized ? d : 0);
+    p.items = items_for(varlen, num_seqs, total_T, max_seqlen, p.C);
+    p.xbuf_words = p.fuse_ok ? p.items * mf::NSLOT * H * 32 : 0;
     size_t off = 0;
     p.off_chunk_off = off;
     if (varlen) off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
     p.off_buf = off;
     if (p.chunked) off += align256((size_t)p.items * H * p.stride * sizeof(float));
     p.off_y = off;
-    if (o.gated && out_dtype != LA_DTYPE_F32) off += align256((size_t)total_T * H * d * sizeof(float));
+    if (o.gated && out_dtype != LA_DTYPE_F32 && !p.fuse_ok)
+        off += align256((size_t)total_T * H * d * sizeof(float));
+    p.off_xbuf = off;
+    off += align256((size_t)p.xbuf_words * sizeof(uint64_t));
     p.total = off;
     return p;
 }
@@ -193,7 +247,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         }
         if (total_T == 0) return LA_OK;
     }
-    const bool need_yws = o.gated && !std::is_same<OutT, float>::value;
+    const bool need_yws = o.gated && !p.fuse_ok && !std::is_same<OutT, float>::value;
     float* ybuf_f = need_yws ? (float*)(ws + p.off_y) : nullptr;
     float* buf = p.chunked ? (float*)(ws + p.off_buf) : nullptr;
     const dim3 grid((unsigned)p.items, (unsigned)H);
@@ -224,6 +278,45 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     }
 
     // main pass: Y in the output dtype, or fp32 (out itself when fp32) when gated
+    // fused gate: one cooperative launch, every (chunk, head) workgroup resident
+    if (p.fuse_ok) {
+        const bool f32o = std::is_same<OutT, float>::value;
+        const void* kern = norm ? (f32o ? (const void*)mf::k_prefill_fused<true, float, 32>
+                                        : (const void*)mf::k_prefill_fused<true, uint16_t, 32>)
+                                : (f32o ? (const void*)mf::k_prefill_fused<false, float, 32>
+                                        : (const void*)mf::k_prefill_fused<false, uint16_t, 32>);
+        uint64_t* xbuf = (uint64_t*)(ws + p.off_xbuf);
+        const int64_t nw = p.xbuf_words;
+        tm.before();
+        k_zero_u64<<<(unsigned)((nw + 255) / 256), 256, 0, st>>>(xbuf, nw);
+        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+        tm.after();
+        const uint16_t* qb = (const uint16_t*)q;
+        const uint16_t* kb = (const uint16_t*)k;
+        const uint16_t* vb = (const uint16_t*)v;
+        const uint16_t* xb = (const uint16_t*)x;
+        int k16 = 16, spin = kSpinLimit, Hh = H;
+        float eps = o.eps;
+        float* so = p.chunked ? nullptr : state_out;
+        float* zo = (p.chunked || !norm) ? nullptr : z_out;
+        const float* bufc = buf;
+        int64_t stride = p.stride;
+        OutT* outp = (OutT*)out;
+        void* args[] = {(void*)&qb, (void*)&kb, (void*)&vb, (void*)&map, (void*)&Hh,
+                        (void*)&bufc, (void*)&stride, (void*)&state_in, (void*)&z_in,
+                        (void*)&outp, (void*)&so, (void*)&zo, (void*)&k16, (void*)&xb,
+                        (void*)&w, (void*)&eps, (void*)&xbuf, (void*)&spin};
+        tm.before();
+        const hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)(p.items * H)),
+                                                        dim3(mf::NT), args, 0, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return LA_ERR_HIP;
+        }
+        tm.after();
+        return LA_OK;
+    }
+
     void* ydst = o.gated ? (need_yws ? (void*)ybuf_f : out) : out;
     const bool y_is_f32 = o.gated || std::is_same<OutT, float>::value;
     tm.before();
@@ -383,13 +476,44 @@ size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out
     return 0;
 }
 
-int32_t la_prefill_chunk_tokens(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
-                                int32_t d, la_dtype_t in_dtype, const la_options_t* opt) {
+la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, int32_t max_seqlen,
+                            int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                            int32_t has_state_out, const la_options_t* opt, la_plan_t* plan) {
+    if (!plan) return LA_ERR_INVALID_ARGUMENT;
+    if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T)
+        return LA_ERR_INVALID_ARGUMENT;
+    if (!varlen && (int64_t)num_seqs * max_seqlen != total_T) return LA_ERR_INVALID_ARGUMENT;
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
     Opts o;
-    if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T) return -1;
-    if (check_shape(H, d, in_dtype, LA_DTYPE_F32) != LA_OK) return -1;
-    if (parse_options(opt, H, d, o) != LA_OK) return -1;
-    return make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, LA_DTYPE_F32, o).C;
+    s = parse_options(opt, H, d, o);
+    if (s != LA_OK) return s;
+    const Plan p = make_plan(varlen != 0, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o);
+    la_plan_t r;
+    std::memset(&r, 0, sizeof(r));
+    r.main_workgroups = total_T > 0 ? p.items * H : 0;
+    r.chunk_tokens = p.C;
+    r.block_size = p.block;
+    r.fused_gate = total_T > 0 && p.fuse_ok;
+    int n = 0;
+    if (varlen) r.kernels[n++] = LA_KERNEL_CHUNK_TABLE;
+    if ((total_T == 0 || (varlen && !p.chunked)) && has_state_out) r.kernels[n++] = LA_KERNEL_STATE_COPY;
+    if (total_T > 0) {
+        if (p.chunked) {
+            r.kernels[n++] = LA_KERNEL_CHUNK_STATE;
+            r.kernels[n++] = LA_KERNEL_CHUNK_SCAN;
+        }
+        if (p.fuse_ok) {
+            r.kernels[n++] = LA_KERNEL_EXCHANGE_CLEAR;
+            r.kernels[n++] = LA_KERNEL_MAIN_GATED;
+        } else {
+            r.kernels[n++] = LA_KERNEL_MAIN;
+            if (o.gated) r.kernels[n++] = LA_KERNEL_GATE;
+        }
+    }
+    r.n_kernels = n;
+    *plan = r;
+    return LA_OK;
 }
 
 la_status_t la_prefill(const void* q, const void* k, const void* v, const void* x_gate,

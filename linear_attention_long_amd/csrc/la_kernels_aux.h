@@ -70,6 +70,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
     }
 }
 
+// n 64-bit words <- 0 (clears the fused gate's exchange buffer; a plain
+// kernel rather than a memset node so the call stays graph-capturable).
+__global__ __launch_bounds__(256) void k_zero_u64(uint64_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0ull;
+}
+
 // state_out <- state_in (or zeros), z_out likewise: the zero-length case.
 __global__ __launch_bounds__(256) void k_fill_state(const float* state_in, const float* z_in,
                                                     float* state_out, float* z_out, int64_t nS,

@@ -76,6 +76,11 @@ struct __attribute__((aligned(16))) SmemMain {
     float zq[TB];                    // normalised mode: phi(q) . z_prev per row
     float zpart[4 * D];              // normalised mode: column sums of phi(k) per wave
     float z[D];                      // normalised mode: running normaliser
+    // fused gate (32-token blocks only; a stub of one element otherwise)
+    static constexpr int FB = TB == 32 ? TB : 1;
+    float ssw[4 * FB];    // per-wave sums of y^2 per token
+    float ssall[8 * FB];  // this block's sums of y^2 of up to 8 heads
+    __attribute__((aligned(16))) float ystash[FB * (D + 4)];  // Y of the waiting block
 };
 
 // (only transposing reads, which are never fused: no padding)
@@ -275,23 +280,127 @@ template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4_
     *(uint2*)p = u;
 }
 
+// Arguments of the fused gate (RMSNorm over all H heads of a token, times
+// w * sigmoid(x)), applied by the main pass when its workgroups run as
+// cooperative teams of H (one per head) that exchange per-token sums of y^2.
+template <typename InT>
+struct GateArgs {
+    const InT* x;            // [tokens, H*D]
+    const float* w;          // [H*D] or nullptr
+    float eps;
+    uint64_t* xbuf;          // [teams][NSLOT][H][TB] (tag << 32 | sum of squares), zeroed per call
+    int team;
+    int spin_limit;
+};
+constexpr int NSLOT = 4;     // exchange slots per team: members are at most 2 blocks apart
+constexpr int FUSE_HMAX = 8; // heads per token the fused gate handles (more: separate gate)
+
+// ---- fused gate helpers ----
+
+// After a barrier: this head's per-token sums of y^2 of the stashed block
+// (summed over the 4 waves' column groups) go to the exchange buffer tagged
+// with the block's sequence number.
+template <int TB>
+__device__ __forceinline__ void publish_ssq(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga, int H,
+                                            int h, uint32_t& tag) {
+    ++tag;
+    const int tid = threadIdx.x;
+    if (tid < TB) {
+        const float ss = (sm.ssw[tid] + sm.ssw[TB + tid]) + (sm.ssw[2 * TB + tid] + sm.ssw[3 * TB + tid]);
+        uint64_t* slot = ga.xbuf + (((size_t)ga.team * NSLOT + (tag % NSLOT)) * H + h) * TB;
+        const uint64_t word = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(ss);
+        __hip_atomic_store(slot + tid, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Keep the block's Y (acc) in LDS for the gate one block later, load its
+// gate input, and put its per-wave sums of y^2 in LDS.
+template <int TB>
+__device__ __forceinline__ void stash_block(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
+                                            const f32x4_t (&acc)[2][Tile<TB>::NQT],
+                                            uint2 (&xprev)[2][Tile<TB>::NQT], int64_t tt0,
+                                            int nvalid, int H, int h, int wave, int g, int c) {
+#pragma unroll
+    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
+        const int row = 16 * qt + c;
+        float ss = 0.f;
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt) {
+            const int col = 32 * wave + 16 * dvt + 4 * g;
+            *(f32x4_t*)&sm.ystash[row * (D + 4) + col] = acc[dvt][qt];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += acc[dvt][qt][i] * acc[dvt][qt][i];
+            xprev[dvt][qt] = make_uint2(0u, 0u);
+            if (row < nvalid)
+                xprev[dvt][qt] = *(const uint2*)(ga.x + ((size_t)(tt0 + row) * H + h) * D + col);
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) sm.ssw[wave * TB + row] = ss;
+    }
+}
+
+// Wait for every head's sums of the stashed block, then write
+// out = y / sqrt(mean over the token's H*D features of y^2 + eps) * w * sigmoid(x).
+template <int TB, typename OutT>
+__device__ __forceinline__ void gate_block(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
+                                           OutT* __restrict__ out,
+                                           const uint2 (&xprev)[2][Tile<TB>::NQT], int64_t tprev,
+                                           int nprev, int H, int h, uint32_t tag, int wave, int g,
+                                           int c) {
+    const int tid = threadIdx.x;
+    const uint64_t* slot = ga.xbuf + ((size_t)ga.team * NSLOT + (tag % NSLOT)) * H * TB;
+    for (int e = tid; e < H * TB; e += NT) {
+        uint64_t word = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int n = 0; (uint32_t)(word >> 32) != tag && n < ga.spin_limit; ++n) {
+            __builtin_amdgcn_s_sleep(2);
+            word = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        sm.ssall[(e % TB) * FUSE_HMAX + e / TB] = __uint_as_float((uint32_t)word);
+    }
+    __syncthreads();
+    const float inv_f = 1.f / (float)(H * D);
+#pragma unroll
+    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
+        const int row = 16 * qt + c;
+        if (row >= nprev) continue;
+        // heads summed in a fixed order: the result does not depend on timing
+        float ss = 0.f;
+        for (int hh = 0; hh < H; ++hh) ss += sm.ssall[row * FUSE_HMAX + hh];
+        const float r = 1.0f / sqrtf(ss * inv_f + ga.eps);
+        OutT* dst = out + ((size_t)(tprev + row) * H + h) * D + 32 * wave + 4 * g;
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt) {
+            const int col = 32 * wave + 16 * dvt + 4 * g;
+            const int f = h * D + col;
+            const f32x4_t yv = *(const f32x4_t*)&sm.ystash[row * (D + 4) + col];
+            float xs[4] = {bf16_lo_to_f32(xprev[dvt][qt].x), bf16_hi_to_f32(xprev[dvt][qt].x),
+                           bf16_lo_to_f32(xprev[dvt][qt].y), bf16_hi_to_f32(xprev[dvt][qt].y)};
+            f32x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = yv[i] * r * (ga.w ? ga.w[f + i] : 1.f) * sigmoid(xs[i]);
+            store4<OutT>(dst + 16 * dvt, o, 1.f);
+        }
+    }
+}
+
 // Main pass over one (chunk, head).  Starting state: prefix[item][h] if
 // prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
 // chunk is a whole sequence (no prefix), the final state is written to
-// state_out/z_out (if given).  Y goes to y[t][h*D + j].  k16 must be 16.
-template <bool NORM, typename OutT, int TB>
-__global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
-    const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
-    float* state_out, float* z_out, int k16) {
+// state_out/z_out (if given).  Unfused: Y goes to y[t][h*D + j].  Fused: the
+// gated output goes there instead, one block after Y (tag_base + block index
+// numbers the exchange).  k16 must be 16.
+template <bool NORM, bool FUSE, typename OutT, typename InT, int TB>
+__device__ __forceinline__ void process_item(
+    SmemMain<TB>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const Item& it, int item, int H, int h,
+    const float* __restrict__ prefix, int64_t prefix_stride, const float* __restrict__ state_in,
+    const float* __restrict__ z_in, OutT* __restrict__ y, float* state_out, float* z_out, int k16,
+    const GateArgs<InT>& ga, uint32_t& tag) {
     using L = Tile<TB>;
     constexpr int PS = L::PS;
-    __shared__ SmemMain<TB> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
-    const int h = blockIdx.y;
-    Item it;
-    if (!decode_item(map, blockIdx.x, it)) return;
 
     // P^T tiles with key tile > query tile are read by the P.V product but
     // never written: they stay zero.
@@ -305,7 +414,7 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
     const float* s0 = nullptr;
     const float* z0 = nullptr;
     if (prefix) {
-        s0 = prefix + ((size_t)blockIdx.x * H + h) * prefix_stride;
+        s0 = prefix + ((size_t)item * H + h) * prefix_stride;
         z0 = s0 + D * D;
     } else {
         if (state_in) s0 = state_in + ((size_t)it.seq * H + h) * D * D;
@@ -321,6 +430,12 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
                 S[dkt][dvt][i] = s0 ? s0[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] : 0.f;
     if (NORM && tid < D) sm.z[tid] = z0 ? z0[tid] : 0.f;
 
+    // fused gate: the previous block's Y and gate input wait here for the
+    // other heads' sums of squares
+    uint2 xprev[2][L::NQT];
+    int64_t tprev = 0;
+    int nprev = 0;
+
     const int ntiles = (it.len + TB - 1) / TB;
     uint4 rq[L::NJ], rk[L::NJ], rv[L::NJ];
     load_tile<L::NJ>(rq, q, it.t0, min(TB, it.len), H, h, tid);
@@ -334,6 +449,7 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
         const int nqt = 2 * nks;
 
         __syncthreads();  // previous block's LDS reads and z update are done
+        if (FUSE && ti > 0) publish_ssq<TB>(sm, ga, H, h, tag);
         {
             const int col = (tid & 15) * 8;
 #pragma unroll
@@ -474,24 +590,42 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
             }
         }
         // acc[dvt][qt][i]: query 16qt + c, feature 32*wave + 16*dvt + 4g + i
+        if (NORM) {
 #pragma unroll
-        for (int qt = 0; qt < L::NQT; ++qt) {
-            const int row = 16 * qt + c;
-            if (qt < nqt && row < nvalid) {
-                float sc = 1.f;
-                if (NORM) {
-                    float den = sm.zq[row];
-                    for (int kt = 0; kt <= qt; ++kt) den += sm.denp[kt * TB + row];
-                    sc = 1.f / den;
-                }
-                OutT* dst = y + ((size_t)(tt0 + row) * H + h) * D + 32 * wave + 4 * g;
+            for (int qt = 0; qt < L::NQT; ++qt) {
+                const int row = 16 * qt + c;
+                float den = sm.zq[row];
+                for (int kt = 0; kt <= qt; ++kt) den += sm.denp[kt * TB + row];
+                const float sc = 1.f / den;
 #pragma unroll
-                for (int dvt = 0; dvt < 2; ++dvt) store4<OutT>(dst + 16 * dvt, acc[dvt][qt], sc);
+                for (int dvt = 0; dvt < 2; ++dvt) acc[dvt][qt] *= sc;
             }
+        }
+        if (!FUSE) {
+#pragma unroll
+            for (int qt = 0; qt < L::NQT; ++qt) {
+                const int row = 16 * qt + c;
+                if (qt < nqt && row < nvalid) {
+                    OutT* dst = y + ((size_t)(tt0 + row) * H + h) * D + 32 * wave + 4 * g;
+#pragma unroll
+                    for (int dvt = 0; dvt < 2; ++dvt) store4<OutT>(dst + 16 * dvt, acc[dvt][qt], 1.f);
+                }
+            }
+        } else {
+            if (ti > 0) gate_block<TB>(sm, ga, y, xprev, tprev, nprev, H, h, tag, wave, g, c);
+            __syncthreads();  // the stash is read by other waves' gate above
+            stash_block<TB>(sm, ga, acc, xprev, tt0, nvalid, H, h, wave, g, c);
+            tprev = tt0;
+            nprev = nvalid;
         }
 
         // ---- S += phi(K)^T phi(V) ----
         state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+    }
+    if (FUSE) {
+        __syncthreads();
+        publish_ssq<TB>(sm, ga, H, h, tag);
+        gate_block<TB>(sm, ga, y, xprev, tprev, nprev, H, h, tag, wave, g, c);
     }
 
     if (!prefix) {
@@ -510,6 +644,46 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
             if (tid < D) z_out[((size_t)it.seq * H + h) * D + tid] = sm.z[tid];
         }
     }
+    __syncthreads();  // the next item reuses the LDS
+}
+
+// Unfused main pass: one workgroup per (chunk = blockIdx.x, head = blockIdx.y).
+template <bool NORM, typename OutT, int TB>
+__global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
+    const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
+    float* state_out, float* z_out, int k16) {
+    __shared__ SmemMain<TB> sm;
+    Item it;
+    if (!decode_item(map, blockIdx.x, it)) return;
+    GateArgs<uint16_t> ga{};
+    uint32_t tag = 0;
+    process_item<NORM, false, OutT, uint16_t, TB>(sm, q, k, v, it, blockIdx.x, H, blockIdx.y,
+                                                   prefix, prefix_stride, state_in, z_in, y,
+                                                   state_out, z_out, k16, ga, tag);
+}
+
+// Fused main pass + gate, one workgroup per (chunk = blockIdx.x / H, head =
+// blockIdx.x % H).  Launched cooperatively: every workgroup is resident, so
+// the H heads of a chunk -- a team -- run together and their per-token sums
+// of y^2 meet in the exchange buffer.  Every wait is bounded.
+template <bool NORM, typename OutT, int TB>
+__global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_fused(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
+    const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ out,
+    float* state_out, float* z_out, int k16, const uint16_t* __restrict__ x,
+    const float* __restrict__ w, float eps, uint64_t* xbuf, int spin_limit) {
+    __shared__ SmemMain<TB> sm;
+    const int item = blockIdx.x / H, h = blockIdx.x - item * H;
+    Item it;
+    if (!decode_item(map, item, it)) return;  // the whole team returns together
+    GateArgs<uint16_t> ga{x, w, eps, xbuf, item, spin_limit};
+    uint32_t tag = 0;
+    process_item<NORM, true, OutT, uint16_t, TB>(sm, q, k, v, it, item, H, h, prefix,
+                                                  prefix_stride, state_in, z_in, out, state_out,
+                                                  z_out, k16, ga, tag);
 }
 
 }  // namespace mf

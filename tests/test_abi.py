@@ -72,20 +72,59 @@ def test_workspace_queries(lib):
     assert lib.la_prefill_workspace_bytes(1, 512, 2, 64, F32, F32, ctypes.byref(o)) == 0
     # two 512-token chunks x 2 heads x d^2 floats
     assert lib.la_prefill_workspace_bytes(1, 1024, 2, 64, F32, F32, ctypes.byref(o)) == 2 * 2 * 64 * 64 * 4
-    # 1M tokens x 8 heads: chunked, chunk 4096 -> 256 chunks x 8 heads x d^2 floats
-    assert lib.la_prefill_chunk_tokens(1, 1 << 20, 1 << 20, 8, 128, BF16, ctypes.byref(o)) == 4096
+    # 1M tokens x 8 heads, ungated: chunk 4096 -> 256 chunks x 8 heads x d^2 floats
+    p = _lib.plan(0, 1, 1 << 20, 1 << 20, 8, 128, BF16, F32, o)
+    assert (p.chunk_tokens, p.block_size, p.fused_gate) == (4096, 32, 0)
     nb = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, F32, ctypes.byref(o))
     assert nb == 256 * 8 * 128 * 128 * 4
-    # gated with a bf16 output adds an fp32 Y buffer
     g = opt(gated=1)
     nb2 = lib.la_prefill_workspace_bytes(1, 1 << 20, 8, 128, BF16, BF16, ctypes.byref(g))
-    assert nb2 == nb + (1 << 20) * 8 * 128 * 4
+    pg = _lib.plan(0, 1, 1 << 20, 1 << 20, 8, 128, BF16, BF16, g)
+    if pg.fused_gate:
+        # fused gate (a device that holds every workgroup): chunk states plus
+        # the exchange buffer (4 slots x H x 32 tokens of 8 bytes per chunk)
+        n = (1 << 20) // pg.chunk_tokens
+        assert nb2 == n * 8 * 128 * 128 * 4 + n * 4 * 8 * 32 * 8
+    else:
+        # separate gate with a bf16 output: an fp32 Y buffer
+        assert nb2 == nb + (1 << 20) * 8 * 128 * 4
     assert lib.la_decode_workspace_bytes(64, 64, 128, F32, ctypes.byref(g)) == 0
     assert lib.la_decode_workspace_bytes(64, 64, 128, BF16, ctypes.byref(g)) == 64 * 64 * 128 * 4
     # rejected arguments report SIZE_MAX
     assert lib.la_prefill_workspace_bytes(1, 16, 2, 96, F32, F32, ctypes.byref(o)) == SIZE_MAX
     assert lib.la_prefill_workspace_bytes(0, 16, 2, 64, F32, F32, ctypes.byref(o)) == SIZE_MAX
     assert lib.la_prefill_varlen_workspace_bytes(10, 2, 11, 2, 64, F32, F32, ctypes.byref(o)) == SIZE_MAX
+
+
+def test_prefill_plan(lib):
+    o = opt()
+    names = lambda *a, **kw: _lib.plan(*a, **kw).kernel_names()
+    assert names(0, 1, 512, 512, 2, 64, F32, F32, o) == ["main"]
+    assert names(0, 1, 1024, 1024, 2, 64, F32, F32, o) == ["chunk_state", "chunk_scan", "main"]
+    assert names(0, 1, 0, 0, 2, 64, F32, F32, o) == ["state_copy"]
+    assert names(0, 1, 0, 0, 2, 64, F32, F32, o, has_state_out=False) == []
+    assert names(1, 3, 900, 400, 2, 64, F32, F32, o) == ["chunk_table", "state_copy", "main"]
+    assert names(1, 3, 1500, 1000, 2, 64, F32, F32, o) == [
+        "chunk_table", "chunk_state", "chunk_scan", "main"]
+    # fp32 inputs never fuse the gate
+    assert names(0, 1, 512, 512, 2, 64, F32, F32, opt(gated=1)) == ["main", "gate"]
+    # per-head norm groups or more than 8 heads keep the gate separate
+    for g in (opt(gated=1, norm_group=128), opt(gated=1)):
+        H = 4 if g.norm_group else 9
+        p = _lib.plan(0, 1, 4096, 4096, H, 128, BF16, F32, g)
+        assert p.fused_gate == 0 and p.kernel_names()[-2:] == ["main", "gate"]
+    p = _lib.plan(0, 2, 2000, 1000, 2, 128, BF16, F32, opt(block_size=64))
+    assert p.block_size == 64 and p.main_workgroups == 2 * 2 * 2  # 2 chunks x 2 seqs x H
+    p = _lib.plan(0, 2, 2000, 1000, 2, 64, F32, F32, o)
+    assert p.block_size == 64
+    r = _lib.Plan()
+    assert lib.la_prefill_plan(0, 2, 2001, 1000, 2, 64, F32, F32, 1, ctypes.byref(o),
+                               ctypes.byref(r)) == INVALID  # total != Bt * T
+    assert lib.la_prefill_plan(1, 2, 100, 101, 2, 64, F32, F32, 1, ctypes.byref(o),
+                               ctypes.byref(r)) == INVALID  # max_seqlen > total
+    assert lib.la_prefill_plan(0, 1, 64, 64, 2, 96, F32, F32, 1, ctypes.byref(o),
+                               ctypes.byref(r)) == UNSUPPORTED
+    assert lib.la_prefill_plan(0, 1, 64, 64, 2, 64, F32, F32, 1, ctypes.byref(o), None) == INVALID
 
 
 def prefill(lib, q=A[0], k=A[1], v=A[2], x=None, w=None, si=None, zi=None, out=A[3], so=None,

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from linear_attention_long_amd import api, inputs
+from linear_attention_long_amd import _lib, api, inputs
 from oracle import oracle as O
 from tests._util import banner, np64, randn, rel_err
 
@@ -163,6 +163,103 @@ def test_prefill_32k_workload():
     e_out, e_S = rel_err(np64(out), ref), rel_err(np64(S), Sref)
     print("prefill_32k rel err out %.3e state %.3e" % (e_out, e_S))
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
+
+
+# ---------------------------------------------------------- fused gate path --
+# bf16 d=128 gated calls whose (chunk, head) workgroups fit on the device at
+# once run the gate inside the main pass (heads of a chunk exchange their
+# per-token sums of y^2).  Each case checks that the plan fuses, then parity.
+
+def fused_plan(varlen, num_seqs, total, max_len, H, out_dtype=_lib.LA_DTYPE_F32, **kw):
+    return _lib.plan(varlen, num_seqs, total, max_len, H, 128, _lib.LA_DTYPE_BF16, out_dtype,
+                     _lib.options(gated=True, **kw))
+
+
+@pytest.mark.parametrize("Bt,T,H,chunk,normalized", [
+    (1, 1, 1, 0, False),       # one token, one head
+    (1, 31, 8, 0, False),      # ragged single block, the most heads fused
+    (2, 33, 3, 0, False),      # odd head count, 32-row block + 1-row tail
+    (1, 1000, 8, 0, True),     # normalised mode
+    (1, 5000, 5, 512, False),  # several chunks (prefix scan) per sequence
+    (2, 3001, 8, 1024, True),  # chunks + normalised + batch, ragged tail
+    (1, 4096, 2, 0, False),
+])
+def test_fused_gate(Bt, T, H, chunk, normalized):
+    banner("fused gate Bt=%d T=%d H=%d chunk=%d normalized=%s" % (Bt, T, H, chunk, normalized))
+    d = 128
+    plan = fused_plan(False, Bt, Bt * T, T, H, chunk_tokens=chunk, normalized=normalized)
+    assert plan.fused_gate == 1, plan.kernel_names()
+    if normalized:
+        q, k = (randn((Bt, T, H, d), 140 + i, 0.5, 1.0, dtype=torch.bfloat16) for i in range(2))
+    else:
+        q, k = (randn((Bt, T, H, d), 140 + i, 1.0 / np.sqrt(d), dtype=torch.bfloat16)
+                for i in range(2))
+    v = randn((Bt, T, H, d), 142, dtype=torch.bfloat16)
+    x = randn((Bt, T, H * d), 143, dtype=torch.bfloat16)
+    S0 = randn((Bt, H, d, d), 144, 0.02)
+    z0 = torch.ones((Bt, H, d)) if normalized else None
+    out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), None, S0.to(DEV),
+                               None if z0 is None else z0.to(DEV), normalized=normalized,
+                               chunk_tokens=chunk)
+    torch.cuda.synchronize()
+    ref, Sref, zref = oracle_forward(q, k, v, x, S0, z0, normalized=normalized)
+    assert rel_err(np64(out), ref) <= TOL_BF16
+    assert rel_err(np64(S), Sref) <= TOL_BF16
+    if normalized:
+        assert rel_err(np64(z), zref) <= 1e-4
+
+
+def test_fused_gate_bf16_out_and_weight():
+    banner("fused gate, bf16 output, rms weight")
+    T, H, d = 2085, 8, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 150 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((1, T, H * d), 153, dtype=torch.bfloat16)
+    w = randn((H * d,), 154, 0.2, 1.0)
+    assert fused_plan(False, 1, T, T, H, _lib.LA_DTYPE_BF16).fused_gate == 1
+    outb, _, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), x.to(DEV), w.to(DEV),
+                                out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _, _ = O.forward(q[0], k[0], v[0], x[0], w, gated=True)
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(np64(outb[0]) - ref)
+    assert (err <= 2.0 ** -8 * np.abs(ref) + TOL_BF16 * rms).all()
+
+
+def test_fused_gate_varlen():
+    banner("fused gate, varlen with empty sequences")
+    lengths = [1, 0, 100, 64, 1500, 33, 0, 257, 4000]
+    cu = inputs.cu_from_lengths(lengths)
+    total, H, d = int(cu[-1]), 4, 128
+    s = 1.0 / np.sqrt(d)
+    for chunk in (0, 512):
+        plan = fused_plan(True, len(lengths), total, max(lengths), H, chunk_tokens=chunk)
+        assert plan.fused_gate == 1, plan.kernel_names()
+        q, k, v = (randn((total, H, d), 160 + i, s, dtype=torch.bfloat16) for i in range(3))
+        x = randn((total, H * d), 163, dtype=torch.bfloat16)
+        S0 = randn((len(lengths), H, d, d), 164, 0.05)
+        out, S, _ = api.la_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV),
+                                          max(lengths), x.to(DEV), None, S0.to(DEV),
+                                          chunk_tokens=chunk)
+        torch.cuda.synchronize()
+        ref, Sref, _ = O.forward(q, k, v, x, None, cu_seqlens=cu.numpy(), state_in=S0, gated=True)
+        assert rel_err(np64(out), ref) <= TOL_BF16
+        assert rel_err(np64(S), Sref) <= TOL_BF16
+        assert torch.equal(S[1].cpu(), S0[1]) and torch.equal(S[6].cpu(), S0[6])
+
+
+def test_unfused_gate_when_heads_exceed_fused_limit():
+    banner("gate not fused: H=9 (unfused path), parity")
+    T, H, d = 700, 9, 128
+    plan = fused_plan(False, 1, T, T, H)
+    assert plan.fused_gate == 0 and plan.kernel_names()[-2:] == ["main", "gate"]
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 170 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((1, T, H * d), 173, dtype=torch.bfloat16)
+    out, S, _ = run_prefill(q, k, v, x)
+    ref, Sref, _ = oracle_forward(q, k, v, x)
+    assert rel_err(np64(out), ref) <= TOL_BF16
+    assert rel_err(np64(S), Sref) <= TOL_BF16
 
 
 # ------------------------------------------------------------------- varlen --

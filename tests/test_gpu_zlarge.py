@@ -8,8 +8,6 @@ first chunks, the first and last token of every sequence, and seeded random
 tokens.  Metric: max|err| / rms(ref) over the sampled outputs (1e-2 for bf16
 inputs) and over every final-state element.
 """
-import ctypes
-
 import numpy as np
 import pytest
 import torch
@@ -23,11 +21,13 @@ pytestmark = pytest.mark.gpu
 TOL_BF16 = 1e-2
 
 
-def chunk_tokens(num_seqs, total, max_len, H, d):
-    lib = _lib.load()
-    o = _lib.options()
-    return lib.la_prefill_chunk_tokens(num_seqs, total, max_len, H, d, _lib.LA_DTYPE_BF16,
-                                       ctypes.byref(o))
+def chunk_tokens(varlen, num_seqs, total, max_len, H, d):
+    """Chunk length of the default plan (printed with its kernels)."""
+    p = _lib.plan(varlen, num_seqs, total, max_len, H, d, _lib.LA_DTYPE_BF16,
+                  _lib.LA_DTYPE_F32, _lib.options(gated=True))
+    print("plan: chunk %d, %d main workgroups, kernels %s"
+          % (p.chunk_tokens, p.main_workgroups, p.kernel_names()))
+    return p.chunk_tokens
 
 
 def sample_tokens(starts, ends, chunk, nrand, seed):
@@ -53,7 +53,7 @@ def test_prefill_1m_workload_sampled():
     q, k, v, x = inputs.prefill_inputs(w, device="cuda")
     out, S, _ = api.la_prefill(q, k, v, x)
     torch.cuda.synchronize()
-    C = chunk_tokens(1, w.T, w.T, w.H, w.d)
+    C = chunk_tokens(False, 1, w.T, w.T, w.H, w.d)
     idx = sample_tokens([0], [w.T], C, 512, 7)
     got = np64(out[0, torch.from_numpy(idx).cuda()])
     S_got = np64(S)
@@ -76,7 +76,7 @@ def test_varlen_512k_workload_sampled():
     lengths = (cu[1:] - cu[:-1]).tolist()
     out, S, _ = api.la_prefill_varlen(q, k, v, cu.cuda(), max(lengths), x)
     torch.cuda.synchronize()
-    C = chunk_tokens(len(lengths), w.total_T, max(lengths), w.H, w.d)
+    C = chunk_tokens(True, len(lengths), w.total_T, max(lengths), w.H, w.d)
     idx = sample_tokens(cu[:-1].tolist(), cu[1:].tolist(), C, 512, 11)
     got = np64(out[torch.from_numpy(idx).cuda()])
     S_got = np64(S)
