@@ -181,6 +181,54 @@ def bench_decode(args, torch, lib, _lib, inputs):
     return res
 
 
+def calibrate_copy(args, torch):
+    """A plain copy of a known number of bytes: under a byte counter, its
+    reading per dispatch against the bytes it must move gives the counter's
+    scale."""
+    n = args.calibrate_copy
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    log("copy of %d bytes: %.3f ms, %.0f GB/s read+write" % (n, dt * 1e3, 2 * n / dt / 1e9))
+    print(json.dumps({"copy_bytes": n, "steps": args.steps, "ms": dt * 1e3}), flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_gated_prefill_1m_traffic.md")
+SOURCES = os.path.join(ROOT, "linear_attention_long_amd", "csrc")
+
+
+def source_digest() -> str:
+    """sha256 over the library's HIP sources (names and contents)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(SOURCES)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            h.update(open(os.path.join(SOURCES, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused main pass from the committed counter
+    summary, or None when the sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith(("source_sha256", "hbm_bytes_per_launch")):
+            key, val = line.strip().strip("`").split(":", 1)
+            vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_sha256") != source_digest() or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
 def cpu_baseline(args, inputs):
     """The oracle (plain fp64 C) on the first tokens of the same workload."""
     import torch
@@ -214,13 +262,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=262144)
     ap.add_argument("--block", type=int, default=0, help="block size (0 = library default)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes --steps times "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the path shards by head or sequence with no collective; see the design "
-              "notes).  Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU code (the path "
+              "shards by head or by sequence with no collective).  Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -231,6 +282,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args, torch)
+        return
     lib = _lib.load()
     log("device: %s" % torch.cuda.get_device_name(0))
 
@@ -248,6 +302,9 @@ def main():
         main_name, main_kernel, main_unit = "main", "main pass (k_prefill_main)", 3 * 256 + 512
     main_ms = pre["per_kernel_ms"][main_name]
     main_bytes = th * main_unit
+    if pre["T"] > pre["chunk"]:
+        # plus the fp32 d x d state each (chunk, head) workgroup starts from
+        main_bytes += pre["main_workgroups"] * pre["d"] * pre["d"] * 4
     main_gbs = main_bytes / (main_ms * 1e-3) / 1e9
     # whole path, minimal traffic: q, k, v, x in (bf16) and fp32 out = 1536 B per token-head
     path_bytes = th * 1536
@@ -278,7 +335,8 @@ def main():
                    "fused_gate": pre["fused_gate"]},
         "roofline": {"bound": "hbm", "kernel": main_kernel,
                      "achieved": main_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": main_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": main_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if main_name == "main_gated" else None,
                      "algorithmic_bytes_per_launch": main_bytes,
                      "avg_launch_ms": main_ms},
         "cpu_baseline": cpu,
