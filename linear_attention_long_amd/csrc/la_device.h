@@ -44,7 +44,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) { return cvt_p
 
 // Split two fp32 values into bf16 hi + bf16 lo with hi = RNE(x), lo = RNE(x - hi);
 // hi*hi' + hi*lo' + lo*hi' then carries ~16 significant bits of each product.
+// x - hi comes from one bf16 dot product per value, (hi0, hi1) . (-1, -0) + x0
+// and (hi0, hi1) . (0, -1) + x1: both products are exact in fp32 and x - hi
+// is representable, so the result is exact whatever the rounding.  The
+// multiplier of x0 is (-1, -0), bits 0x8000bf80, on purpose: the compiler
+// encodes (-1, +0) as the inline constant -1.0, which the hardware reads as
+// the fp32 bit pattern 0xbf800000, i.e. (+0, -1) -- a wrong split.  No inline
+// constant has the pattern 0x8000bf80, so it is emitted as a literal.
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const f32x2_t v = {x0, x1};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    const bf16x2_t m0 = {(__bf16)-1.0f, (__bf16)-0.0f};
+    const bf16x2_t m1 = {(__bf16)0.0f, (__bf16)-1.0f};
+    const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, m0, x0, false);
+    const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, m1, x1, false);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = cvt_pk_bf16(l0, l1);
+}
+
+// The same split for values that stay live afterwards (the dot product
+// accumulates in place, which would cost a copy): x - hi by unpacking hi.
+__device__ __forceinline__ void split2_keep(float x0, float x1, uint32_t& hi, uint32_t& lo) {
     hi = cvt_pk_bf16(x0, x1);
     lo = cvt_pk_bf16(x0 - bf16_lo_to_f32(hi), x1 - bf16_hi_to_f32(hi));
 }

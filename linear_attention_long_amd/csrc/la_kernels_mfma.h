@@ -78,9 +78,10 @@ struct __attribute__((aligned(16))) SmemMain {
     float z[D];                      // normalised mode: running normaliser
     // fused gate (32-token blocks only; a stub of one element otherwise)
     static constexpr int FB = TB == 32 ? TB : 1;
-    float ssw[4 * FB];    // per-wave sums of y^2 per token
-    float ssall[8 * FB];  // this block's sums of y^2 of up to 8 heads
-    __attribute__((aligned(16))) float ystash[FB * (D + 4)];  // Y of the waiting block
+    float ssw[4 * FB];  // per-wave sums of y^2 per token
+    float ssum[FB];     // all heads' sums of y^2 per token
+    __attribute__((aligned(16))) float wgate[TB == 32 ? D : 4];  // this head's RMSNorm weights
+    __attribute__((aligned(16))) float ystash[FB * (D + 4)];  // Y of the block awaiting its gate
 };
 
 // (only transposing reads, which are never fused: no padding)
@@ -95,19 +96,28 @@ struct __attribute__((aligned(16))) SmemState {
 
 // Thread tid loads rows (tid>>4) + 16j, j < NJ, columns (tid&15)*8 .. +7 of
 // a 16*NJ x 128 bf16 tile of one head; rows at or past nvalid read as zero.
+// `blk` points at the tile's first row (same for the whole workgroup) and
+// `rs` is the row stride in elements (H*D).
 template <int NJ>
-__device__ __forceinline__ void load_tile(uint4 (&dst)[NJ], const uint16_t* __restrict__ src,
-                                          int64_t t0, int nvalid, int H, int h, int tid) {
-    const int col = (tid & 15) * 8;
+__device__ __forceinline__ void load_tile(uint4 (&dst)[NJ], const uint16_t* __restrict__ blk,
+                                          uint32_t rs, int nvalid, int tid) {
+    const uint32_t off = (uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8;
+    if (nvalid >= 16 * NJ) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int r = (tid >> 4) + 16 * j;
-        if (r < nvalid) {
-            dst[j] = *(const uint4*)(src + ((size_t)(t0 + r) * H + h) * D + col);
-        } else {
-            dst[j] = make_uint4(0u, 0u, 0u, 0u);
+        for (int j = 0; j < NJ; ++j) dst[j] = *(const uint4*)(blk + off + (uint32_t)(16 * j) * rs);
+    } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int r = (tid >> 4) + 16 * j;
+            dst[j] = r < nvalid ? *(const uint4*)(blk + off + (uint32_t)(16 * j) * rs)
+                                : make_uint4(0u, 0u, 0u, 0u);
         }
     }
+}
+
+// First element of token t, head h of a [tokens, H, D] tensor.
+__device__ __forceinline__ const uint16_t* head_row(const uint16_t* p, int64_t t, int H, int h) {
+    return p + ((size_t)t * H + h) * D;
 }
 
 __device__ __forceinline__ void silu8(const uint4& w, float (&f)[8]) {
@@ -240,18 +250,22 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     float zacc = 0.f;
 
     const int ntiles = (it.len + TB - 1) / TB;
+    const uint32_t rs = (uint32_t)H * D;
+    const uint16_t* kb = head_row(k, it.t0, H, h);
+    const uint16_t* vb = head_row(v, it.t0, H, h);
     uint4 rk[L::NJ], rv[L::NJ];
-    load_tile<L::NJ>(rk, k, it.t0, min(TB, it.len), H, h, tid);
-    load_tile<L::NJ>(rv, v, it.t0, min(TB, it.len), H, h, tid);
+    load_tile<L::NJ>(rk, kb, rs, min(TB, it.len), tid);
+    load_tile<L::NJ>(rv, vb, rs, min(TB, it.len), tid);
     for (int ti = 0; ti < ntiles; ++ti) {
         const int nvalid = min(TB, it.len - ti * TB);
         __syncthreads();
         stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         if (ti + 1 < ntiles) {
-            const int64_t t1 = it.t0 + (int64_t)(ti + 1) * TB;
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
-            load_tile<L::NJ>(rk, k, t1, nv1, H, h, tid);
-            load_tile<L::NJ>(rv, v, t1, nv1, H, h, tid);
+            kb += (size_t)TB * rs;
+            vb += (size_t)TB * rs;
+            load_tile<L::NJ>(rk, kb, rs, nv1, tid);
+            load_tile<L::NJ>(rv, vb, rs, nv1, tid);
         }
         __syncthreads();
         if (NORM && tid < D)
@@ -292,18 +306,70 @@ struct GateArgs {
     int team;
     int spin_limit;
 };
-constexpr int NSLOT = 4;     // exchange slots per team: members are at most 2 blocks apart
+constexpr int NSLOT = 4;     // exchange slots per team (2 suffice: see publish order)
 constexpr int FUSE_HMAX = 8; // heads per token the fused gate handles (more: separate gate)
 
 // ---- fused gate helpers ----
 
-// After a barrier: this head's per-token sums of y^2 of the stashed block
-// (summed over the 4 waves' column groups) go to the exchange buffer tagged
-// with the block's sequence number.
+// Keep the block's Y in LDS until its gate one block later (each wave
+// writes, and later reads, only its own 32 columns), put its per-wave sums
+// of y^2 per token in ssw[wave][row], and load its gate input.
 template <int TB>
-__device__ __forceinline__ void publish_ssq(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga, int H,
-                                            int h, uint32_t& tag) {
-    ++tag;
+__device__ __forceinline__ void stash_block(SmemMain<TB>& sm, const f32x4_t (&acc)[2][Tile<TB>::NQT],
+                                            uint2 (&xr)[2][Tile<TB>::NQT], const uint16_t* xb,
+                                            uint32_t rs, int nvalid, int wave, int g, int c) {
+#pragma unroll
+    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
+        const int row = 16 * qt + c;
+        float ss = 0.f;
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt) {
+            *(f32x4_t*)&sm.ystash[row * (D + 4) + 32 * wave + 16 * dvt + 4 * g] = acc[dvt][qt];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += acc[dvt][qt][i] * acc[dvt][qt][i];
+            xr[dvt][qt] = row < nvalid ? *(const uint2*)(xb + (uint32_t)row * rs + 16 * dvt)
+                                       : make_uint2(0u, 0u);
+        }
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (g == 0) sm.ssw[wave * TB + row] = ss;
+    }
+}
+
+// After gather_ssq and a barrier: out = y / sqrt(mean over the token's H*D
+// features of y^2 + eps) * w * sigmoid(x) for the stashed block.
+template <int TB, typename OutT>
+__device__ __forceinline__ void gate_block(const SmemMain<TB>& sm, OutT* __restrict__ out,
+                                           const uint2 (&xr)[2][Tile<TB>::NQT], float inv_f, float eps,
+                                           int64_t t0, int nvalid, int H, int h, int wave, int g,
+                                           int c) {
+#pragma unroll
+    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
+        const int row = 16 * qt + c;
+        if (row < nvalid) {
+            const float r = rsqrtf(sm.ssum[row] * inv_f + eps);
+            OutT* dst = out + ((size_t)(t0 + row) * H + h) * D + 32 * wave + 4 * g;
+#pragma unroll
+            for (int dvt = 0; dvt < 2; ++dvt) {
+                const f32x4_t yv = *(const f32x4_t*)&sm.ystash[row * (D + 4) + 32 * wave + 16 * dvt + 4 * g];
+                const f32x4_t wv = *(const f32x4_t*)&sm.wgate[32 * wave + 16 * dvt + 4 * g];
+                const float xs[4] = {bf16_lo_to_f32(xr[dvt][qt].x), bf16_hi_to_f32(xr[dvt][qt].x),
+                                     bf16_lo_to_f32(xr[dvt][qt].y), bf16_hi_to_f32(xr[dvt][qt].y)};
+                f32x4_t o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = yv[i] * r * wv[i] * sigmoid(xs[i]);
+                store4<OutT>(dst + 16 * dvt, o, 1.f);
+            }
+        }
+    }
+}
+
+// After a barrier: the head's per-token sums (the 4 waves' column groups
+// added) go to its slot of the exchange buffer, tagged with the block's
+// sequence number.  Threads of wave 0 only.
+template <int TB>
+__device__ __forceinline__ void publish_ssq(const SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
+                                            int H, int h, uint32_t tag) {
     const int tid = threadIdx.x;
     if (tid < TB) {
         const float ss = (sm.ssw[tid] + sm.ssw[TB + tid]) + (sm.ssw[2 * TB + tid] + sm.ssw[3 * TB + tid]);
@@ -313,91 +379,60 @@ __device__ __forceinline__ void publish_ssq(SmemMain<TB>& sm, const GateArgs<uin
     }
 }
 
-// Keep the block's Y (acc) in LDS for the gate one block later, load its
-// gate input, and put its per-wave sums of y^2 in LDS.
+// Wave 0, in two steps: gather_issue starts the loads of the team's words
+// for block `tag` (lane l: words l + 64j, i.e. head l/32 + 2j, token l%32);
+// gather_finish, later, re-reads (bounded) any word whose tag is not yet
+// current, then ssum[token] = sum over heads.  The heads are added in a
+// fixed order, so the sum does not depend on timing.
 template <int TB>
-__device__ __forceinline__ void stash_block(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
-                                            const f32x4_t (&acc)[2][Tile<TB>::NQT],
-                                            uint2 (&xprev)[2][Tile<TB>::NQT], int64_t tt0,
-                                            int nvalid, int H, int h, int wave, int g, int c) {
+__device__ __forceinline__ void gather_issue(const GateArgs<uint16_t>& ga, int H, uint32_t tag,
+                                             int lane, uint64_t (&word)[4]) {
+    static_assert(TB == 32, "the fused gate runs on 32-token blocks");
+    const uint64_t* slot = ga.xbuf + ((size_t)ga.team * NSLOT + (tag % NSLOT)) * H * TB;
 #pragma unroll
-    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
-        const int row = 16 * qt + c;
-        float ss = 0.f;
-#pragma unroll
-        for (int dvt = 0; dvt < 2; ++dvt) {
-            const int col = 32 * wave + 16 * dvt + 4 * g;
-            *(f32x4_t*)&sm.ystash[row * (D + 4) + col] = acc[dvt][qt];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ss += acc[dvt][qt][i] * acc[dvt][qt][i];
-            xprev[dvt][qt] = make_uint2(0u, 0u);
-            if (row < nvalid)
-                xprev[dvt][qt] = *(const uint2*)(ga.x + ((size_t)(tt0 + row) * H + h) * D + col);
-        }
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (g == 0) sm.ssw[wave * TB + row] = ss;
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        word[j] = e < H * TB ? __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : (uint64_t)tag << 32;
     }
 }
 
-// Wait for every head's sums of the stashed block, then write
-// out = y / sqrt(mean over the token's H*D features of y^2 + eps) * w * sigmoid(x).
-template <int TB, typename OutT>
-__device__ __forceinline__ void gate_block(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
-                                           OutT* __restrict__ out,
-                                           const uint2 (&xprev)[2][Tile<TB>::NQT], int64_t tprev,
-                                           int nprev, int H, int h, uint32_t tag, int wave, int g,
-                                           int c) {
-    const int tid = threadIdx.x;
+template <int TB>
+__device__ __forceinline__ void gather_finish(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
+                                              int H, uint32_t tag, int lane, uint64_t (&word)[4]) {
     const uint64_t* slot = ga.xbuf + ((size_t)ga.team * NSLOT + (tag % NSLOT)) * H * TB;
-    for (int e = tid; e < H * TB; e += NT) {
-        uint64_t word = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int n = 0; (uint32_t)(word >> 32) != tag && n < ga.spin_limit; ++n) {
-            __builtin_amdgcn_s_sleep(2);
-            word = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        sm.ssall[(e % TB) * FUSE_HMAX + e / TB] = __uint_as_float((uint32_t)word);
-    }
-    __syncthreads();
-    const float inv_f = 1.f / (float)(H * D);
+    for (int n = 0; n < ga.spin_limit; ++n) {
+        bool ready = true;
 #pragma unroll
-    for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
-        const int row = 16 * qt + c;
-        if (row >= nprev) continue;
-        // heads summed in a fixed order: the result does not depend on timing
-        float ss = 0.f;
-        for (int hh = 0; hh < H; ++hh) ss += sm.ssall[row * FUSE_HMAX + hh];
-        const float r = 1.0f / sqrtf(ss * inv_f + ga.eps);
-        OutT* dst = out + ((size_t)(tprev + row) * H + h) * D + 32 * wave + 4 * g;
+        for (int j = 0; j < 4; ++j) ready = ready && (word[j] >> 32) == (uint64_t)tag;
+        if (ready) break;
+        __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-        for (int dvt = 0; dvt < 2; ++dvt) {
-            const int col = 32 * wave + 16 * dvt + 4 * g;
-            const int f = h * D + col;
-            const f32x4_t yv = *(const f32x4_t*)&sm.ystash[row * (D + 4) + col];
-            float xs[4] = {bf16_lo_to_f32(xprev[dvt][qt].x), bf16_hi_to_f32(xprev[dvt][qt].x),
-                           bf16_lo_to_f32(xprev[dvt][qt].y), bf16_hi_to_f32(xprev[dvt][qt].y)};
-            f32x4_t o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = yv[i] * r * (ga.w ? ga.w[f + i] : 1.f) * sigmoid(xs[i]);
-            store4<OutT>(dst + 16 * dvt, o, 1.f);
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane + 64 * j;
+            if ((word[j] >> 32) != (uint64_t)tag)
+                word[j] = __hip_atomic_load(slot + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    float ss = (__uint_as_float((uint32_t)word[0]) + __uint_as_float((uint32_t)word[1])) +
+               (__uint_as_float((uint32_t)word[2]) + __uint_as_float((uint32_t)word[3]));
+    ss += __shfl_xor(ss, 32, 64);
+    if (lane < TB) sm.ssum[lane] = ss;
 }
 
 // Main pass over one (chunk, head).  Starting state: prefix[item][h] if
 // prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
 // chunk is a whole sequence (no prefix), the final state is written to
 // state_out/z_out (if given).  Unfused: Y goes to y[t][h*D + j].  Fused: the
-// gated output goes there instead, one block after Y (tag_base + block index
-// numbers the exchange).  k16 must be 16.
+// gated output goes there instead; the heads of the chunk exchange each
+// block's per-token sums of y^2 (tag = block number + 1).  k16 must be 16.
 template <bool NORM, bool FUSE, typename OutT, typename InT, int TB>
 __device__ __forceinline__ void process_item(
     SmemMain<TB>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const Item& it, int item, int H, int h,
     const float* __restrict__ prefix, int64_t prefix_stride, const float* __restrict__ state_in,
     const float* __restrict__ z_in, OutT* __restrict__ y, float* state_out, float* z_out, int k16,
-    const GateArgs<InT>& ga, uint32_t& tag) {
+    const GateArgs<InT>& ga) {
     using L = Tile<TB>;
     constexpr int PS = L::PS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
@@ -430,17 +465,28 @@ __device__ __forceinline__ void process_item(
                 S[dkt][dvt][i] = s0 ? s0[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] : 0.f;
     if (NORM && tid < D) sm.z[tid] = z0 ? z0[tid] : 0.f;
 
-    // fused gate: the previous block's Y and gate input wait here for the
-    // other heads' sums of squares
-    uint2 xprev[2][L::NQT];
+    // fused gate: the gate of block n runs one block later, when the other heads' sums of
+    // y^2 for it have had a block's time to arrive
+    uint2 xr[2][L::NQT];  // gate input of the stashed block
+    const uint16_t* xb = nullptr;
+    float inv_f = 0.f;
     int64_t tprev = 0;
     int nprev = 0;
+    if constexpr (FUSE) {
+        if (tid < D) sm.wgate[tid] = ga.w ? ga.w[h * D + tid] : 1.f;  // read after the first barrier
+        xb = ga.x + ((size_t)it.t0 * H + h) * D + 32 * wave + 4 * g;
+        inv_f = 1.f / (float)(H * D);
+    }
 
     const int ntiles = (it.len + TB - 1) / TB;
+    const uint32_t rs = (uint32_t)H * D;
+    const uint16_t* qb = head_row(q, it.t0, H, h);
+    const uint16_t* kb = head_row(k, it.t0, H, h);
+    const uint16_t* vb = head_row(v, it.t0, H, h);
     uint4 rq[L::NJ], rk[L::NJ], rv[L::NJ];
-    load_tile<L::NJ>(rq, q, it.t0, min(TB, it.len), H, h, tid);
-    load_tile<L::NJ>(rk, k, it.t0, min(TB, it.len), H, h, tid);
-    load_tile<L::NJ>(rv, v, it.t0, min(TB, it.len), H, h, tid);
+    load_tile<L::NJ>(rq, qb, rs, min(TB, it.len), tid);
+    load_tile<L::NJ>(rk, kb, rs, min(TB, it.len), tid);
+    load_tile<L::NJ>(rv, vb, rs, min(TB, it.len), tid);
 
     for (int ti = 0; ti < ntiles; ++ti) {
         const int64_t tt0 = it.t0 + (int64_t)ti * TB;
@@ -449,7 +495,9 @@ __device__ __forceinline__ void process_item(
         const int nqt = 2 * nks;
 
         __syncthreads();  // previous block's LDS reads and z update are done
-        if (FUSE && ti > 0) publish_ssq<TB>(sm, ga, H, h, tag);
+        if constexpr (FUSE) {
+            if (ti > 0) publish_ssq<TB>(sm, ga, H, h, (uint32_t)ti);
+        }
         {
             const int col = (tid & 15) * 8;
 #pragma unroll
@@ -472,11 +520,13 @@ __device__ __forceinline__ void process_item(
             stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         }
         if (ti + 1 < ntiles) {
-            const int64_t t1 = tt0 + TB;
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
-            load_tile<L::NJ>(rq, q, t1, nv1, H, h, tid);
-            load_tile<L::NJ>(rk, k, t1, nv1, H, h, tid);
-            load_tile<L::NJ>(rv, v, t1, nv1, H, h, tid);
+            qb += (size_t)TB * rs;
+            kb += (size_t)TB * rs;
+            vb += (size_t)TB * rs;
+            load_tile<L::NJ>(rq, qb, rs, nv1, tid);
+            load_tile<L::NJ>(rk, kb, rs, nv1, tid);
+            load_tile<L::NJ>(rv, vb, rs, nv1, tid);
         }
         __syncthreads();
         if (NORM && tid < D)  // read again only after the next block's first barrier
@@ -516,17 +566,23 @@ __device__ __forceinline__ void process_item(
                     // row sums over this tile's 16 keys (the 16 lanes of a group)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float rs = acc[i];
-                        rs += __shfl_xor(rs, 1, 64);
-                        rs += __shfl_xor(rs, 2, 64);
-                        rs += __shfl_xor(rs, 4, 64);
-                        rs += __shfl_xor(rs, 8, 64);
-                        if (c == 0) sm.denp[kt * TB + 16 * qt + 4 * g + i] = rs;
+                        float rsum = acc[i];
+                        rsum += __shfl_xor(rsum, 1, 64);
+                        rsum += __shfl_xor(rsum, 2, 64);
+                        rsum += __shfl_xor(rsum, 4, 64);
+                        rsum += __shfl_xor(rsum, 8, 64);
+                        if (c == 0) sm.denp[kt * TB + 16 * qt + 4 * g + i] = rsum;
                     }
                 }
             }
         }
         __syncthreads();
+        // fused gate: the previous block's sums were published at the top of
+        // this block; start reading them now, use them after the products
+        uint64_t xw[4];
+        if constexpr (FUSE) {
+            if (ti > 0 && wave == 0) gather_issue<TB>(ga, H, (uint32_t)ti, lane, xw);
+        }
 
         // ---- Y^T = V^T P^T (intra) + S^T Q^T (inter), this wave's 32 columns ----
         f32x4_t acc[2][L::NQT];
@@ -568,10 +624,10 @@ __device__ __forceinline__ void process_item(
 #pragma unroll
             for (int dvt = 0; dvt < 2; ++dvt) {
                 uint4 ah, al;
-                split2(S[2 * s][dvt][0], S[2 * s][dvt][1], ah.x, al.x);
-                split2(S[2 * s][dvt][2], S[2 * s][dvt][3], ah.y, al.y);
-                split2(S[2 * s + 1][dvt][0], S[2 * s + 1][dvt][1], ah.z, al.z);
-                split2(S[2 * s + 1][dvt][2], S[2 * s + 1][dvt][3], ah.w, al.w);
+                split2_keep(S[2 * s][dvt][0], S[2 * s][dvt][1], ah.x, al.x);
+                split2_keep(S[2 * s][dvt][2], S[2 * s][dvt][3], ah.y, al.y);
+                split2_keep(S[2 * s + 1][dvt][0], S[2 * s + 1][dvt][1], ah.z, al.z);
+                split2_keep(S[2 * s + 1][dvt][2], S[2 * s + 1][dvt][3], ah.w, al.w);
                 Ah[dvt] = as_bf16x8(ah);
                 Al[dvt] = as_bf16x8(al);
             }
@@ -601,7 +657,7 @@ __device__ __forceinline__ void process_item(
                 for (int dvt = 0; dvt < 2; ++dvt) acc[dvt][qt] *= sc;
             }
         }
-        if (!FUSE) {
+        if constexpr (!FUSE) {
 #pragma unroll
             for (int qt = 0; qt < L::NQT; ++qt) {
                 const int row = 16 * qt + c;
@@ -612,20 +668,32 @@ __device__ __forceinline__ void process_item(
                 }
             }
         } else {
-            if (ti > 0) gate_block<TB>(sm, ga, y, xprev, tprev, nprev, H, h, tag, wave, g, c);
-            __syncthreads();  // the stash is read by other waves' gate above
-            stash_block<TB>(sm, ga, acc, xprev, tt0, nvalid, H, h, wave, g, c);
+            if (ti > 0) {
+                // the previous block: every head published its sums at the
+                // top of this block
+                if (wave == 0) gather_finish<TB>(sm, ga, H, (uint32_t)ti, lane, xw);
+                __syncthreads();
+                gate_block<TB, OutT>(sm, y, xr, inv_f, ga.eps, tprev, nprev, H, h, wave, g, c);
+            }
+            stash_block<TB>(sm, acc, xr, xb, rs, nvalid, wave, g, c);
             tprev = tt0;
             nprev = nvalid;
+            xb += (size_t)TB * rs;
         }
 
         // ---- S += phi(K)^T phi(V) ----
         state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
     }
-    if (FUSE) {
+    if constexpr (FUSE) {
         __syncthreads();
-        publish_ssq<TB>(sm, ga, H, h, tag);
-        gate_block<TB>(sm, ga, y, xprev, tprev, nprev, H, h, tag, wave, g, c);
+        publish_ssq<TB>(sm, ga, H, h, (uint32_t)ntiles);
+        if (wave == 0) {
+            uint64_t w[4];
+            gather_issue<TB>(ga, H, (uint32_t)ntiles, lane, w);
+            gather_finish<TB>(sm, ga, H, (uint32_t)ntiles, lane, w);
+        }
+        __syncthreads();
+        gate_block<TB, OutT>(sm, y, xr, inv_f, ga.eps, tprev, nprev, H, h, wave, g, c);
     }
 
     if (!prefix) {
@@ -644,7 +712,6 @@ __device__ __forceinline__ void process_item(
             if (tid < D) z_out[((size_t)it.seq * H + h) * D + tid] = sm.z[tid];
         }
     }
-    __syncthreads();  // the next item reuses the LDS
 }
 
 // Unfused main pass: one workgroup per (chunk = blockIdx.x, head = blockIdx.y).
@@ -658,10 +725,9 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
     Item it;
     if (!decode_item(map, blockIdx.x, it)) return;
     GateArgs<uint16_t> ga{};
-    uint32_t tag = 0;
     process_item<NORM, false, OutT, uint16_t, TB>(sm, q, k, v, it, blockIdx.x, H, blockIdx.y,
                                                    prefix, prefix_stride, state_in, z_in, y,
-                                                   state_out, z_out, k16, ga, tag);
+                                                   state_out, z_out, k16, ga);
 }
 
 // Fused main pass + gate, one workgroup per (chunk = blockIdx.x / H, head =
@@ -680,10 +746,9 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_fused(
     Item it;
     if (!decode_item(map, item, it)) return;  // the whole team returns together
     GateArgs<uint16_t> ga{x, w, eps, xbuf, item, spin_limit};
-    uint32_t tag = 0;
     process_item<NORM, true, OutT, uint16_t, TB>(sm, q, k, v, it, item, H, h, prefix,
                                                   prefix_stride, state_in, z_in, out, state_out,
-                                                  z_out, k16, ga, tag);
+                                                  z_out, k16, ga);
 }
 
 }  // namespace mf

@@ -165,6 +165,25 @@ def test_prefill_32k_workload():
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
 
 
+@pytest.mark.parametrize("gated,block", [(False, 32), (False, 64), (True, 32)])
+def test_bf16_split_precision_canary(gated, block):
+    """The matrix-core path splits every operand into bf16 hi + lo (about 16
+    significant bits), so its error sits near 1e-5 .. 1e-4 of rms here.  A
+    split that lost its low part would err by ~1e-3 and still pass the 1e-2
+    tolerance; this bound (5e-4, an implementation check, not the tolerance)
+    catches that."""
+    banner("bf16 split precision canary gated=%s block=%d" % (gated, block))
+    T, H, d = 1000, 2, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((1, T, H, d), 180 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((1, T, H * d), 183, dtype=torch.bfloat16) if gated else None
+    out, S, _ = run_prefill(q, k, v, x, block_size=block)
+    ref, Sref, _ = oracle_forward(q, k, v, x)
+    e_out, e_S = rel_err(np64(out), ref), rel_err(np64(S), Sref)
+    print("canary: rel err out %.3e state %.3e" % (e_out, e_S))
+    assert e_out <= 5e-4 and e_S <= 5e-4
+
+
 # ---------------------------------------------------------- fused gate path --
 # bf16 d=128 gated calls whose (chunk, head) workgroups fit on the device at
 # once run the gate inside the main pass (heads of a chunk exchange their
