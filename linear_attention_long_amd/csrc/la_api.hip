@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kMfmaDefaultBlock = 32;   // bf16 d=128: two workgroups per CU
 constexpr int kValuDefaultBlock = 64;
-constexpr int kStateTile = 64;          // tile of the chunk-state kernel (any block size)
 constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
 constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
@@ -256,8 +255,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     if (p.chunked) {
         tm.before();
         if (p.mfma) {
-            if (norm) mf::k_chunk_state<true, kStateTile><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
-            else mf::k_chunk_state<false, kStateTile><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            if (norm) mf::k_chunk_state<true><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            else mf::k_chunk_state<false><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
         } else if (d == 128) {
             if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
             else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);

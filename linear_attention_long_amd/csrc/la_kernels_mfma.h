@@ -36,6 +36,8 @@
 //    current block computes.
 #pragma once
 
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_items.h"
 
@@ -84,14 +86,15 @@ struct __attribute__((aligned(16))) SmemMain {
     __attribute__((aligned(16))) float ystash[FB * (D + 4)];  // Y of the block awaiting its gate
 };
 
-// (only transposing reads, which are never fused: no padding)
-template <int TB>
+// Chunk-state pass: two 32-token buffers (only transposing reads, which are
+// never fused: no padding).
 struct __attribute__((aligned(16))) SmemState {
-    __attribute__((aligned(16))) uint16_t kh[TB * KS];
-    __attribute__((aligned(16))) uint16_t kl[TB * KS];
-    __attribute__((aligned(16))) uint16_t vh[TB * KS];
-    __attribute__((aligned(16))) uint16_t vl[TB * KS];
-    float zpart[4 * D];
+    static constexpr int TB = 32;
+    __attribute__((aligned(16))) uint16_t kh[2][TB * KS];
+    __attribute__((aligned(16))) uint16_t kl[2][TB * KS];
+    __attribute__((aligned(16))) uint16_t vh[2][TB * KS];
+    __attribute__((aligned(16))) uint16_t vl[2][TB * KS];
+    float zpart[2][4 * D];
 };
 
 // Thread tid loads rows (tid>>4) + 16j, j < NJ, columns (tid&15)*8 .. +7 of
@@ -118,6 +121,28 @@ __device__ __forceinline__ void load_tile(uint4 (&dst)[NJ], const uint16_t* __re
 // First element of token t, head h of a [tokens, H, D] tensor.
 __device__ __forceinline__ const uint16_t* head_row(const uint16_t* p, int64_t t, int H, int h) {
     return p + ((size_t)t * H + h) * D;
+}
+
+// Buffer resource over the rows [0, nvalid) of one head's tile starting at
+// `blk` (row stride rs elements): loads past the last valid row return zero
+// with no memory access (nvalid <= 0: every load does).  Word 3 is the gfx9
+// raw-buffer configuration (32-bit data format, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* blk, uint32_t rs,
+                                                            int nvalid) {
+    const int32_t bytes = nvalid > 0 ? (int32_t)((uint32_t)(nvalid - 1) * rs * 2u + 2u * D) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, bytes, 0x00020000);
+}
+
+// load_tile through a tile_rsrc: no branches, zeros past the valid rows.
+template <int NJ>
+__device__ __forceinline__ void load_tile_buf(uint4 (&dst)[NJ], __amdgpu_buffer_rsrc_t rsrc,
+                                              uint32_t rs, int tid) {
+    const uint32_t off = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + (uint32_t)(16 * j) * rs * 2u, 0, 0);
+        dst[j] = __builtin_bit_cast(uint4, w);
+    }
 }
 
 __device__ __forceinline__ void silu8(const uint4& w, float (&f)[8]) {
@@ -230,14 +255,20 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
 
 // Per-chunk state increment dS = sum_{t in chunk} phi(k_t) phi(v_t)^T (and
 // dz = sum phi(k_t)), written to buf[item][h] = [dS (D*D) | dz (D)].
-template <bool NORM, int TB>
+// Software-pipelined over 32-token blocks with two LDS buffers: in step n
+// the workgroup stages block n+1 (SiLU + split, vector ALU) into one buffer
+// while the state update of block n (matrix cores) reads the other, with
+// one barrier per step; raw k, v are loaded two blocks ahead.
+template <bool NORM>
 __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, ItemMap map,
                                                        int H, float* __restrict__ buf,
                                                        int64_t buf_stride) {
+    constexpr int TB = SmemState::TB;
     using L = Tile<TB>;
-    __shared__ SmemState<TB> sm;
+    __shared__ SmemState sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+    (void)lane;
     const int h = blockIdx.y;
     Item it;
     if (!decode_item(map, blockIdx.x, it)) return;
@@ -254,23 +285,44 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     const uint16_t* kb = head_row(k, it.t0, H, h);
     const uint16_t* vb = head_row(v, it.t0, H, h);
     uint4 rk[L::NJ], rv[L::NJ];
-    load_tile<L::NJ>(rk, kb, rs, min(TB, it.len), tid);
-    load_tile<L::NJ>(rv, vb, rs, min(TB, it.len), tid);
-    for (int ti = 0; ti < ntiles; ++ti) {
-        const int nvalid = min(TB, it.len - ti * TB);
-        __syncthreads();
-        stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
-        if (ti + 1 < ntiles) {
-            const int nv1 = min(TB, it.len - (ti + 1) * TB);
-            kb += (size_t)TB * rs;
-            vb += (size_t)TB * rs;
-            load_tile<L::NJ>(rk, kb, rs, nv1, tid);
-            load_tile<L::NJ>(rv, vb, rs, nv1, tid);
+    // block 0 staged, block 1 in registers
+    load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, it.len), rs, tid);
+    load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, it.len), rs, tid);
+    stage_kv<NORM, L::NJ>(rk, rv, sm.kh[0], sm.kl[0], sm.vh[0], sm.vl[0], sm.zpart[0], tid);
+    kb += (size_t)TB * rs;
+    vb += (size_t)TB * rs;
+    load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, it.len - TB), rs, tid);
+    load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, it.len - TB), rs, tid);
+    __syncthreads();
+    // one step: state update of block ti from buffer CUR, staging of block
+    // ti+1 into the other buffer, loads of block ti+2 (the buffers are
+    // compile-time distinct, so the update's reads and the staging's writes
+    // may interleave)
+    auto step = [&](auto cur_tag, int ti) {
+        constexpr int CUR = decltype(cur_tag)::value;
+        if (NORM && tid < D)
+            zacc += (sm.zpart[CUR][tid] + sm.zpart[CUR][D + tid]) +
+                    (sm.zpart[CUR][2 * D + tid] + sm.zpart[CUR][3 * D + tid]);
+        uint4 nk[L::NJ], nv[L::NJ];
+        kb += (size_t)TB * rs;
+        vb += (size_t)TB * rs;
+        const int n2 = it.len - (ti + 2) * TB;
+        load_tile_buf<L::NJ>(nk, tile_rsrc(kb, rs, n2), rs, tid);
+        load_tile_buf<L::NJ>(nv, tile_rsrc(vb, rs, n2), rs, tid);
+        state_update<1>(S, sm.kh[CUR], sm.kl[CUR], sm.vh[CUR], sm.vl[CUR], 1, wave, g, c);
+        stage_kv<NORM, L::NJ>(rk, rv, sm.kh[CUR ^ 1], sm.kl[CUR ^ 1], sm.vh[CUR ^ 1],
+                              sm.vl[CUR ^ 1], sm.zpart[CUR ^ 1], tid);
+#pragma unroll
+        for (int j = 0; j < L::NJ; ++j) {
+            rk[j] = nk[j];
+            rv[j] = nv[j];
         }
         __syncthreads();
-        if (NORM && tid < D)
-            zacc += (sm.zpart[tid] + sm.zpart[D + tid]) + (sm.zpart[2 * D + tid] + sm.zpart[3 * D + tid]);
-        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nvalid <= 32 ? 1 : L::NKS, wave, g, c);
+    };
+    for (int ti = 0; ti < ntiles; ti += 2) {
+        step(std::integral_constant<int, 0>{}, ti);
+        if (ti + 1 == ntiles) break;
+        step(std::integral_constant<int, 1>{}, ti + 1);
     }
     float* dst = buf + ((size_t)blockIdx.x * H + h) * buf_stride;
 #pragma unroll
