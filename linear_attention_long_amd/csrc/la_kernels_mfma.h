@@ -46,8 +46,13 @@ namespace mf {
 
 constexpr int D = 128;   // head dim
 constexpr int NT = 256;  // threads per workgroup
-constexpr int QS = 136;  // LDS row stride of the Q tile (bf16 elements)
-constexpr int KS = 144;  // LDS row stride of the K and V tiles
+// LDS row strides (bf16 elements).  Q is read only along rows, two 8-byte
+// pieces per lane that the compiler merges into one ds_read2_b64: at a
+// stride of 132 (264 bytes) such pairs hit 64 distinct banks, at 136 or 144
+// they conflict (measured).  K and V are read by transposing reads, which
+// need 144; their row reads (K in P) stay single 8-byte reads.
+constexpr int QS = 132;  // Q tile
+constexpr int KS = 144;  // K and V tiles
 // 16 bytes after each LDS array: neighbouring hi/lo arrays then are not a
 // multiple of 512 bytes apart, so the compiler cannot fuse a read of one with
 // a read of the other into a ds_read2st64 that lands both halves in the same
@@ -166,6 +171,19 @@ __device__ __forceinline__ void store_split8(const float (&f)[8], uint16_t* dh, 
     *(uint4*)dl = lo;
 }
 
+// The same into rows that are only 8-byte aligned (the Q tile).
+__device__ __forceinline__ void store_split8_a8(const float (&f)[8], uint16_t* dh, uint16_t* dl) {
+    uint2 h0, h1, l0, l1;
+    split2(f[0], f[1], h0.x, l0.x);
+    split2(f[2], f[3], h0.y, l0.y);
+    split2(f[4], f[5], h1.x, l1.x);
+    split2(f[6], f[7], h1.y, l1.y);
+    *(uint2*)dh = h0;
+    *(uint2*)(dh + 4) = h1;
+    *(uint2*)dl = l0;
+    *(uint2*)(dl + 4) = l1;
+}
+
 // phi(k) and phi(v) of the block into LDS (hi/lo); with NORM, column sums of
 // phi(k) over the wave's rows into zpart[wave][col..col+7].
 template <bool NORM, int NJ>
@@ -211,9 +229,10 @@ __device__ __forceinline__ bf16x8_t tr_operand(const uint16_t* tile, int stride,
 }
 
 // Operand over 32 columns (head-dim features) of one row for the permuted k
-// order: columns {k0 + 4g + i, k0 + 16 + 4g + i} of row `row`.  `k16` is 16
-// at run time; passing it as a value keeps the two 8-byte reads separate
-// (a merged 2 x 8-byte read conflicts on LDS banks, two single ones do not).
+// order: columns {k0 + 4g + i, k0 + 16 + 4g + i} of row `row`.  With k16 a
+// literal 16 the compiler merges the two 8-byte reads into one ds_read2_b64
+// (conflict-free at the Q stride); passed as a run-time value (16), it keeps
+// them separate, which the K stride needs.
 __device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, int stride, int row, int k0,
                                                 int g, int k16) {
     const uint16_t* p = tile + row * stride + k0 + 4 * g;
@@ -557,7 +576,7 @@ __device__ __forceinline__ void process_item(
                 const int r = (tid >> 4) + 16 * j;
                 float f[8];
                 silu8(rq[j], f);
-                store_split8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
+                store_split8_a8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
                 if (NORM) {
                     float part = 0.f;
 #pragma unroll
@@ -594,10 +613,11 @@ __device__ __forceinline__ void process_item(
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const bf16x8_t ah = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
-                    const bf16x8_t al = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
-                    const bf16x8_t bh = row_operand(sm.kh, KS, 16 * kt + c, 32 * s, g, k16);
-                    const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 32 * s, g, k16);
+                    const bf16x8_t ah = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, 16);
+                    const bf16x8_t al = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
+                    // run-time column steps: no merged K reads (they conflict at KS)
+                    const bf16x8_t bh = row_operand(sm.kh, KS, 16 * kt + c, 2 * k16 * s, g, k16);
+                    const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 2 * k16 * s, g, k16);
                     acc = mfma16x16x32(ah, bh, acc);
                     acc = mfma16x16x32(ah, bl, acc);
                     acc = mfma16x16x32(al, bh, acc);
@@ -686,8 +706,8 @@ __device__ __forceinline__ void process_item(
 #pragma unroll
             for (int qt = 0; qt < L::NQT; ++qt) {
                 if (qt < nqt) {
-                    const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, k16);
-                    const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, k16);
+                    const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, 16);
+                    const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
 #pragma unroll
                     for (int dvt = 0; dvt < 2; ++dvt) {
                         acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bh, acc[dvt][qt]);
