@@ -138,6 +138,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* blk,
     return __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, bytes, 0x00020000);
 }
 
+// Buffer resource over `nrows` rows of `width_bytes` each, `row_bytes` apart,
+// from `base`: accesses past the last row are dropped (stores) or read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t row_bytes,
+                                                            uint32_t width_bytes, int nrows) {
+    const int32_t bytes = nrows > 0 ? (int32_t)((uint32_t)(nrows - 1) * row_bytes + width_bytes) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// Four outputs at element offset `off` through a rows_rsrc (dropped past its rows).
+template <typename OutT>
+__device__ __forceinline__ void store4_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v);
+template <>
+__device__ __forceinline__ void store4_buf<float>(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off * 4u, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store4_buf<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+    const u32x2_t u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, off * 2u, 0, 0);
+}
+
 // load_tile through a tile_rsrc: no branches, zeros past the valid rows.
 template <int NJ>
 __device__ __forceinline__ void load_tile_buf(uint4 (&dst)[NJ], __amdgpu_buffer_rsrc_t rsrc,
@@ -384,11 +408,13 @@ constexpr int FUSE_HMAX = 8; // heads per token the fused gate handles (more: se
 
 // Keep the block's Y in LDS until its gate one block later (each wave
 // writes, and later reads, only its own 32 columns), put its per-wave sums
-// of y^2 per token in ssw[wave][row], and load its gate input.
+// of y^2 per token in ssw[wave][row], and load its gate input (xrs: the
+// block's rows of x, zero past the valid ones).
 template <int TB>
 __device__ __forceinline__ void stash_block(SmemMain<TB>& sm, const f32x4_t (&acc)[2][Tile<TB>::NQT],
-                                            uint2 (&xr)[2][Tile<TB>::NQT], const uint16_t* xb,
-                                            uint32_t rs, int nvalid, int wave, int g, int c) {
+                                            uint2 (&xr)[2][Tile<TB>::NQT],
+                                            __amdgpu_buffer_rsrc_t xrs, uint32_t rs, int wave, int g,
+                                            int c) {
 #pragma unroll
     for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
         const int row = 16 * qt + c;
@@ -398,39 +424,38 @@ __device__ __forceinline__ void stash_block(SmemMain<TB>& sm, const f32x4_t (&ac
             *(f32x4_t*)&sm.ystash[row * (D + 4) + 32 * wave + 16 * dvt + 4 * g] = acc[dvt][qt];
 #pragma unroll
             for (int i = 0; i < 4; ++i) ss += acc[dvt][qt][i] * acc[dvt][qt][i];
-            xr[dvt][qt] = row < nvalid ? *(const uint2*)(xb + (uint32_t)row * rs + 16 * dvt)
-                                       : make_uint2(0u, 0u);
+            const uint32_t off = ((uint32_t)row * rs + 32 * wave + 16 * dvt + 4 * g) * 2u;
+            xr[dvt][qt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xrs, off, 0, 0));
         }
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);
-        if (g == 0) sm.ssw[wave * TB + row] = ss;
+        sm.ssw[wave * TB + row] = ss;  // the 4 lane groups hold the same sum: no branch
     }
 }
 
-// After gather_ssq and a barrier: out = y / sqrt(mean over the token's H*D
-// features of y^2 + eps) * w * sigmoid(x) for the stashed block.
+// After gather_finish and a barrier: out = y / sqrt(mean over the token's H*D
+// features of y^2 + eps) * w * sigmoid(x) for the stashed block; `ors`
+// covers its valid output rows (stores past them are dropped), so the code
+// has no branches.
 template <int TB, typename OutT>
-__device__ __forceinline__ void gate_block(const SmemMain<TB>& sm, OutT* __restrict__ out,
+__device__ __forceinline__ void gate_block(const SmemMain<TB>& sm, __amdgpu_buffer_rsrc_t ors,
                                            const uint2 (&xr)[2][Tile<TB>::NQT], float inv_f, float eps,
-                                           int64_t t0, int nvalid, int H, int h, int wave, int g,
-                                           int c) {
+                                           uint32_t rs, int wave, int g, int c) {
 #pragma unroll
     for (int qt = 0; qt < Tile<TB>::NQT; ++qt) {
         const int row = 16 * qt + c;
-        if (row < nvalid) {
-            const float r = rsqrtf(sm.ssum[row] * inv_f + eps);
-            OutT* dst = out + ((size_t)(t0 + row) * H + h) * D + 32 * wave + 4 * g;
+        const float r = rsqrtf(sm.ssum[row] * inv_f + eps);
 #pragma unroll
-            for (int dvt = 0; dvt < 2; ++dvt) {
-                const f32x4_t yv = *(const f32x4_t*)&sm.ystash[row * (D + 4) + 32 * wave + 16 * dvt + 4 * g];
-                const f32x4_t wv = *(const f32x4_t*)&sm.wgate[32 * wave + 16 * dvt + 4 * g];
-                const float xs[4] = {bf16_lo_to_f32(xr[dvt][qt].x), bf16_hi_to_f32(xr[dvt][qt].x),
-                                     bf16_lo_to_f32(xr[dvt][qt].y), bf16_hi_to_f32(xr[dvt][qt].y)};
-                f32x4_t o;
+        for (int dvt = 0; dvt < 2; ++dvt) {
+            const int col = 32 * wave + 16 * dvt + 4 * g;
+            const f32x4_t yv = *(const f32x4_t*)&sm.ystash[row * (D + 4) + col];
+            const f32x4_t wv = *(const f32x4_t*)&sm.wgate[col];
+            const float xs[4] = {bf16_lo_to_f32(xr[dvt][qt].x), bf16_hi_to_f32(xr[dvt][qt].x),
+                                 bf16_lo_to_f32(xr[dvt][qt].y), bf16_hi_to_f32(xr[dvt][qt].y)};
+            f32x4_t o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = yv[i] * r * wv[i] * sigmoid(xs[i]);
-                store4<OutT>(dst + 16 * dvt, o, 1.f);
-            }
+            for (int i = 0; i < 4; ++i) o[i] = yv[i] * r * wv[i] * sigmoid(xs[i]);
+            store4_buf<OutT>(ors, (uint32_t)row * rs + col, o);
         }
     }
 }
@@ -491,6 +516,29 @@ __device__ __forceinline__ void gather_finish(SmemMain<TB>& sm, const GateArgs<u
     if (lane < TB) sm.ssum[lane] = ss;
 }
 
+// phi(q) of the block into the Q tile (hi/lo); with NORM zq[row] = phi(q_row) . z.
+template <bool NORM, int NJ, typename SM>
+__device__ __forceinline__ void stage_q(SM& sm, const uint4 (&rq)[NJ], int tid) {
+    const int col = (tid & 15) * 8;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int r = (tid >> 4) + 16 * j;
+        float f[8];
+        silu8(rq[j], f);
+        store_split8_a8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
+        if (NORM) {
+            float part = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part += f[e] * sm.z[col + e];
+            part += __shfl_xor(part, 1, 64);
+            part += __shfl_xor(part, 2, 64);
+            part += __shfl_xor(part, 4, 64);
+            part += __shfl_xor(part, 8, 64);
+            if ((tid & 15) == 0) sm.zq[r] = part;
+        }
+    }
+}
+
 // Main pass over one (chunk, head).  Starting state: prefix[item][h] if
 // prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
 // chunk is a whole sequence (no prefix), the final state is written to
@@ -539,13 +587,13 @@ __device__ __forceinline__ void process_item(
     // fused gate: the gate of block n runs one block later, when the other heads' sums of
     // y^2 for it have had a block's time to arrive
     uint2 xr[2][L::NQT];  // gate input of the stashed block
-    const uint16_t* xb = nullptr;
-    float inv_f = 0.f;
-    int64_t tprev = 0;
+    const uint16_t* xb = nullptr;  // x rows of the current block (this head)
+    OutT* ob = y;                  // output rows of the stashed block
     int nprev = 0;
+    float inv_f = 0.f;
     if constexpr (FUSE) {
         if (tid < D) sm.wgate[tid] = ga.w ? ga.w[h * D + tid] : 1.f;  // read after the first barrier
-        xb = ga.x + ((size_t)it.t0 * H + h) * D + 32 * wave + 4 * g;
+        xb = ga.x + ((size_t)it.t0 * H + h) * D;
         inv_f = 1.f / (float)(H * D);
     }
 
@@ -558,6 +606,9 @@ __device__ __forceinline__ void process_item(
     load_tile<L::NJ>(rq, qb, rs, min(TB, it.len), tid);
     load_tile<L::NJ>(rk, kb, rs, min(TB, it.len), tid);
     load_tile<L::NJ>(rv, vb, rs, min(TB, it.len), tid);
+    __syncthreads();  // z (normalised mode) is set
+    // the Q tile of block n is staged at the end of block n-1 (here, block 0)
+    stage_q<NORM, L::NJ>(sm, rq, tid);
 
     for (int ti = 0; ti < ntiles; ++ti) {
         const int64_t tt0 = it.t0 + (int64_t)ti * TB;
@@ -569,27 +620,7 @@ __device__ __forceinline__ void process_item(
         if constexpr (FUSE) {
             if (ti > 0) publish_ssq<TB>(sm, ga, H, h, (uint32_t)ti);
         }
-        {
-            const int col = (tid & 15) * 8;
-#pragma unroll
-            for (int j = 0; j < L::NJ; ++j) {
-                const int r = (tid >> 4) + 16 * j;
-                float f[8];
-                silu8(rq[j], f);
-                store_split8_a8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
-                if (NORM) {
-                    float part = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) part += f[e] * sm.z[col + e];
-                    part += __shfl_xor(part, 1, 64);
-                    part += __shfl_xor(part, 2, 64);
-                    part += __shfl_xor(part, 4, 64);
-                    part += __shfl_xor(part, 8, 64);
-                    if ((tid & 15) == 0) sm.zq[r] = part;
-                }
-            }
-            stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
-        }
+        stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         if (ti + 1 < ntiles) {
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
             qb += (size_t)TB * rs;
@@ -729,32 +760,43 @@ __device__ __forceinline__ void process_item(
                 for (int dvt = 0; dvt < 2; ++dvt) acc[dvt][qt] *= sc;
             }
         }
+        if constexpr (FUSE) {
+            // the previous block: every head published its sums at the top
+            // of this block
+            if (ti > 0 && wave == 0) gather_finish<TB>(sm, ga, H, (uint32_t)ti, lane, xw);
+        }
+        __syncthreads();  // every wave's reads of this block's Q tile are done
+
+        // ---- last phase: output, next block's Q tile, S += phi(K)^T phi(V) ----
+        // (no branches on the data, so the vector work can interleave with
+        // the state update's matrix-core work)
+        OutT* yb = y + ((size_t)tt0 * H + h) * D;
         if constexpr (!FUSE) {
+            const __amdgpu_buffer_rsrc_t ors = rows_rsrc(yb, rs * sizeof(OutT), D * sizeof(OutT), nvalid);
 #pragma unroll
             for (int qt = 0; qt < L::NQT; ++qt) {
-                const int row = 16 * qt + c;
-                if (qt < nqt && row < nvalid) {
-                    OutT* dst = y + ((size_t)(tt0 + row) * H + h) * D + 32 * wave + 4 * g;
+                if (qt < nqt) {
+                    const uint32_t row = 16 * qt + c;
 #pragma unroll
-                    for (int dvt = 0; dvt < 2; ++dvt) store4<OutT>(dst + 16 * dvt, acc[dvt][qt], 1.f);
+                    for (int dvt = 0; dvt < 2; ++dvt)
+                        store4_buf<OutT>(ors, row * rs + 32 * wave + 16 * dvt + 4 * g, acc[dvt][qt]);
                 }
             }
-        } else {
-            if (ti > 0) {
-                // the previous block: every head published its sums at the
-                // top of this block
-                if (wave == 0) gather_finish<TB>(sm, ga, H, (uint32_t)ti, lane, xw);
-                __syncthreads();
-                gate_block<TB, OutT>(sm, y, xr, inv_f, ga.eps, tprev, nprev, H, h, wave, g, c);
-            }
-            stash_block<TB>(sm, acc, xr, xb, rs, nvalid, wave, g, c);
-            tprev = tt0;
+        }
+        // the state update first: its LDS reads then precede the writes
+        // below, which the compiler cannot prove disjoint from them
+        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+        if constexpr (FUSE) {
+            // (for the first block nprev = 0: every store is dropped)
+            gate_block<TB, OutT>(sm, rows_rsrc(ob, rs * sizeof(OutT), D * sizeof(OutT), nprev), xr,
+                                 inv_f, ga.eps, rs, wave, g, c);
+            stash_block<TB>(sm, acc, xr, rows_rsrc(xb, rs * 2u, D * 2u, nvalid), rs, wave, g, c);
+            ob = yb;
             nprev = nvalid;
             xb += (size_t)TB * rs;
         }
-
-        // ---- S += phi(K)^T phi(V) ----
-        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+        // rq holds block ti+1 (stale past the last block: staged, never read)
+        stage_q<NORM, L::NJ>(sm, rq, tid);
     }
     if constexpr (FUSE) {
         __syncthreads();
@@ -765,7 +807,8 @@ __device__ __forceinline__ void process_item(
             gather_finish<TB>(sm, ga, H, (uint32_t)ntiles, lane, w);
         }
         __syncthreads();
-        gate_block<TB, OutT>(sm, y, xr, inv_f, ga.eps, tprev, nprev, H, h, wave, g, c);
+        gate_block<TB, OutT>(sm, rows_rsrc(ob, rs * sizeof(OutT), D * sizeof(OutT), nprev), xr, inv_f,
+                             ga.eps, rs, wave, g, c);
     }
 
     if (!prefix) {
