@@ -181,6 +181,64 @@ def bench_decode(args, torch, lib, _lib, inputs):
     return res
 
 
+def bench_other_prefill(args, torch, api, inputs):
+    """The 32K-token and packed-varlen workloads through the Python binding:
+    whole-call time (HIP events on the current stream), median over repeats."""
+    res = {}
+    for name, reps in (("prefill_32k", 50), ("varlen_512k", 10)):
+        w = inputs.WORKLOADS[name]
+        if w.kind == "prefill":
+            q, k, v, x = inputs.prefill_inputs(w, device="cuda")
+            run = lambda: api.la_prefill(q, k, v, x)
+            tokens = w.T
+        else:
+            q, k, v, x, cu = inputs.varlen_inputs(w, device="cuda")
+            cu_d = cu.cuda()
+            maxlen = int((cu[1:] - cu[:-1]).max())
+            run = lambda: api.la_prefill_varlen(q, k, v, cu_d, maxlen, x)
+            tokens = w.total_T
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        times.sort()
+        med = times[len(times) // 2]
+        th = tokens * w.H
+        res[name] = {"ms_median": med, "ms_p10": times[len(times) // 10],
+                     "ms_p90": times[(9 * len(times)) // 10], "tokens_per_s": tokens / (med * 1e-3),
+                     "path_min_bytes_GBps": th * 1536 / (med * 1e-3) / 1e9,
+                     "note": "whole call incl. workspace allocation in the binding; " + w.note}
+        log("%s: %.3f ms median (p10 %.3f, p90 %.3f), %.0f tokens/s" %
+            (name, med, res[name]["ms_p10"], res[name]["ms_p90"], res[name]["tokens_per_s"]))
+        del q, k, v, x
+        torch.cuda.empty_cache()
+    return res
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (read + write bytes per second) on this GPU."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    b.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def calibrate_copy(args, torch):
     """A plain copy of a known number of bytes: under a byte counter, its
     reading per dispatch against the bytes it must move gives the counter's
@@ -260,6 +318,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 32K-token and varlen timings and the copy-bandwidth reference")
     ap.add_argument("--cpu-tokens", type=int, default=262144)
     ap.add_argument("--block", type=int, default=0, help="block size (0 = library default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -290,6 +350,17 @@ def main():
 
     pre = bench_prefill(args, torch, lib, _lib, inputs)
     dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
+    other = None
+    if not args.no_extra:
+        from linear_attention_long_amd import api
+
+        other = bench_other_prefill(args, torch, api, inputs)
+        if dec is not None:
+            cgbs = copy_bandwidth(torch)
+            log("device copy: %.0f GB/s" % cgbs)
+            for key in dec:
+                dec[key]["device_copy_GBps"] = cgbs
+                dec[key]["frac_of_copy"] = dec[key]["GBps"] / cgbs
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, inputs)
 
     th = pre["token_heads"]
@@ -344,6 +415,7 @@ def main():
                     "path_hbm_roofline_frac": path_gbs / HBM_PEAK_GBS,
                     "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS},
         "decode": dec,
+        "other_prefill": other,
     }
     print(json.dumps(line), flush=True)
 

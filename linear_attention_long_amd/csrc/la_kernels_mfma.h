@@ -641,7 +641,8 @@ __device__ __forceinline__ void process_item(
             for (int tau = wave; tau < ntau; tau += 4) {
                 const int qt = tau >= 6 ? 3 : tau >= 3 ? 2 : tau >= 1 ? 1 : 0;
                 const int kt = tau - qt * (qt + 1) / 2;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                // three independent accumulator chains (hi.hi, hi.lo, lo.hi)
+                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, a2 = a0;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const bf16x8_t ah = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, 16);
@@ -649,10 +650,11 @@ __device__ __forceinline__ void process_item(
                     // run-time column steps: no merged K reads (they conflict at KS)
                     const bf16x8_t bh = row_operand(sm.kh, KS, 16 * kt + c, 2 * k16 * s, g, k16);
                     const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 2 * k16 * s, g, k16);
-                    acc = mfma16x16x32(ah, bh, acc);
-                    acc = mfma16x16x32(ah, bl, acc);
-                    acc = mfma16x16x32(al, bh, acc);
+                    a0 = mfma16x16x32(ah, bh, a0);
+                    a1 = mfma16x16x32(ah, bl, a1);
+                    a2 = mfma16x16x32(al, bh, a2);
                 }
+                f32x4_t acc = a0 + (a1 + a2);
                 // acc[i]: query 16qt + 4g + i, key 16kt + c; keep key <= query
                 if (kt == qt) {
 #pragma unroll
