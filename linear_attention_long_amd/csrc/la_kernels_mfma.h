@@ -689,6 +689,11 @@ __device__ __forceinline__ void process_item(
             if (ti > 0 && wave == 0) gather_issue<TB>(ga, H, (uint32_t)ti, lane, xw);
         }
 
+        // Matrix-core sections run at a raised wave priority (s_setprio 1):
+        // with two workgroups per CU, the SIMD then issues the MFMA stream
+        // of one wave first and fills its gaps with the other wave's vector
+        // work (measured: main pass -4.5%).
+        __builtin_amdgcn_s_setprio(1);
         // ---- Y^T = V^T P^T (intra) + S^T Q^T (inter), this wave's 32 columns ----
         f32x4_t acc[2][L::NQT];
 #pragma unroll
@@ -750,6 +755,7 @@ __device__ __forceinline__ void process_item(
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // acc[dvt][qt][i]: query 16qt + c, feature 32*wave + 16*dvt + 4g + i
         if (NORM) {
 #pragma unroll
@@ -787,7 +793,9 @@ __device__ __forceinline__ void process_item(
         }
         // the state update first: its LDS reads then precede the writes
         // below, which the compiler cannot prove disjoint from them
+        __builtin_amdgcn_s_setprio(1);
         state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (FUSE) {
             // (for the first block nprev = 0: every store is dropped)
             gate_block<TB, OutT>(sm, rows_rsrc(ob, rs * sizeof(OutT), D * sizeof(OutT), nprev), xr,
