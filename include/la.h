@@ -203,6 +203,11 @@ typedef struct {
     int32_t chunk_tokens;     /* tokens per chunk */
     int32_t block_size;       /* resolved block size */
     int32_t fused_gate;       /* 1: the gate runs inside the main pass */
+    int32_t chunk_on_device;  /* 1 (varlen with the fused gate): the chunk
+                                 length is chosen on the device from
+                                 cu_seqlens -- the smallest multiple of 64,
+                                 at most chunk_tokens, whose chunks all fit
+                                 at once -- so chunk_tokens is an upper bound */
     int32_t n_kernels;        /* kernels launched, <= 8 */
     int32_t kernels[8];       /* la_kernel_t values, launch order */
 } la_plan_t;

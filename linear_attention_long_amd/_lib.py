@@ -62,6 +62,7 @@ class Plan(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("fused_gate", ctypes.c_int32),
+        ("chunk_on_device", ctypes.c_int32),
         ("n_kernels", ctypes.c_int32),
         ("kernels", ctypes.c_int32 * 8),
     ]

@@ -77,6 +77,9 @@ struct Plan {
     int C;             // tokens per chunk
     int64_t items;     // grid size bound in chunks
     int64_t stride;    // floats per (item, head) in the state buffer
+    bool cdev;         // varlen, fused: the chunk length is searched on the device (<= C)
+    int c_lo;          // its lower bound
+    int64_t teams;     // fused: resident (chunk, head) teams = items bound
     size_t off_chunk_off, off_buf, off_y, total;
 };
 
@@ -171,6 +174,7 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
             if (items <= teams) {
                 p.fuse_ok = true;
                 p.C = (int)C;
+                p.teams = teams;
             }
         }
     }
@@ -182,10 +186,23 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
         p.C = (int)(c < 64 ? 64 : c);
     }
     p.items = items_for(varlen, num_seqs, total_T, max_seqlen, p.C);
+    // Fused varlen batches whose sequences span chunks: C above is sized for
+    // the worst case of the lengths (every sequence ends in a short chunk);
+    // the chunk planner searches, on the device, the smallest chunk length
+    // (multiple of 64, at least kMinAutoChunk unless C is smaller) whose
+    // chunk count still fits the resident teams.
+    p.cdev = varlen && p.fuse_ok && p.chunked && !o.chunk;
+    if (p.cdev) {
+        int64_t lo = (total_T + p.teams - 1) / p.teams;
+        lo = (lo + 63) / 64 * 64;
+        if (lo < kMinAutoChunk) lo = kMinAutoChunk;
+        p.c_lo = (int)(lo < p.C ? lo : p.C);
+        p.items = p.teams;
+    }
     p.xbuf_words = p.fuse_ok ? p.items * mf::NSLOT * H * 32 : 0;
     size_t off = 0;
     p.off_chunk_off = off;
-    if (varlen) off += align256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    if (varlen) off += align256((size_t)(num_seqs + 2) * sizeof(int32_t));
     p.off_buf = off;
     if (p.chunked) off += align256((size_t)p.items * H * p.stride * sizeof(float));
     p.off_y = off;
@@ -226,7 +243,9 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         map.cu = cu;
         map.chunk_off = (int32_t*)(ws + p.off_chunk_off);
         tm.before();
-        k_plan_chunks<<<1, 256, 0, st>>>(cu, nseq, p.C, (int32_t*)(ws + p.off_chunk_off));
+        k_plan_chunks<<<1, 256, 0, st>>>(cu, nseq, p.C, (int32_t*)(ws + p.off_chunk_off),
+                                         p.cdev ? 1 : 0, p.c_lo, (int32_t)p.teams);
+        map.cdev = p.cdev ? 1 : 0;
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
     } else {
@@ -494,6 +513,7 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, i
     r.chunk_tokens = p.C;
     r.block_size = p.block;
     r.fused_gate = total_T > 0 && p.fuse_ok;
+    r.chunk_on_device = total_T > 0 && p.cdev;
     int n = 0;
     if (varlen) r.kernels[n++] = LA_KERNEL_CHUNK_TABLE;
     if ((total_T == 0 || (varlen && !p.chunked)) && has_state_out) r.kernels[n++] = LA_KERNEL_STATE_COPY;

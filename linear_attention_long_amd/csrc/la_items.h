@@ -19,6 +19,8 @@ struct ItemMap {
     int32_t T;                 // equal-length batches: tokens per sequence
     int32_t C;                 // tokens per chunk (multiple of 64)
     int32_t cps;               // equal-length batches: chunks per sequence
+    int32_t cdev;              // varlen: 1 = the chunk length is chunk_off[nseq + 1]
+                               // (chosen on the device), 0 = C
 };
 
 struct Item {
@@ -50,9 +52,10 @@ __device__ __forceinline__ bool decode_item(const ItemMap& m, int32_t item, Item
     }
     it.seq = lo;
     it.chunk = item - m.chunk_off[lo];
+    const int32_t C = m.cdev ? m.chunk_off[m.nseq + 1] : m.C;
     const int32_t s0 = m.cu[lo], s1 = m.cu[lo + 1];
-    it.t0 = (int64_t)s0 + (int64_t)it.chunk * m.C;
-    it.len = (int32_t)min((int64_t)m.C, (int64_t)s1 - it.t0);
+    it.t0 = (int64_t)s0 + (int64_t)it.chunk * C;
+    it.len = (int32_t)min((int64_t)C, (int64_t)s1 - it.t0);
     it.last = (it.chunk == m.chunk_off[lo + 1] - m.chunk_off[lo] - 1);
     return it.len > 0;
 }

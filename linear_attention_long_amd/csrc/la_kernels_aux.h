@@ -7,14 +7,42 @@
 
 namespace la {
 
-// chunk_off[s] = sum_{s' < s} ceil(len_s' / C) from device cu_seqlens, one
-// workgroup of 256 threads, no host round trip.
+// Chunk table of a packed batch: chunk_off[s] = first item of sequence s,
+// chunk_off[nseq] = number of items, with chunks of C tokens.  With
+// search != 0 the kernel first picks C on the device: the smallest multiple
+// of 64 in [c_lo, C] with sum_s ceil(L_s / C) <= max_items (a binary search;
+// the count does not increase with C, and C itself must qualify), stored in
+// chunk_off[nseq + 1].  One workgroup of 256 threads.
+__device__ __forceinline__ int32_t block_sum_256(int32_t v, int32_t* red) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    const int tid = threadIdx.x;
+    __syncthreads();  // red is free
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void k_plan_chunks(const int32_t* __restrict__ cu, int32_t nseq,
-                                                     int32_t C, int32_t* __restrict__ chunk_off) {
+                                                     int32_t C, int32_t* __restrict__ chunk_off,
+                                                     int32_t search, int32_t c_lo,
+                                                     int32_t max_items) {
     __shared__ int32_t part[257];
+    __shared__ int32_t red[4];
     const int tid = threadIdx.x;
     const int per = (nseq + 255) / 256;
     const int s0 = min(nseq, tid * per), s1 = min(nseq, s0 + per);
+    if (search) {
+        int32_t lo = max(1, c_lo / 64), hi = C / 64;  // C (= 64 * hi) qualifies
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1, cm = 64 * mid;
+            int32_t local = 0;
+            for (int s = s0; s < s1; ++s) local += (max(0, cu[s + 1] - cu[s]) + cm - 1) / cm;
+            if (block_sum_256(local, red) <= max_items) hi = mid; else lo = mid + 1;
+        }
+        C = 64 * hi;
+        if (tid == 0) chunk_off[nseq + 1] = C;
+    }
     int32_t local = 0;
     for (int s = s0; s < s1; ++s) {
         const int32_t L = max(0, cu[s + 1] - cu[s]);

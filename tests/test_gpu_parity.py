@@ -267,6 +267,31 @@ def test_fused_gate_varlen():
         assert torch.equal(S[1].cpu(), S0[1]) and torch.equal(S[6].cpu(), S0[6])
 
 
+def test_fused_gate_varlen_device_chunking():
+    """40 sequences of 50..3000 tokens, 8 heads: the fused plan's chunk length
+    is searched on the device (below the worst-case bound the host sets);
+    every output and final state against the oracle."""
+    banner("fused gate, varlen, chunk length chosen on the device")
+    rng = np.random.default_rng(190)
+    lengths = rng.integers(50, 3001, size=40).tolist()
+    cu = inputs.cu_from_lengths(lengths)
+    total, H, d = int(cu[-1]), 8, 128
+    plan = fused_plan(True, len(lengths), total, max(lengths), H)
+    assert plan.fused_gate == 1 and plan.chunk_on_device == 1, plan.kernel_names()
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (randn((total, H, d), 191 + i, s, dtype=torch.bfloat16) for i in range(3))
+    x = randn((total, H * d), 194, dtype=torch.bfloat16)
+    S0 = randn((len(lengths), H, d, d), 195, 0.05)
+    out, S, _ = api.la_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lengths),
+                                      x.to(DEV), None, S0.to(DEV))
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(q, k, v, x, None, cu_seqlens=cu.numpy(), state_in=S0, gated=True)
+    e_out, e_S = rel_err(np64(out), ref), rel_err(np64(S), Sref)
+    print("varlen device chunking (host bound %d tokens): rel err out %.3e state %.3e"
+          % (plan.chunk_tokens, e_out, e_S))
+    assert e_out <= TOL_BF16 and e_S <= TOL_BF16
+
+
 def test_unfused_gate_when_heads_exceed_fused_limit():
     banner("gate not fused: H=9 (unfused path), parity")
     T, H, d = 700, 9, 128

@@ -22,21 +22,31 @@ TOL_BF16 = 1e-2
 
 
 def chunk_tokens(varlen, num_seqs, total, max_len, H, d):
-    """Chunk length of the default plan (printed with its kernels)."""
+    """Chunk length of the default plan (printed with its kernels) and whether
+    the device chooses it (then the returned length is an upper bound)."""
     p = _lib.plan(varlen, num_seqs, total, max_len, H, d, _lib.LA_DTYPE_BF16,
                   _lib.LA_DTYPE_F32, _lib.options(gated=True))
-    print("plan: chunk %d, %d main workgroups, kernels %s"
-          % (p.chunk_tokens, p.main_workgroups, p.kernel_names()))
-    return p.chunk_tokens
+    print("plan: chunk %d%s, %d main workgroups, kernels %s"
+          % (p.chunk_tokens, " (bound; chosen on the device)" if p.chunk_on_device else "",
+             p.main_workgroups, p.kernel_names()))
+    return p.chunk_tokens, bool(p.chunk_on_device)
 
 
-def sample_tokens(starts, ends, chunk, nrand, seed):
+def sample_tokens(starts, ends, chunk, nrand, seed, every64=False):
+    """Sequence ends, tokens around each chunk start (every 64-token boundary
+    when the chunk length is chosen on the device), and seeded random ones."""
     idx = set()
     rng = np.random.default_rng(seed)
     for a, b in zip(starts, ends):
         if b <= a:
             continue
         idx.update([a, b - 1])
+        if every64:
+            for c0 in range(a, b, 64):
+                for off in (-1, 0):
+                    if a <= c0 + off < b:
+                        idx.add(c0 + off)
+            continue
         for c0 in range(a, b, chunk):
             for off in (-2, -1, 0, 1, 31, 32, 33, 63, 64):
                 t = c0 + off
@@ -53,8 +63,8 @@ def test_prefill_1m_workload_sampled():
     q, k, v, x = inputs.prefill_inputs(w, device="cuda")
     out, S, _ = api.la_prefill(q, k, v, x)
     torch.cuda.synchronize()
-    C = chunk_tokens(False, 1, w.T, w.T, w.H, w.d)
-    idx = sample_tokens([0], [w.T], C, 512, 7)
+    C, dev = chunk_tokens(False, 1, w.T, w.T, w.H, w.d)
+    idx = sample_tokens([0], [w.T], C, 512, 7, every64=dev)
     got = np64(out[0, torch.from_numpy(idx).cuda()])
     S_got = np64(S)
     del out, S
@@ -76,8 +86,8 @@ def test_varlen_512k_workload_sampled():
     lengths = (cu[1:] - cu[:-1]).tolist()
     out, S, _ = api.la_prefill_varlen(q, k, v, cu.cuda(), max(lengths), x)
     torch.cuda.synchronize()
-    C = chunk_tokens(True, len(lengths), w.total_T, max(lengths), w.H, w.d)
-    idx = sample_tokens(cu[:-1].tolist(), cu[1:].tolist(), C, 512, 11)
+    C, dev = chunk_tokens(True, len(lengths), w.total_T, max(lengths), w.H, w.d)
+    idx = sample_tokens(cu[:-1].tolist(), cu[1:].tolist(), C, 512, 11, every64=dev)
     got = np64(out[torch.from_numpy(idx).cuda()])
     S_got = np64(S)
     del out, S
