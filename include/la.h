@@ -92,7 +92,17 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               kernel it launches on hip_stream, for i < n_timing.  The
  *               kernels of a prefill call, in launch order, are listed by
  *               la_prefill_plan; la_decode_step launches decode, then [gate]
- *               when gated.                                                  */
+ *               when gated.
+ *   state_slots, state_rows
+ *               NULL (default): sequence s uses row s of state_in, z_in,
+ *               state_out, z_out (the shapes given per call).  Otherwise a
+ *               DEVICE int32 array with one entry per sequence of the call:
+ *               sequence s uses row state_slots[s] of state arrays that have
+ *               state_rows rows ([state_rows, H, d, d] and [state_rows, H, d]),
+ *               e.g. a pool of per-request states updated in place (state_out
+ *               = state_in).  Slots of one call must be distinct (not
+ *               checked); a slot outside [0, state_rows) makes that sequence
+ *               start from zero and write no state (decode: y = 0).          */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -102,6 +112,8 @@ typedef struct {
     int32_t chunk_tokens;
     void* timing_events;
     int32_t n_timing;
+    const int32_t* state_slots;
+    int32_t state_rows;
 } la_options_t;
 
 la_options_t la_default_options(void);
@@ -226,6 +238,71 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T,
                             la_dtype_t in_dtype, la_dtype_t out_dtype,
                             int32_t has_state_out, const la_options_t* opt,
                             la_plan_t* plan);
+
+/* ------------------------------------------------------------- serving --
+ * Prefill/decode co-scheduling with chunked prefill ([Deploy] section 3:
+ * chunked prefill under a token budget; section 6: prefill and decode run as
+ * separate work, on two streams).  Every request owns one row ("slot") of a
+ * state pool; a step moves each decoding request by one token and each
+ * prefilling request by one chunk of its prompt, carrying the state in the
+ * pool (the state_slots option of the calls above).                        */
+
+typedef struct {
+    int32_t remaining;  /* prompt tokens not yet prefilled; 0 = decoding */
+    int32_t slot;       /* the request's row in the state pool */
+} la_request_t;
+
+typedef struct {
+    int32_t num_decode;      /* requests decoding this step (1 token each) */
+    int32_t num_prefill;     /* requests with a prefill chunk this step */
+    int32_t prefill_tokens;  /* tokens of those chunks */
+    int32_t max_chunk;       /* longest chunk */
+} la_step_t;
+
+/* One step's work: every decoding request first (in request order), then
+ * prefill chunks in request order, each as long as its remaining prompt and
+ * the budget (max_batched_tokens minus the tokens already taken) allow; the
+ * step stops at the first request the budget cannot serve.  order[i] is the
+ * request of packed sequence i (decoders first, then chunks, i < num_decode +
+ * num_prefill) and chunk[i] its tokens this step (1 for decoders).  order and
+ * chunk need room for R entries.  Host only.  Returns
+ * LA_ERR_INVALID_ARGUMENT for R < 0, a negative remaining count, a budget
+ * below the number of decoders, or NULL arrays (with R > 0). */
+la_status_t la_schedule_step(const la_request_t* reqs, int32_t R, int32_t max_batched_tokens,
+                             int32_t* order, int32_t* chunk, la_step_t* step);
+
+/* One serving step, its two parts on two streams (concurrently).
+ *   q, k, v     [num_decode + prefill_tokens, H, d] in_dtype, packed in the
+ *               order of la_schedule_step: rows [0, num_decode) are the
+ *               decoders' tokens, then the chunks back to back
+ *   x_gate      [rows, H*d] | NULL (required iff gated);  rms_weight [H*d] | NULL
+ *   state_pool  [state_rows, H, d, d] fp32, z_pool [state_rows, H, d] fp32
+ *               (normalised mode): updated IN PLACE
+ *   decode_slots   DEVICE int32 [num_decode]: decoders' rows in the pool
+ *   prefill_cu     DEVICE int32 [num_prefill + 1]: chunk offsets, relative to
+ *                  row num_decode (0 = c_0 <= ... = prefill_tokens)
+ *   prefill_slots  DEVICE int32 [num_prefill]: the chunks' requests' rows
+ *   max_chunk      host bound of the chunk lengths
+ *   out         [rows, H*d] out_dtype
+ *   workspace   la_serve_step_workspace_bytes(...) bytes, 256-byte aligned
+ * The decode step runs on decode_stream and the chunks (la_prefill_varlen
+ * with slots) on prefill_stream; the call returns once both are enqueued,
+ * so the caller synchronises both streams.  The slots of one step must be
+ * distinct (not checked).  Errors as the two calls. */
+la_status_t la_serve_step(const void* q, const void* k, const void* v,
+                          const void* x_gate, const float* rms_weight,
+                          float* state_pool, float* z_pool, int32_t state_rows,
+                          const int32_t* decode_slots, int32_t num_decode,
+                          const int32_t* prefill_cu, const int32_t* prefill_slots,
+                          int32_t num_prefill, int32_t prefill_tokens, int32_t max_chunk,
+                          void* out, int32_t H, int32_t d,
+                          la_dtype_t in_dtype, la_dtype_t out_dtype,
+                          const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                          void* decode_stream, void* prefill_stream);
+size_t la_serve_step_workspace_bytes(int32_t num_decode, int32_t num_prefill,
+                                     int32_t prefill_tokens, int32_t max_chunk,
+                                     int32_t H, int32_t d, la_dtype_t in_dtype,
+                                     la_dtype_t out_dtype, const la_options_t* opt);
 
 /* Static, NUL-terminated description of a status code. */
 const char* la_status_string(la_status_t status);

@@ -26,6 +26,9 @@ EXPORTS = (
     "la_prefill_varlen_workspace_bytes",
     "la_decode_workspace_bytes",
     "la_prefill_plan",
+    "la_schedule_step",
+    "la_serve_step",
+    "la_serve_step_workspace_bytes",
     "la_status_string",
 )
 
@@ -40,6 +43,8 @@ class Options(ctypes.Structure):
         ("chunk_tokens", ctypes.c_int32),
         ("timing_events", ctypes.c_void_p),
         ("n_timing", ctypes.c_int32),
+        ("state_slots", ctypes.c_void_p),
+        ("state_rows", ctypes.c_int32),
     ]
 
 
@@ -69,6 +74,19 @@ class Plan(ctypes.Structure):
 
     def kernel_names(self):
         return [KERNEL_NAMES[self.kernels[i]] for i in range(self.n_kernels)]
+
+
+class Request(ctypes.Structure):
+    _fields_ = [("remaining", ctypes.c_int32), ("slot", ctypes.c_int32)]
+
+
+class Step(ctypes.Structure):
+    _fields_ = [
+        ("num_decode", ctypes.c_int32),
+        ("num_prefill", ctypes.c_int32),
+        ("prefill_tokens", ctypes.c_int32),
+        ("max_chunk", ctypes.c_int32),
+    ]
 
 
 class LAError(RuntimeError):
@@ -123,6 +141,17 @@ def load() -> ctypes.CDLL:
         lib.la_prefill_plan.restype = ctypes.c_int
         lib.la_prefill_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                                         ctypes.c_int, _i32, _optp, ctypes.POINTER(Plan)]
+        lib.la_schedule_step.restype = ctypes.c_int
+        lib.la_schedule_step.argtypes = [ctypes.POINTER(Request), _i32, _i32,
+                                         ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                         ctypes.POINTER(Step)]
+        lib.la_serve_step.restype = ctypes.c_int
+        lib.la_serve_step.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _i32, _vp, _i32, _vp, _vp,
+                                      _i32, _i32, _i32, _vp, _i32, _i32, ctypes.c_int,
+                                      ctypes.c_int, _optp, _vp, _sz, _vp, _vp]
+        lib.la_serve_step_workspace_bytes.restype = _sz
+        lib.la_serve_step_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                      ctypes.c_int, ctypes.c_int, _optp]
         _lib = lib
         return lib
 

@@ -89,12 +89,29 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
     return out, state_out, z_out
 
 
+def _slots(opt, state_slots, pool):
+    """Slot table (int32 on the GPU) over a state pool [rows, H, d, d]."""
+    if state_slots is None:
+        return None
+    if state_slots.dtype != torch.int32:
+        raise TypeError("state_slots must be int32")
+    if pool is None:
+        raise ValueError("state_slots needs the state pool")
+    opt.state_slots = _ptr(state_slots).value
+    opt.state_rows = int(pool.shape[0])
+    return state_slots
+
+
 def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=None, z_in=None,
                       *, normalized=False, block_size=0, norm_group=0, rms_eps=1e-6,
-                      chunk_tokens=0, out_dtype=torch.float32, return_state=True, stream=None):
+                      chunk_tokens=0, out_dtype=torch.float32, return_state=True,
+                      state_slots=None, out=None, stream=None):
     """Prefill of a packed batch.  q, k, v: [total_T, H, d]; cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
-    Returns (out [total_T, H*d], state_out [num_seqs, H, d, d], z_out)."""
+    Returns (out [total_T, H*d], state_out [num_seqs, H, d, d], z_out).
+    With ``state_slots`` (int32 [num_seqs] on the GPU), state_in / z_in are
+    pools of per-request states indexed by slot and are updated in place;
+    they are returned as the states."""
     lib = _lib.load()
     total_T, H, d = q.shape
     num_seqs = cu_seqlens.numel() - 1
@@ -102,13 +119,18 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
         raise TypeError("cu_seqlens must be int32")
     gated = x is not None
     opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens)
+    _slots(opt, state_slots, state_in)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
-    out = torch.empty((total_T, H * d), dtype=out_dtype, device=dev)
-    state_out = (torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=dev)
-                 if return_state else None)
-    z_out = (torch.empty((num_seqs, H, d), dtype=torch.float32, device=dev)
-             if (return_state and normalized) else None)
+    if out is None:
+        out = torch.empty((total_T, H * d), dtype=out_dtype, device=dev)
+    if state_slots is not None:
+        state_out, z_out = state_in, z_in
+    else:
+        state_out = (torch.empty((num_seqs, H, d, d), dtype=torch.float32, device=dev)
+                     if return_state else None)
+        z_out = (torch.empty((num_seqs, H, d), dtype=torch.float32, device=dev)
+                 if (return_state and normalized) else None)
     nbytes = lib.la_prefill_varlen_workspace_bytes(total_T, num_seqs, int(max_seqlen), H, d,
                                                    in_dt, out_dt, ctypes.byref(opt))
     ws = _workspace(nbytes, dev)
@@ -122,14 +144,18 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
 
 
 def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, norm_group=0,
-                   rms_eps=1e-6, out_dtype=torch.float32, out=None, workspace=None, stream=None):
+                   rms_eps=1e-6, out_dtype=torch.float32, out=None, workspace=None,
+                   state_slots=None, stream=None):
     """One decode token per sequence.  q, k, v: [N, H, d]; state [N, H, d, d]
-    float32 and z [N, H, d] (normalised mode) are updated in place.
-    Returns out [N, H*d].  ``out``/``workspace`` may be passed to reuse buffers."""
+    float32 and z [N, H, d] (normalised mode) are updated in place (with
+    ``state_slots``, int32 [N] on the GPU: pools [rows, H, d, d] / [rows, H, d]
+    indexed by slot).  Returns out [N, H*d].  ``out``/``workspace`` may be
+    passed to reuse buffers."""
     lib = _lib.load()
     N, H, d = q.shape
     gated = x is not None
     opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0)
+    _slots(opt, state_slots, state)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     if out is None:
         out = torch.empty((N, H * d), dtype=out_dtype, device=q.device)
@@ -144,7 +170,67 @@ def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, 
     return out
 
 
+def la_schedule_step(remaining, max_batched_tokens=32768):
+    """Host-side step choice (la_schedule_step) for requests with the given
+    remaining prompt tokens (0 = decoding).  Returns (order, chunk, step):
+    packed sequence i of the step is request order[i] with chunk[i] tokens;
+    step has num_decode, num_prefill, prefill_tokens, max_chunk."""
+    lib = _lib.load()
+    R = len(remaining)
+    reqs = (_lib.Request * max(R, 1))()
+    for i, r in enumerate(remaining):
+        reqs[i].remaining = int(r)
+        reqs[i].slot = i
+    order = (ctypes.c_int32 * max(R, 1))()
+    chunk = (ctypes.c_int32 * max(R, 1))()
+    step = _lib.Step()
+    _lib.check(lib.la_schedule_step(reqs, R, int(max_batched_tokens), order, chunk,
+                                    ctypes.byref(step)), "la_schedule_step")
+    n = step.num_decode + step.num_prefill
+    return list(order)[:n], list(chunk)[:n], step
+
+
+def la_serve_step(q, k, v, state_pool, decode_slots, prefill_cu, prefill_slots, max_chunk,
+                  x=None, w=None, z_pool=None, *, normalized=False, norm_group=0, rms_eps=1e-6,
+                  out_dtype=torch.float32, out=None, decode_stream=None, prefill_stream=None):
+    """One serving step (la_serve_step): rows [0, len(decode_slots)) of the
+    packed q, k, v (and x) are decode tokens, the rest prefill chunks at
+    prefill_cu (int32 on the GPU, relative offsets); decode_slots and
+    prefill_slots (int32 on the GPU) index the state pool, updated in place.
+    The two parts are enqueued on decode_stream and prefill_stream."""
+    lib = _lib.load()
+    rows, H, d = q.shape
+    nd = decode_slots.numel() if decode_slots is not None else 0
+    npf = prefill_slots.numel() if prefill_slots is not None else 0
+    ptok = rows - nd
+    opt = _lib.options(0, normalized, x is not None, norm_group, rms_eps, 0)
+    in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
+    if out is None:
+        out = torch.empty((rows, H * d), dtype=out_dtype, device=q.device)
+    nbytes = lib.la_serve_step_workspace_bytes(nd, npf, ptok, int(max_chunk), H, d, in_dt, out_dt,
+                                               ctypes.byref(opt))
+    ws = _workspace(nbytes, q.device)
+    st = lib.la_serve_step(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(state_pool),
+                           _ptr(z_pool), int(state_pool.shape[0]),
+                           _ptr(decode_slots) if nd else None, nd,
+                           _ptr(prefill_cu) if npf else None, _ptr(prefill_slots) if npf else None,
+                           npf, ptok, int(max_chunk), _ptr(out), H, d, in_dt, out_dt,
+                           ctypes.byref(opt), _ptr(ws), 0 if ws is None else ws.numel(),
+                           _stream(decode_stream), _stream(prefill_stream))
+    _lib.check(st, "la_serve_step")
+    # the buffers made here are used on the two streams: keep the caching
+    # allocator from reusing them before that work is done
+    for t in (out, ws):
+        if t is not None:
+            for sm in (decode_stream, prefill_stream):
+                if sm is not None:
+                    t.record_stream(sm)
+    return out
+
+
 # the same calls under short names
 prefill = la_prefill
 prefill_varlen = la_prefill_varlen
 decode_step = la_decode_step
+schedule_step = la_schedule_step
+serve_step = la_serve_step

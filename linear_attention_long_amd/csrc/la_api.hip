@@ -48,6 +48,8 @@ struct Opts {
     int chunk;      // requested chunk tokens (0 = auto)
     hipEvent_t* events;
     int n_events;
+    const int32_t* slots;  // state row per sequence (device), or nullptr
+    int rows;              // rows of the state arrays when slots is given
 };
 
 // Records the caller's timing events around each launched kernel.
@@ -113,6 +115,9 @@ la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
     if (x.n_timing < 0 || (x.n_timing > 0 && !x.timing_events)) return LA_ERR_INVALID_ARGUMENT;
     o.events = (hipEvent_t*)x.timing_events;
     o.n_events = x.timing_events ? x.n_timing : 0;
+    o.slots = x.state_slots;
+    o.rows = x.state_slots ? x.state_rows : 0;
+    if (x.state_slots && (x.state_rows < 1 || !aligned(x.state_slots, 4))) return LA_ERR_INVALID_ARGUMENT;
     return LA_OK;
 }
 
@@ -239,6 +244,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     ItemMap map{};
     map.nseq = nseq;
     map.C = p.C;
+    map.slots = o.slots;
+    map.rows = o.rows;
     if (p.varlen) {
         map.cu = cu;
         map.chunk_off = (int32_t*)(ws + p.off_chunk_off);
@@ -252,14 +259,12 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         map.T = T;
         map.cps = (T + p.C - 1) / p.C;
     }
-    const int64_t nS = (int64_t)nseq * H * d * d, nz = (int64_t)nseq * H * d;
     if (total_T == 0 || (p.varlen && !p.chunked)) {
         // zero-length sequences keep their state; others are overwritten below
         if (state_out || z_out) {
-            const int64_t n = nS;
             tm.before();
-            k_fill_state<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
-                state_in, z_in, state_out, o.normalized ? z_out : nullptr, nS, nz);
+            k_fill_state<<<dim3((unsigned)((d * d + d + 255) / 256), (unsigned)((int64_t)nseq * H)), 256, 0, st>>>(
+                state_in, z_in, state_out, o.normalized ? z_out : nullptr, map, H, d);
             if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
             tm.after();
         }
@@ -415,8 +420,9 @@ la_status_t check_prefill_common(const void* q, const void* k, const void* v, co
         if (sp && !aligned(sp, 16)) return LA_ERR_INVALID_ARGUMENT;
     const size_t in_bytes = (size_t)total_T * H * d * dtype_size(in_dtype);
     const size_t out_bytes = (size_t)total_T * H * d * dtype_size(out_dtype);
-    const size_t s_bytes = (size_t)nseq * H * d * d * sizeof(float);
-    const size_t z_bytes = (size_t)nseq * H * d * sizeof(float);
+    const int64_t srows = o.slots ? o.rows : nseq;  // rows of the state arrays
+    const size_t s_bytes = (size_t)srows * H * d * d * sizeof(float);
+    const size_t z_bytes = (size_t)srows * H * d * sizeof(float);
     const void* ins[4] = {q, k, v, o.gated ? x_gate : nullptr};
     for (const void* ip : ins)
         if (overlap(out, out_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
@@ -451,6 +457,8 @@ la_options_t la_default_options(void) {
     o.chunk_tokens = 0;
     o.timing_events = nullptr;
     o.n_timing = 0;
+    o.state_slots = nullptr;
+    o.state_rows = 0;
     return o;
 }
 
@@ -559,13 +567,16 @@ la_status_t la_prefill(const void* q, const void* k, const void* v, const void* 
                           (hipStream_t)hip_stream);
 }
 
-la_status_t la_prefill_varlen(const void* q, const void* k, const void* v, const void* x_gate,
-                              const float* rms_weight, const int32_t* cu_seqlens, int32_t num_seqs,
-                              int32_t total_T, int32_t max_seqlen, const float* state_in,
-                              const float* z_in, void* out, float* state_out, float* z_out,
-                              int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
-                              const la_options_t* opt, void* workspace, size_t workspace_bytes,
-                              void* hip_stream) {
+// Validation, then (launch) the kernels: with launch = false a call is only
+// checked, so that a serving step can check both of its parts first.
+static la_status_t prefill_varlen_impl(bool launch, const void* q, const void* k, const void* v,
+                                       const void* x_gate, const float* rms_weight,
+                                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t total_T,
+                                       int32_t max_seqlen, const float* state_in, const float* z_in,
+                                       void* out, float* state_out, float* z_out, int32_t H, int32_t d,
+                                       la_dtype_t in_dtype, la_dtype_t out_dtype,
+                                       const la_options_t* opt, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream) {
     la_status_t s = check_shape(H, d, in_dtype, out_dtype);
     if (s != LA_OK) return s;
     if (!cu_seqlens || !aligned(cu_seqlens, 4) || num_seqs < 1 || total_T < 0 || max_seqlen < 0 ||
@@ -579,17 +590,30 @@ la_status_t la_prefill_varlen(const void* q, const void* k, const void* v, const
     if (s != LA_OK) return s;
     const Plan p = make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o);
     s = check_workspace(p, workspace, workspace_bytes);
-    if (s != LA_OK) return s;
+    if (s != LA_OK || !launch) return s;
     return launch_prefill(p, o, in_dtype, out_dtype, q, k, v, x_gate, rms_weight, cu_seqlens,
                           num_seqs, 0, total_T, state_in, z_in, out, state_out, z_out, H, d,
                           (char*)workspace, (hipStream_t)hip_stream);
 }
 
-la_status_t la_decode_step(const void* q, const void* k, const void* v, const void* x_gate,
-                           const float* rms_weight, float* state, float* z, void* out, int32_t N,
-                           int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
-                           const la_options_t* opt, void* workspace, size_t workspace_bytes,
-                           void* hip_stream) {
+la_status_t la_prefill_varlen(const void* q, const void* k, const void* v, const void* x_gate,
+                              const float* rms_weight, const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t total_T, int32_t max_seqlen, const float* state_in,
+                              const float* z_in, void* out, float* state_out, float* z_out,
+                              int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                              const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+    return prefill_varlen_impl(true, q, k, v, x_gate, rms_weight, cu_seqlens, num_seqs, total_T,
+                               max_seqlen, state_in, z_in, out, state_out, z_out, H, d, in_dtype,
+                               out_dtype, opt, workspace, workspace_bytes, hip_stream);
+}
+
+static la_status_t decode_step_impl(bool launch, const void* q, const void* k, const void* v,
+                                    const void* x_gate, const float* rms_weight, float* state,
+                                    float* z, void* out, int32_t N, int32_t H, int32_t d,
+                                    la_dtype_t in_dtype, la_dtype_t out_dtype,
+                                    const la_options_t* opt, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
     la_status_t s = check_shape(H, d, in_dtype, out_dtype);
     if (s != LA_OK) return s;
     if (N < 0) return LA_ERR_INVALID_ARGUMENT;
@@ -605,28 +629,29 @@ la_status_t la_decode_step(const void* q, const void* k, const void* v, const vo
     if (rms_weight && !aligned(rms_weight, 16)) return LA_ERR_INVALID_ARGUMENT;
     const size_t in_bytes = (size_t)N * H * d * dtype_size(in_dtype);
     const size_t out_bytes = (size_t)N * H * d * dtype_size(out_dtype);
-    const size_t s_bytes = (size_t)N * H * d * d * sizeof(float);
+    const int64_t srows = o.slots ? o.rows : N;  // rows of state and z
+    const size_t s_bytes = (size_t)srows * H * d * d * sizeof(float);
     const void* ins[4] = {q, k, v, o.gated ? x_gate : nullptr};
     for (const void* ip : ins) {
         if (overlap(out, out_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
         if (overlap(state, s_bytes, ip, in_bytes)) return LA_ERR_INVALID_ARGUMENT;
     }
     if (overlap(out, out_bytes, state, s_bytes)) return LA_ERR_INVALID_ARGUMENT;
-    if (z && (overlap(out, out_bytes, z, (size_t)N * H * d * 4) || overlap(state, s_bytes, z, (size_t)N * H * d * 4)))
+    if (z && (overlap(out, out_bytes, z, (size_t)srows * H * d * 4) || overlap(state, s_bytes, z, (size_t)srows * H * d * 4)))
         return LA_ERR_INVALID_ARGUMENT;
     const size_t need = (o.gated && out_dtype != LA_DTYPE_F32) ? align256((size_t)N * H * d * sizeof(float)) : 0;
     if (need) {
         if (!workspace || !aligned(workspace, 256)) return LA_ERR_INVALID_ARGUMENT;
         if (workspace_bytes < need) return LA_ERR_WORKSPACE_TOO_SMALL;
     }
-    if (N == 0) return LA_OK;
+    if (N == 0 || !launch) return LA_OK;
     hipStream_t st = (hipStream_t)hip_stream;
     Timer tm(o, st);
     void* ydst = o.gated ? (need ? workspace : out) : out;
     const bool yf32 = o.gated || out_dtype == LA_DTYPE_F32;
     const unsigned grid = (unsigned)((int64_t)N * H);
 #define LA_DEC(DD, IT, OT, NN) \
-    k_decode<DD, IT, OT, NN><<<grid, 256, 0, st>>>((const IT*)q, (const IT*)k, (const IT*)v, state, z, (OT*)ydst)
+    k_decode<DD, IT, OT, NN><<<grid, 256, 0, st>>>((const IT*)q, (const IT*)k, (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H)
 #define LA_DEC_OUT(DD, IT)                                                                  \
     do {                                                                                    \
         if (yf32) { if (o.normalized) LA_DEC(DD, IT, float, true); else LA_DEC(DD, IT, float, false); } \
@@ -660,6 +685,147 @@ la_status_t la_decode_step(const void* q, const void* k, const void* v, const vo
 #undef LA_GATE
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
+    }
+    return LA_OK;
+}
+
+la_status_t la_decode_step(const void* q, const void* k, const void* v, const void* x_gate,
+                           const float* rms_weight, float* state, float* z, void* out, int32_t N,
+                           int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                           const la_options_t* opt, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    return decode_step_impl(true, q, k, v, x_gate, rms_weight, state, z, out, N, H, d, in_dtype,
+                            out_dtype, opt, workspace, workspace_bytes, hip_stream);
+}
+
+// ------------------------------------------------------------- serving --
+
+la_status_t la_schedule_step(const la_request_t* reqs, int32_t R, int32_t max_batched_tokens,
+                             int32_t* order, int32_t* chunk, la_step_t* step) {
+    if (R < 0 || !step || (R > 0 && (!reqs || !order || !chunk))) return LA_ERR_INVALID_ARGUMENT;
+    int32_t nd = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        if (reqs[r].remaining < 0) return LA_ERR_INVALID_ARGUMENT;
+        if (reqs[r].remaining == 0) ++nd;
+    }
+    if (max_batched_tokens < nd) return LA_ERR_INVALID_ARGUMENT;
+    la_step_t st{};
+    int32_t n = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        if (reqs[r].remaining == 0) {
+            order[n] = r;
+            chunk[n] = 1;
+            ++n;
+        }
+    }
+    st.num_decode = n;
+    int64_t budget = (int64_t)max_batched_tokens - n;
+    for (int32_t r = 0; r < R && budget > 0; ++r) {
+        if (reqs[r].remaining == 0) continue;
+        const int32_t c = (int32_t)(reqs[r].remaining < budget ? reqs[r].remaining : budget);
+        order[n] = r;
+        chunk[n] = c;
+        ++n;
+        ++st.num_prefill;
+        st.prefill_tokens += c;
+        if (c > st.max_chunk) st.max_chunk = c;
+        budget -= c;
+    }
+    *step = st;
+    return LA_OK;
+}
+
+namespace {
+
+// Workspace split of a serving step: [decode part | prefill part], each
+// 256-byte aligned.
+struct ServeWs {
+    size_t dec, pre, total;
+};
+
+ServeWs serve_ws(int32_t num_decode, int32_t num_prefill, int32_t prefill_tokens,
+                 int32_t max_chunk, int32_t H, int32_t d, la_dtype_t in_dtype,
+                 la_dtype_t out_dtype, const la_options_t* opt) {
+    ServeWs w{0, 0, (size_t)-1};
+    const size_t a = num_decode > 0 ? la_decode_workspace_bytes(num_decode, H, d, out_dtype, opt) : 0;
+    const size_t b = num_prefill > 0
+                         ? la_prefill_varlen_workspace_bytes(prefill_tokens, num_prefill, max_chunk, H,
+                                                             d, in_dtype, out_dtype, opt)
+                         : 0;
+    if (a == (size_t)-1 || b == (size_t)-1) return w;
+    w.dec = align256(a);
+    w.pre = align256(b);
+    w.total = w.dec + w.pre;
+    return w;
+}
+
+}  // namespace
+
+size_t la_serve_step_workspace_bytes(int32_t num_decode, int32_t num_prefill,
+                                     int32_t prefill_tokens, int32_t max_chunk, int32_t H,
+                                     int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                                     const la_options_t* opt) {
+    if (num_decode < 0 || num_prefill < 0 || prefill_tokens < 0) return (size_t)-1;
+    return serve_ws(num_decode, num_prefill, prefill_tokens, max_chunk, H, d, in_dtype, out_dtype,
+                    opt).total;
+}
+
+la_status_t la_serve_step(const void* q, const void* k, const void* v, const void* x_gate,
+                          const float* rms_weight, float* state_pool, float* z_pool,
+                          int32_t state_rows, const int32_t* decode_slots, int32_t num_decode,
+                          const int32_t* prefill_cu, const int32_t* prefill_slots,
+                          int32_t num_prefill, int32_t prefill_tokens, int32_t max_chunk,
+                          void* out, int32_t H, int32_t d, la_dtype_t in_dtype,
+                          la_dtype_t out_dtype, const la_options_t* opt, void* workspace,
+                          size_t workspace_bytes, void* decode_stream, void* prefill_stream) {
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
+    if (num_decode < 0 || num_prefill < 0 || prefill_tokens < 0 || state_rows < 1 || !state_pool)
+        return LA_ERR_INVALID_ARGUMENT;
+    if ((num_decode > 0 && !decode_slots) || (num_prefill > 0 && (!prefill_slots || !prefill_cu)))
+        return LA_ERR_INVALID_ARGUMENT;
+    if (num_prefill == 0 && prefill_tokens != 0) return LA_ERR_INVALID_ARGUMENT;
+    if (num_prefill > 0 && (max_chunk < 1 || max_chunk > prefill_tokens)) return LA_ERR_INVALID_ARGUMENT;
+    const la_options_t base = opt ? *opt : la_default_options();
+    if (base.state_slots) return LA_ERR_INVALID_ARGUMENT;  // the slots are arguments here
+    const ServeWs w = serve_ws(num_decode, num_prefill, prefill_tokens, max_chunk, H, d, in_dtype,
+                               out_dtype, &base);
+    if (w.total == (size_t)-1) return LA_ERR_INVALID_ARGUMENT;
+    if (w.total) {
+        if (!workspace || !aligned(workspace, 256)) return LA_ERR_INVALID_ARGUMENT;
+        if (workspace_bytes < w.total) return LA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    // both parts are checked before either is enqueued: a rejected step has no side effects
+    const size_t isz = dtype_size(in_dtype), osz = dtype_size(out_dtype);
+    const size_t row_in = (size_t)H * d * isz, row_out = (size_t)H * d * osz;
+    la_options_t od = base, op = base;
+    od.state_slots = decode_slots;
+    od.state_rows = state_rows;
+    op.state_slots = prefill_slots;
+    op.state_rows = state_rows;
+    od.timing_events = op.timing_events = nullptr;
+    od.n_timing = op.n_timing = 0;
+    char* ws = (char*)workspace;
+    const char* qb = (const char*)q + (size_t)num_decode * row_in;
+    const char* kb = (const char*)k + (size_t)num_decode * row_in;
+    const char* vb = (const char*)v + (size_t)num_decode * row_in;
+    const char* xb = x_gate ? (const char*)x_gate + (size_t)num_decode * row_in : nullptr;
+    char* ob = (char*)out + (size_t)num_decode * row_out;
+    for (int pass = 0; pass < 2; ++pass) {
+        const bool launch = pass == 1;
+        if (num_decode > 0) {
+            s = decode_step_impl(launch, q, k, v, x_gate, rms_weight, state_pool, z_pool, out,
+                                 num_decode, H, d, in_dtype, out_dtype, &od, w.dec ? ws : nullptr,
+                                 w.dec, decode_stream);
+            if (s != LA_OK) return s;
+        }
+        if (num_prefill > 0) {
+            s = prefill_varlen_impl(launch, qb, kb, vb, xb, rms_weight, prefill_cu, num_prefill,
+                                    prefill_tokens, max_chunk, state_pool, z_pool, ob, state_pool,
+                                    z_pool, H, d, in_dtype, out_dtype, &op, w.pre ? ws + w.dec : nullptr,
+                                    w.pre, prefill_stream);
+            if (s != LA_OK) return s;
+        }
     }
     return LA_OK;
 }

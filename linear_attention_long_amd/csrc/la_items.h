@@ -21,7 +21,18 @@ struct ItemMap {
     int32_t cps;               // equal-length batches: chunks per sequence
     int32_t cdev;              // varlen: 1 = the chunk length is chunk_off[nseq + 1]
                                // (chosen on the device), 0 = C
+    const int32_t* slots;      // device [nseq] state rows, or nullptr (row = sequence)
+    int32_t rows;              // rows of the state arrays when slots is given
 };
+
+// Row of sequence s in the state arrays: s itself, or slots[s] when a slot
+// table is given; -1 for a slot outside [0, rows) (that sequence then starts
+// from a zero state and writes none).
+__device__ __forceinline__ int32_t state_row(const ItemMap& m, int32_t s) {
+    if (!m.slots) return s;
+    const int32_t r = m.slots[s];
+    return (r >= 0 && r < m.rows) ? r : -1;
+}
 
 struct Item {
     int32_t seq;
@@ -29,6 +40,7 @@ struct Item {
     int64_t t0;      // first global token of the chunk
     int32_t len;     // tokens in the chunk (>= 1)
     bool last;       // last chunk of its sequence
+    int32_t row;     // state row of the sequence (state_row), -1 for none
 };
 
 // Returns false for items past the end (the grid is sized by an upper bound).
@@ -41,6 +53,7 @@ __device__ __forceinline__ bool decode_item(const ItemMap& m, int32_t item, Item
         it.t0 = (int64_t)it.seq * m.T + start;
         it.len = min(m.C, m.T - start);
         it.last = (it.chunk == m.cps - 1);
+        it.row = state_row(m, it.seq);
         return it.len > 0;
     }
     if (item >= m.chunk_off[m.nseq]) return false;
@@ -57,6 +70,7 @@ __device__ __forceinline__ bool decode_item(const ItemMap& m, int32_t item, Item
     it.t0 = (int64_t)s0 + (int64_t)it.chunk * C;
     it.len = (int32_t)min((int64_t)C, (int64_t)s1 - it.t0);
     it.last = (it.chunk == m.chunk_off[lo + 1] - m.chunk_off[lo] - 1);
+    it.row = state_row(m, it.seq);
     return it.len > 0;
 }
 

@@ -81,20 +81,24 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
     const int h = blockIdx.y, s = blockIdx.z;
     int32_t first, count;
     seq_items(map, s, first, count);
+    const int32_t row = state_row(map, s);
     const int DD = D * D;
-    float acc;
-    if (e < DD) acc = state_in ? state_in[((size_t)s * H + h) * DD + e] : 0.f;
-    else acc = z_in ? z_in[((size_t)s * H + h) * D + (e - DD)] : 0.f;
+    float acc = 0.f;
+    if (row >= 0) {
+        if (e < DD) acc = state_in ? state_in[((size_t)row * H + h) * DD + e] : 0.f;
+        else acc = z_in ? z_in[((size_t)row * H + h) * D + (e - DD)] : 0.f;
+    }
     for (int32_t i = 0; i < count; ++i) {
         float* p = buf + ((size_t)(first + i) * H + h) * stride + e;
         const float dlt = *p;
         *p = acc;
         acc += dlt;
     }
+    if (row < 0) return;
     if (e < DD) {
-        if (state_out) state_out[((size_t)s * H + h) * DD + e] = acc;
+        if (state_out) state_out[((size_t)row * H + h) * DD + e] = acc;
     } else if (z_out) {
-        z_out[((size_t)s * H + h) * D + (e - DD)] = acc;
+        z_out[((size_t)row * H + h) * D + (e - DD)] = acc;
     }
 }
 
@@ -105,13 +109,25 @@ __global__ __launch_bounds__(256) void k_zero_u64(uint64_t* __restrict__ p, int6
     if (i < n) p[i] = 0ull;
 }
 
-// state_out <- state_in (or zeros), z_out likewise: the zero-length case.
+// For every (sequence, head) = blockIdx.y: state_out row <- state_in row (or
+// zeros), z likewise -- the state of sequences the main pass does not write
+// (no tokens).  Rows follow the map's slot table; an in-place array (the same
+// pointer in and out) is left as it is.
 __global__ __launch_bounds__(256) void k_fill_state(const float* state_in, const float* z_in,
-                                                    float* state_out, float* z_out, int64_t nS,
-                                                    int64_t nz) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (state_out && i < nS) state_out[i] = state_in ? state_in[i] : 0.f;
-    if (z_out && i < nz) z_out[i] = z_in ? z_in[i] : 0.f;
+                                                    float* state_out, float* z_out, ItemMap map,
+                                                    int H, int D) {
+    const int s = blockIdx.y / H, h = blockIdx.y - (blockIdx.y / H) * H;
+    const int32_t row = state_row(map, s);
+    if (row < 0) return;
+    const int DD = D * D;
+    const size_t sb = ((size_t)row * H + h) * DD, zb = ((size_t)row * H + h) * D;
+    for (int e = blockIdx.x * 256 + threadIdx.x; e < DD + D; e += gridDim.x * 256) {
+        if (e < DD) {
+            if (state_out && state_out != state_in) state_out[sb + e] = state_in ? state_in[sb + e] : 0.f;
+        } else if (z_out && z_out != z_in) {
+            z_out[zb + e - DD] = z_in ? z_in[zb + e - DD] : 0.f;
+        }
+    }
 }
 
 // Output gate (page "MiniMax-Text-01 405B MoE模型架构与训练策略解析" section 2.1):
@@ -208,10 +224,15 @@ __global__ __launch_bounds__(256) void k_gate4(const float* y, const XT* __restr
 // and z, and reads its output from them).  One workgroup per (sequence,
 // head) streams the d x d state once: S += phi(k) phi(v)^T in place, then
 // y = phi(q)^T S (read after the update), optionally / phi(q).z.
+// With a slot table (slots != nullptr) the state of sequence n is row
+// slots[n] of S and z (rows of them); a slot outside [0, rows) gives y = 0
+// and touches no state.
 template <int D, typename InT, typename OutT, bool NORM>
 __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const InT* __restrict__ k,
                                                 const InT* __restrict__ v, float* __restrict__ S,
-                                                float* __restrict__ z, OutT* __restrict__ y) {
+                                                float* __restrict__ z, OutT* __restrict__ y,
+                                                const int32_t* __restrict__ slots, int32_t rows,
+                                                int H) {
     constexpr int CQ = D / 4;      // threads per state row (float4 each)
     constexpr int RG = 256 / CQ;   // row groups
     constexpr int M = D / RG;      // rows per thread
@@ -219,8 +240,18 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
     __shared__ float4 part[RG][CQ];
     __shared__ float dpart[4];
     const int tid = threadIdx.x;
-    const size_t pair = blockIdx.x;  // sequence * H + head
+    const size_t pair = blockIdx.x;  // sequence * H + head (token rows)
     const size_t vb = pair * D;
+    size_t spair = pair;             // row * H + head (state rows)
+    if (slots) {
+        const int n = (int)(pair / H), h = (int)(pair - (size_t)n * H);
+        const int32_t r = slots[n];
+        if (r < 0 || r >= rows) {
+            if (tid < D) store_from_f32<OutT>(y + vb + tid, 0.f);
+            return;
+        }
+        spair = (size_t)r * H + h;
+    }
     if (tid < D) {
         fq[tid] = silu(load_as_f32<InT>(q + vb + tid));
         fk[tid] = silu(load_as_f32<InT>(k + vb + tid));
@@ -229,13 +260,13 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
     __syncthreads();
     float den_part = 0.f;
     if (NORM && tid < D) {
-        const float zn = z[vb + tid] + fk[tid];
-        z[vb + tid] = zn;
+        const float zn = z[spair * D + tid] + fk[tid];
+        z[spair * D + tid] = zn;
         den_part = fq[tid] * zn;
     }
     const int cq = tid % CQ, rg = tid / CQ;
     const float4 v4 = make_float4(fv[4 * cq], fv[4 * cq + 1], fv[4 * cq + 2], fv[4 * cq + 3]);
-    float4* S4 = (float4*)(S + pair * D * D);
+    float4* S4 = (float4*)(S + spair * D * D);
     float4 s[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) s[m] = S4[(rg + RG * m) * CQ + cq];

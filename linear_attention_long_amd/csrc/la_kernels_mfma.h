@@ -571,8 +571,8 @@ __device__ __forceinline__ void process_item(
         s0 = prefix + ((size_t)item * H + h) * prefix_stride;
         z0 = s0 + D * D;
     } else {
-        if (state_in) s0 = state_in + ((size_t)it.seq * H + h) * D * D;
-        if (z_in) z0 = z_in + ((size_t)it.seq * H + h) * D;
+        if (state_in && it.row >= 0) s0 = state_in + ((size_t)it.row * H + h) * D * D;
+        if (z_in && it.row >= 0) z0 = z_in + ((size_t)it.row * H + h) * D;
     }
     f32x4_t S[8][2];
 #pragma unroll
@@ -821,9 +821,9 @@ __device__ __forceinline__ void process_item(
                              ga.eps, rs, wave, g, c);
     }
 
-    if (!prefix) {
+    if (!prefix && it.row >= 0) {
         if (state_out) {
-            float* dst = state_out + ((size_t)it.seq * H + h) * D * D;
+            float* dst = state_out + ((size_t)it.row * H + h) * D * D;
 #pragma unroll
             for (int dkt = 0; dkt < 8; ++dkt)
 #pragma unroll
@@ -834,7 +834,7 @@ __device__ __forceinline__ void process_item(
         }
         if (NORM && z_out) {
             __syncthreads();
-            if (tid < D) z_out[((size_t)it.seq * H + h) * D + tid] = sm.z[tid];
+            if (tid < D) z_out[((size_t)it.row * H + h) * D + tid] = sm.z[tid];
         }
     }
 }

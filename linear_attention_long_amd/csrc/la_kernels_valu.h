@@ -108,8 +108,8 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
         s0 = prefix + ((size_t)blockIdx.x * H + h) * prefix_stride;
         z0 = s0 + D * D;
     } else {
-        if (state_in) s0 = state_in + ((size_t)it.seq * H + h) * D * D;
-        if (z_in) z0 = z_in + ((size_t)it.seq * H + h) * D;
+        if (state_in && it.row >= 0) s0 = state_in + ((size_t)it.row * H + h) * D * D;
+        if (z_in && it.row >= 0) z0 = z_in + ((size_t)it.row * H + h) * D;
     }
     for (int e = tid; e < D * D; e += NT) sm.S[e] = s0 ? s0[e] : 0.f;
     if (NORM && tid < D) sm.z[tid] = z0 ? z0[tid] : 0.f;
@@ -194,13 +194,13 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
             }
         }
     }
-    if (!prefix) {
+    if (!prefix && it.row >= 0) {
         __syncthreads();
         if (state_out) {
-            float* dst = state_out + ((size_t)it.seq * H + h) * D * D;
+            float* dst = state_out + ((size_t)it.row * H + h) * D * D;
             for (int e = tid; e < D * D; e += NT) dst[e] = sm.S[e];
         }
-        if (NORM && z_out && tid < D) z_out[((size_t)it.seq * H + h) * D + tid] = sm.z[tid];
+        if (NORM && z_out && tid < D) z_out[((size_t)it.row * H + h) * D + tid] = sm.z[tid];
     }
 }
 
