@@ -222,6 +222,128 @@ def bench_other_prefill(args, torch, api, inputs):
     return res
 
 
+def bench_serving(args, torch, api, inputs, reps=50):
+    """One serving step (64 decode tokens + a 32704-token prompt chunk, all
+    continuing from pool rows) run four ways, median over repeats (HIP events):
+      two_streams   la_serve_step, decode tokens and the chunk on two streams;
+      serve_one_stream   la_serve_step with both parts on one stream (decode
+                    first; decode_ms is then the whole step);
+      one_stream    the decode call, then the prefill call, on one stream;
+      one_call      every row as one packed varlen call (the decode tokens as
+                    length-1 sequences);
+      decode_alone / chunk_alone   each part by itself.
+    decode_ms is the time from the step's start until the decode tokens'
+    outputs are written; step_ms until the whole step is done.  The pool is
+    updated in place each repeat (timing only).  Two views: "wall" starts the
+    clock when the host begins submitting the step (host submission in the
+    binding included); "device" first holds the stream with a spin kernel
+    until the host has submitted the whole step, so only device time counts."""
+    w = inputs.WORKLOADS["serve_mixed_32k"]
+    q, k, v, x, pool = inputs.serve_inputs(w, device="cuda")
+    nd, rows = w.N, w.total_T
+    dev = q.device
+    dslots = torch.arange(nd, dtype=torch.int32, device=dev)
+    pslots = torch.tensor([nd], dtype=torch.int32, device=dev)
+    pcu = torch.tensor([0, rows - nd], dtype=torch.int32, device=dev)
+    all_slots = torch.arange(nd + 1, dtype=torch.int32, device=dev)
+    all_cu = torch.tensor(list(range(nd + 1)) + [rows], dtype=torch.int32, device=dev)
+    cur = torch.cuda.current_stream()
+    s_dec, s_pre = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    # spin-kernel cycles for ~2 ms of hold, from one timed spin
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record(cur)
+    torch.cuda._sleep(1 << 20)
+    b.record(cur)
+    b.synchronize()
+    hold_cycles = int((1 << 20) * 2.0 / max(a.elapsed_time(b), 1e-3))
+    hold = [False]
+    log("serving: device view holds the stream %d spin cycles (~2 ms)" % hold_cycles)
+
+    def start():
+        if hold[0]:
+            torch.cuda._sleep(hold_cycles)
+        a = ev()
+        a.record(cur)
+        return a
+
+    def two_streams():
+        a, e_dec, e_pre = start(), ev(), ev()
+        s_dec.wait_stream(cur)
+        s_pre.wait_stream(cur)
+        api.la_serve_step(q, k, v, pool, dslots, pcu, pslots, rows - nd, x=x,
+                          decode_stream=s_dec, prefill_stream=s_pre)
+        e_dec.record(s_dec)
+        e_pre.record(s_pre)
+        cur.wait_stream(s_dec)
+        cur.wait_stream(s_pre)
+        return a, e_dec, (e_dec, e_pre)
+
+    def serve_one_stream():
+        a, e_end = start(), ev()
+        api.la_serve_step(q, k, v, pool, dslots, pcu, pslots, rows - nd, x=x,
+                          decode_stream=cur, prefill_stream=cur)
+        e_end.record(cur)
+        return a, e_end, (e_end,)
+
+    def one_stream():
+        a, e_dec, e_end = start(), ev(), ev()
+        api.la_decode_step(q[:nd], k[:nd], v[:nd], pool, x=x[:nd], state_slots=dslots)
+        e_dec.record(cur)
+        api.la_prefill_varlen(q[nd:], k[nd:], v[nd:], pcu, rows - nd, x[nd:], None, pool,
+                              state_slots=pslots)
+        e_end.record(cur)
+        return a, e_dec, (e_end,)
+
+    def one_call():
+        a, e_end = start(), ev()
+        api.la_prefill_varlen(q, k, v, all_cu, rows - nd, x, None, pool, state_slots=all_slots)
+        e_end.record(cur)
+        return a, e_end, (e_end,)
+
+    def decode_alone():
+        a, e_end = start(), ev()
+        api.la_decode_step(q[:nd], k[:nd], v[:nd], pool, x=x[:nd], state_slots=dslots)
+        e_end.record(cur)
+        return a, e_end, (e_end,)
+
+    def chunk_alone():
+        a, e_end = start(), ev()
+        api.la_prefill_varlen(q[nd:], k[nd:], v[nd:], pcu, rows - nd, x[nd:], None, pool,
+                              state_slots=pslots)
+        e_end.record(cur)
+        return a, e_end, (e_end,)
+
+    res = {"workload": w.note, "reps": reps}
+    for view in ("wall", "device"):
+        hold[0] = view == "device"
+        res[view] = {}
+        for name, fn in (("two_streams", two_streams), ("serve_one_stream", serve_one_stream),
+                         ("one_stream", one_stream),
+                         ("one_call", one_call), ("decode_alone", decode_alone),
+                         ("chunk_alone", chunk_alone)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            dts, sts = [], []
+            for _ in range(reps):
+                a, e_dec, ends = fn()
+                torch.cuda.synchronize()
+                dts.append(a.elapsed_time(e_dec))
+                sts.append(max(a.elapsed_time(e) for e in ends))
+            dts.sort()
+            sts.sort()
+            res[view][name] = {"decode_ms": dts[reps // 2], "step_ms": sts[reps // 2],
+                               "step_ms_p90": sts[(9 * reps) // 10]}
+            log("serving (%s) %s: decode tokens ready %.4f ms, step %.4f ms (median)"
+                % (view, name, dts[reps // 2], sts[reps // 2]))
+    del q, k, v, x, pool
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy rate (read + write bytes per second) on this GPU."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -350,11 +472,12 @@ def main():
 
     pre = bench_prefill(args, torch, lib, _lib, inputs)
     dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
-    other = None
+    other = serve = None
     if not args.no_extra:
         from linear_attention_long_amd import api
 
         other = bench_other_prefill(args, torch, api, inputs)
+        serve = bench_serving(args, torch, api, inputs)
         if dec is not None:
             cgbs = copy_bandwidth(torch)
             log("device copy: %.0f GB/s" % cgbs)
@@ -416,6 +539,7 @@ def main():
                     "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS},
         "decode": dec,
         "other_prefill": other,
+        "serving_step": serve,
     }
     print(json.dumps(line), flush=True)
 

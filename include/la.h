@@ -271,7 +271,10 @@ typedef struct {
 la_status_t la_schedule_step(const la_request_t* reqs, int32_t R, int32_t max_batched_tokens,
                              int32_t* order, int32_t* chunk, la_step_t* step);
 
-/* One serving step, its two parts on two streams (concurrently).
+/* One serving step ([Deploy] section 6: prefill and decode kept apart;
+ * section 3: chunked prefill under a token budget): the decode tokens and the
+ * prefill chunks, each on a stream of its own, or both on one stream (decode
+ * first) when the two streams are the same.
  *   q, k, v     [num_decode + prefill_tokens, H, d] in_dtype, packed in the
  *               order of la_schedule_step: rows [0, num_decode) are the
  *               decoders' tokens, then the chunks back to back
@@ -287,8 +290,12 @@ la_status_t la_schedule_step(const la_request_t* reqs, int32_t R, int32_t max_ba
  *   workspace   la_serve_step_workspace_bytes(...) bytes, 256-byte aligned
  * The decode step runs on decode_stream and the chunks (la_prefill_varlen
  * with slots) on prefill_stream; the call returns once both are enqueued,
- * so the caller synchronises both streams.  The slots of one step must be
- * distinct (not checked).  Errors as the two calls. */
+ * so the caller synchronises both streams.  With two distinct streams the
+ * parts run concurrently; on MI355X one stream finishes the step sooner (the
+ * chunk's workgroups fill the compute units and slow the decode kernel
+ * beside them).  The slots of one step must be distinct (not checked).
+ * Every argument of both parts is checked before either is enqueued; errors
+ * as the two calls. */
 la_status_t la_serve_step(const void* q, const void* k, const void* v,
                           const void* x_gate, const float* rms_weight,
                           float* state_pool, float* z_pool, int32_t state_rows,

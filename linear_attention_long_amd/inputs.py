@@ -33,15 +33,15 @@ DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "prefill" | "varlen" | "decode"
+    kind: str            # "prefill" | "varlen" | "decode" | "serve"
     seed: int
     H: int
     d: int
     dtype: str           # "f32" | "bf16"
     T: int = 0           # prefill: tokens per sequence
     batch: int = 1       # prefill: sequences
-    total_T: int = 0     # varlen: packed tokens
-    N: int = 0           # decode: sequences
+    total_T: int = 0     # varlen: packed tokens; serve: the step's token budget
+    N: int = 0           # decode / serve: decoding sequences
     steps: int = 0       # decode: steps
     scale: float = 1.0   # multiplier of the N(0,1) q, k, v draws
     block: int = 64
@@ -75,6 +75,14 @@ WORKLOADS = {
     "decode_64x64": Workload("decode_64x64", "decode", 1005, H=64, d=128, dtype="bf16",
                              N=64, steps=1000, state_std=0.01, gen_device="cuda",
                              note="decode, N=64 H=64 d=128, fp32 state N(0,0.01)"),
+    # one serving step under a 32768-token budget: 64 decoding sequences (one
+    # token each) and 32704 tokens of one prompt's chunk, all continuing from
+    # fp32 states in a pool
+    "serve_mixed_32k": Workload("serve_mixed_32k", "serve", 1006, H=8, d=128, dtype="bf16",
+                                N=64, total_T=32768, scale=INV_SQRT128, gated=True,
+                                state_std=0.01, gen_device="cuda",
+                                note="serving step, 64 decode tokens + a 32704-token prompt "
+                                     "chunk, H=8 d=128, gated, state pool N(0,0.01)"),
 }
 
 
@@ -145,6 +153,21 @@ def varlen_inputs(w: Workload, total_T: int | None = None, device: str | None = 
     v = normal(shape, w.seed, 2, w.scale, dt, dev)
     x = normal((total, w.H * w.d), w.seed, 3, 1.0, dt, dev) if w.gated else None
     return q, k, v, x, cu
+
+
+def serve_inputs(w: Workload, device: str | None = None):
+    """One serving step: packed q, k, v [total_T, H, d] and x [total_T, H*d]
+    (rows [0, N) are the decode tokens, the rest one prompt chunk) and the
+    fp32 state pool [N + 1, H, d, d] (row N belongs to the prompt)."""
+    dev = w.gen_device if device is None else device
+    dt = DTYPES[w.dtype]
+    shape = (w.total_T, w.H, w.d)
+    q = normal(shape, w.seed, 0, w.scale, dt, dev)
+    k = normal(shape, w.seed, 1, w.scale, dt, dev)
+    v = normal(shape, w.seed, 2, w.scale, dt, dev)
+    x = normal((w.total_T, w.H * w.d), w.seed, 3, 1.0, dt, dev) if w.gated else None
+    pool = normal((w.N + 1, w.H, w.d, w.d), w.seed, 4, w.state_std, torch.float32, dev)
+    return q, k, v, x, pool
 
 
 def decode_state(w: Workload, N: int | None = None, H: int | None = None, device=None):

@@ -4,8 +4,8 @@ Each request has a token stream (pre-activation q, k, v and, when gated, the
 gate input x; the first `prompt` tokens are its prompt) and owns one row of a
 state pool.  Each step, la_schedule_step picks the work (every decoding
 request one token, prompts in chunks under the token budget), this module
-packs those rows in that order, and la_serve_step runs the decode part and the
-prefill chunks on two streams.  Only data movement happens here (gathering
+packs those rows in that order, and la_serve_step runs the decode part and then
+the prefill chunks (on one stream, or on two).  Only data movement happens here (gathering
 the step's rows, scattering the outputs); every computation runs in the
 library's kernels.
 """
@@ -35,13 +35,23 @@ class Request:
 
 
 def run(requests, state_pool, *, z_pool=None, w=None, normalized=False, max_batched_tokens=32768,
-        out_dtype=torch.float32, decode_stream=None, prefill_stream=None, on_step=None):
+        out_dtype=torch.float32, two_streams=False, decode_stream=None, prefill_stream=None,
+        on_step=None):
     """Process every request's whole token stream.  Returns the number of
     steps; each request's outputs end up in `torch.cat(req.out)`.  on_step,
-    if given, is called with (step index, la_step_t) before each step."""
+    if given, is called with (step index, la_step_t) before each step.
+
+    By default both parts of a step go on the current stream, decode tokens
+    first: on MI355X that finishes the step sooner than two concurrent
+    streams (the prefill chunk's workgroups fill every compute unit, so the
+    decode kernel gains nothing from running beside them and is slowed by
+    them).  two_streams=True (or passing the streams) runs them on two."""
     dev = state_pool.device
-    s_dec = decode_stream or torch.cuda.Stream(device=dev)
-    s_pre = prefill_stream or torch.cuda.Stream(device=dev)
+    if two_streams or decode_stream is not None or prefill_stream is not None:
+        s_dec = decode_stream or torch.cuda.Stream(device=dev)
+        s_pre = prefill_stream or torch.cuda.Stream(device=dev)
+    else:
+        s_dec = s_pre = torch.cuda.current_stream(dev)
     gated = requests[0].x is not None if requests else False
     nsteps = 0
     while True:
@@ -61,19 +71,22 @@ def run(requests, state_pool, *, z_pool=None, w=None, normalized=False, max_batc
         cu = torch.tensor([0] + [c for _, c in spans[nd:]], dtype=torch.int64).cumsum(0)
         cu = cu.to(torch.int32).to(dev)
         cur = torch.cuda.current_stream(dev)
-        s_dec.wait_stream(cur)
-        s_pre.wait_stream(cur)
+        split = not (s_dec == cur and s_pre == cur)
+        if split:
+            s_dec.wait_stream(cur)
+            s_pre.wait_stream(cur)
         out = api.la_serve_step(q, k, v, state_pool, slots[:nd], cu, slots[nd:],
                                 max(1, st.max_chunk), x=x, w=w, z_pool=z_pool,
                                 normalized=normalized, out_dtype=out_dtype,
                                 decode_stream=s_dec, prefill_stream=s_pre)
-        cur.wait_stream(s_dec)
-        cur.wait_stream(s_pre)
-        # keep the step's inputs alive until both streams are done with them
-        for t in (q, k, v, x, slots, cu, out):
-            if t is not None:
-                t.record_stream(s_dec)
-                t.record_stream(s_pre)
+        if split:
+            cur.wait_stream(s_dec)
+            cur.wait_stream(s_pre)
+            # keep the step's inputs alive until both streams are done with them
+            for t in (q, k, v, x, slots, cu, out):
+                if t is not None:
+                    t.record_stream(s_dec)
+                    t.record_stream(s_pre)
         row = 0
         for r, c in spans:
             r.out.append(out[row:row + c])

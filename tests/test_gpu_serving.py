@@ -70,12 +70,15 @@ def test_varlen_with_state_slots_in_place(chunk):
         assert torch.equal(pool[r].cpu(), pool0[r])
 
 
-@pytest.mark.parametrize("gated,normalized,budget", [(True, False, 2048), (False, True, 1500)])
-def test_serving_streams_match_oracle(gated, normalized, budget):
+@pytest.mark.parametrize("gated,normalized,budget,two", [(True, False, 2048, True),
+                                                         (False, True, 1500, True),
+                                                         (True, False, 1024, False)])
+def test_serving_streams_match_oracle(gated, normalized, budget, two):
     """Five requests (prompts 3000, 1, 37, 5000, 700; then 6 decoded tokens
     each) under a small token budget: prompts are split across steps and
-    decode steps run beside prefill chunks on the other stream."""
-    banner("serving gated=%s normalized=%s budget=%d" % (gated, normalized, budget))
+    decode tokens share steps with prefill chunks (on two streams, or one)."""
+    banner("serving gated=%s normalized=%s budget=%d two_streams=%s"
+           % (gated, normalized, budget, two))
     H, d = 4, 128
     prompts = [3000, 1, 37, 5000, 700]
     ndec = 6
@@ -99,7 +102,7 @@ def test_serving_streams_match_oracle(gated, normalized, budget):
     zp = zp0.to(DEV) if normalized else None
     steps = []
     nsteps = serving.run(reqs, pool, z_pool=zp, normalized=normalized, max_batched_tokens=budget,
-                         on_step=lambda i, st: steps.append((st.num_decode, st.num_prefill,
+                         two_streams=two, on_step=lambda i, st: steps.append((st.num_decode, st.num_prefill,
                                                              st.prefill_tokens)))
     torch.cuda.synchronize()
     # the budget forces mixed steps: some with both decoders and chunks
