@@ -317,6 +317,15 @@ def bench_serving(args, torch, api, inputs, reps=50):
         return a, e_end, (e_end,)
 
     res = {"workload": w.note, "reps": reps}
+    from linear_attention_long_amd import _lib
+    opt = _lib.options(0, False, True, 0, 1e-6, 0)
+    for name, nseq, maxlen in (("one_call", nd + 1, rows - nd), ("chunk_alone", 1, rows - nd)):
+        p = _lib.plan(True, nseq, rows if nseq > 1 else rows - nd, maxlen, w.H, w.d,
+                      _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32, opt)
+        res["plan_" + name] = {"fused_gate": bool(p.fused_gate), "chunk_tokens": p.chunk_tokens,
+                               "main_workgroups": p.main_workgroups,
+                               "kernels": p.kernel_names()}
+        log("serving %s plan: %s" % (name, res["plan_" + name]))
     for view in ("wall", "device"):
         hold[0] = view == "device"
         res[view] = {}
