@@ -155,27 +155,38 @@ def bench_decode(args, torch, lib, _lib, inputs):
         for s in range(min(10, steps)):
             call(s, False)
         torch.cuda.synchronize()
-        ev.record(2 * steps, stream)
-        t0 = time.perf_counter()
-        for s in range(steps):
-            call(s, True)
-        ev.record(2 * steps + 1, stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        kern = sum(ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)) / steps
-        loop = ev.elapsed_ms(2 * steps, 2 * steps + 1) / steps
+        # three trials of `steps` back-to-back steps: per-step kernel times
+        # (HIP events around each launch), loop time and host wall time
+        per_step, loops, walls = [], [], []
+        for _trial in range(3):
+            ev.record(2 * steps, stream)
+            t0 = time.perf_counter()
+            for s in range(steps):
+                call(s, True)
+            ev.record(2 * steps + 1, stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            per_step += [ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)]
+            loops.append(ev.elapsed_ms(2 * steps, 2 * steps + 1) / steps)
+            walls.append((t1 - t0) / steps)
+        per_step.sort()
+        kern = per_step[len(per_step) // 2]
+        kern_mean = sum(per_step) / len(per_step)
+        loop = sorted(loops)[1]
+        wall = sorted(walls)[1]
         # algorithmic bytes per step: S read + write, z read + write, q/k/v in, y out
         nbytes = 2 * N * H * d * d * 4 + 3 * N * H * d * 2 + N * H * d * 4
         if normalized:
             nbytes += 2 * N * H * d * 4
         key = "normalized" if normalized else "plain"
         res[key] = {
-            "kernel_us": kern * 1e3, "loop_us_per_step": loop * 1e3,
-            "wall_us_per_step": (t1 - t0) * 1e6 / steps, "bytes_per_step": nbytes,
+            "kernel_us": kern * 1e3, "kernel_us_mean": kern_mean * 1e3,
+            "loop_us_per_step": loop * 1e3, "trials": 3, "steps_per_trial": steps,
+            "wall_us_per_step": wall * 1e6, "bytes_per_step": nbytes,
             "GBps": nbytes / (kern * 1e-3) / 1e9, "hbm_frac": nbytes / (kern * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
-        log("decode %s: kernel %.1f us/step (%.0f GB/s), loop %.1f us/step" %
-            (key, kern * 1e3, res[key]["GBps"], loop * 1e3))
+        log("decode %s: kernel %.1f us/step median of %d (%.0f GB/s), loop %.1f us/step" %
+            (key, kern * 1e3, len(per_step), res[key]["GBps"], loop * 1e3))
     del toks, S, z
     torch.cuda.empty_cache()
     return res
@@ -185,7 +196,7 @@ def bench_other_prefill(args, torch, api, inputs):
     """The 32K-token and packed-varlen workloads through the Python binding:
     whole-call time (HIP events on the current stream), median over repeats."""
     res = {}
-    for name, reps in (("prefill_32k", 50), ("varlen_512k", 10)):
+    for name, reps in (("prefill_32k", 100), ("varlen_512k", 20)):
         w = inputs.WORKLOADS[name]
         if w.kind == "prefill":
             q, k, v, x = inputs.prefill_inputs(w, device="cuda")

@@ -5,8 +5,10 @@ final states are compared in full.
 
 Samples: every token around each chunk boundary and block boundary of the
 first chunks, the first and last token of every sequence, and seeded random
-tokens.  Metric: max|err| / rms(ref) over the sampled outputs (1e-2 for bf16
-inputs) and over every final-state element.
+tokens; for the 1M-token sequence also every token of the 256-token blocks
+0, 1, 2047, 2048 and 4095 and 4096 seeded random tokens.  Metric: max|err| /
+rms(ref) over the sampled outputs (1e-2 for bf16 inputs) and over every
+final-state element.  The decode workload is compared at every step.
 """
 import numpy as np
 import pytest
@@ -64,7 +66,9 @@ def test_prefill_1m_workload_sampled():
     out, S, _ = api.la_prefill(q, k, v, x)
     torch.cuda.synchronize()
     C, dev = chunk_tokens(False, 1, w.T, w.T, w.H, w.d)
-    idx = sample_tokens([0], [w.T], C, 512, 7, every64=dev)
+    idx = sample_tokens([0], [w.T], C, 4096, 7, every64=dev)
+    blocks = np.concatenate([np.arange(256 * b, 256 * (b + 1)) for b in (0, 1, 2047, 2048, 4095)])
+    idx = np.union1d(idx, blocks).astype(np.int64)
     got = np64(out[0, torch.from_numpy(idx).cuda()])
     S_got = np64(S)
     del out, S
@@ -103,27 +107,75 @@ def test_varlen_512k_workload_sampled():
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
 
 
-def test_decode_workload_1000_steps():
-    """64 x 64 x d=128 decode, 1000 steps from S0 ~ N(0, 0.01): the final
-    state of every (sequence, head) and the last step's outputs, against the
-    oracle run as a 1000-token prefill from the same state."""
-    w = inputs.WORKLOADS["decode_64x64"]
-    banner("decode_64x64 workload, %d steps" % w.steps)
-    S0, _ = inputs.decode_state(w, device="cuda")
+def _decode_outputs(w, normalized):
+    """Every step's y [steps, N, H*d] (fp32, on the GPU), the final state and
+    normaliser, and the initial ones, for the decode workload."""
+    S0, z0 = inputs.decode_state(w, device="cuda")
     S = S0.clone()
+    z = z0.clone() if normalized else None
     toks = [inputs.decode_token(w, s, device="cuda") for s in range(w.steps)]
+    Y = torch.empty((w.steps, w.N, w.H * w.d), dtype=torch.float32, device="cuda")
     for s in range(w.steps):
-        y = api.la_decode_step(*toks[s], S)
+        api.la_decode_step(*toks[s], S, z, normalized=normalized, out=Y[s])
     torch.cuda.synchronize()
-    got_S, got_y = np64(S), np64(y)
-    # packed as 64 sequences of 1000 tokens: [N * steps, H, d]
-    qs, ks, vs = (torch.stack([t[i] for t in toks], dim=1).reshape(w.N * w.steps, w.H, w.d)
-                  .float().cpu() for i in range(3))
-    cu = np.arange(0, w.N * w.steps + 1, w.steps, dtype=np.int64)
-    last = cu[1:] - 1
-    yr, S_ref, _ = O.prefill_sampled_f32(qs, ks, vs, last, cu_seqlens=cu, state_in=S0.cpu(),
-                                         nthreads=16)
+    return toks, Y, S, z, S0, z0
+
+
+@pytest.mark.parametrize("normalized", [False, True])
+def test_decode_workload_1000_steps(normalized):
+    """64 x 64 x d=128 decode, 1000 steps from S0 (and z0) ~ N(0, 0.01): every
+    step's output, the final state and normaliser of every (sequence, head),
+    against the oracle run as 1000-token prefills from the same state, 16
+    sequences at a time.  Normalised mode: the features can be negative, so
+    denominators phi(q).z come arbitrarily close to zero; outputs are compared
+    on the (token, head) rows whose oracle denominator has magnitude >= 0.5,
+    and the excluded count is printed.  The denominator is num / y of the
+    oracle's unnormalised and normalised runs (same state, same tokens)."""
+    w = inputs.WORKLOADS["decode_64x64"]
+    banner("decode_64x64 workload, %d steps, normalized=%s" % (w.steps, normalized))
+    toks, Y, S, z, S0, z0 = _decode_outputs(w, normalized)
+    got_S = np64(S)
+    got_z = np64(z) if normalized else None
+    del S, z
+    steps, N, H, d = w.steps, w.N, w.H, w.d
+    S0c, z0c = S0.cpu(), z0.cpu()
+    per = 16
+    max_err, sumsq, cnt, excluded = 0.0, 0.0, 0, 0
+    S_ref = np.zeros((N, H, d, d))
+    z_ref = np.zeros((N, H, d))
+    for n0 in range(0, N, per):
+        n1 = min(N, n0 + per)
+        # sequences n0..n1-1 as 1000-token sequences: [nb * steps, H, d]
+        qs, ks, vs = (torch.stack([t[i][n0:n1] for t in toks], dim=1).reshape(-1, H, d)
+                      .float().cpu() for i in range(3))
+        cu = np.arange(0, (n1 - n0) * steps + 1, steps, dtype=np.int64)
+        allidx = np.arange((n1 - n0) * steps, dtype=np.int64)
+        yr, Sr, zr = O.prefill_sampled_f32(qs, ks, vs, allidx, cu_seqlens=cu,
+                                           state_in=S0c[n0:n1], z_in=z0c[n0:n1] if normalized
+                                           else None, normalized=normalized, nthreads=16)
+        S_ref[n0:n1] = Sr
+        z_ref[n0:n1] = zr
+        got = np64(Y[:, n0:n1].permute(1, 0, 2).reshape(-1, H, d))
+        if normalized:
+            num, _, _ = O.prefill_sampled_f32(qs, ks, vs, allidx, cu_seqlens=cu,
+                                              state_in=S0c[n0:n1], nthreads=16)
+            j = np.abs(num).argmax(axis=-1)[..., None]
+            den = np.take_along_axis(num, j, -1)[..., 0] / np.take_along_axis(yr, j, -1)[..., 0]
+            keep = np.abs(den) >= 0.5
+            excluded += int((~keep).sum())
+            got, yr = got[keep], yr[keep]
+        max_err = max(max_err, float(np.abs(got - yr).max()))
+        sumsq += float((yr * yr).sum())
+        cnt += yr.size
+        del qs, ks, vs, yr, got
+    e_y = max_err / np.sqrt(sumsq / cnt)
     e_S = rel_err(got_S, S_ref)
-    e_y = rel_err(got_y, yr.reshape(w.N, w.H * w.d))
-    print("decode 1000 steps: rel err state %.3e last y %.3e" % (e_S, e_y))
+    msg = "decode 1000 steps (%s): rel err every step's y %.3e, state %.3e" % (
+        "normalized" if normalized else "plain", e_y, e_S)
+    if normalized:
+        e_z = rel_err(got_z, z_ref)
+        msg += ", z %.3e; %d of %d (token, head) rows excluded (|den| < 0.5)" % (
+            e_z, excluded, steps * N * H)
+        assert e_z <= 1e-5
+    print(msg)
     assert e_S <= 1e-4 and e_y <= TOL_BF16
