@@ -67,11 +67,30 @@ class HipEvents:
         return float(ms.value)
 
 
+def inputs_digest(torch, tensors, span=4 << 20):
+    """sha256 of each input tensor's first and last `span` bytes (a fingerprint
+    of the seeded inputs that costs no full copy to the host)."""
+    import hashlib
+
+    res = {}
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        b = t.contiguous().view(torch.uint8).reshape(-1)
+        h = hashlib.sha256()
+        h.update(b[:span].cpu().numpy().tobytes())
+        h.update(b[-span:].cpu().numpy().tobytes())
+        res[name] = h.hexdigest()
+    res["recipe"] = "sha256 of the first and last %d bytes of each tensor" % span
+    return res
+
+
 def bench_prefill(args, torch, lib, _lib, inputs):
     w = inputs.WORKLOADS[args.workload]
     T, H, d = w.T, w.H, w.d
     log("generating %s inputs on the GPU (%s)" % (w.name, w.note))
     q, k, v, x = inputs.prefill_inputs(w, device="cuda")
+    digest = inputs_digest(torch, {"q": q, "k": k, "v": v, "x": x})
     dev = q.device
     out = torch.empty((1, T, H * d), dtype=torch.float32, device=dev)
     state_out = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
@@ -120,6 +139,7 @@ def bench_prefill(args, torch, lib, _lib, inputs):
         "fused_gate": bool(plan.fused_gate), "main_workgroups": plan.main_workgroups,
         "ms_per_step": ms_step,
         "tokens_per_s": T / (ms_step * 1e-3), "per_kernel_ms": per_kernel, "token_heads": th,
+        "inputs_sha256": digest,
     }
     del q, k, v, x, out, ws
     torch.cuda.empty_cache()
@@ -555,6 +575,7 @@ def main():
                      "avg_launch_ms": main_ms},
         "cpu_baseline": cpu,
         "prefill": {"per_kernel_ms": pre["per_kernel_ms"], "path_min_bytes_GBps": path_gbs,
+                    "inputs_sha256": pre["inputs_sha256"],
                     "path_hbm_roofline_frac": path_gbs / HBM_PEAK_GBS,
                     "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS},
         "decode": dec,
