@@ -201,8 +201,11 @@ typedef enum {
                                       varlen batch held in one chunk each) */
     LA_KERNEL_CHUNK_STATE = 3,     /* per-chunk increments of S (and z) */
     LA_KERNEL_CHUNK_SCAN = 4,      /* exclusive prefix of the increments over
-                                      each sequence's chunks; final states */
-    LA_KERNEL_EXCHANGE_CLEAR = 5,  /* fused gate: clears its exchange buffer */
+                                      each sequence's chunks; final states;
+                                      with the fused gate it also clears the
+                                      gate's exchange buffer */
+    LA_KERNEL_EXCHANGE_CLEAR = 5,  /* fused gate without chunking: clears its
+                                      exchange buffer */
     LA_KERNEL_MAIN = 6,            /* main pass: y of every token */
     LA_KERNEL_MAIN_GATED = 7,      /* main pass with the gate fused in */
     LA_KERNEL_GATE = 8             /* RMSNorm * w * sigmoid(x) gate */

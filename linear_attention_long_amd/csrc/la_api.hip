@@ -295,7 +295,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         tm.before();
         k_chunk_scan<<<dim3((unsigned)nblk, (unsigned)H, (unsigned)nseq), 256, 0, st>>>(
             buf, p.stride, map, H, d, E, state_in, norm ? z_in : nullptr, state_out,
-            norm ? z_out : nullptr);
+            norm ? z_out : nullptr, p.fuse_ok ? (uint64_t*)(ws + p.off_xbuf) : nullptr,
+            p.fuse_ok ? p.xbuf_words : 0);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
     }
@@ -310,10 +311,12 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
                                         : (const void*)mf::k_prefill_fused<false, uint16_t, 32>);
         uint64_t* xbuf = (uint64_t*)(ws + p.off_xbuf);
         const int64_t nw = p.xbuf_words;
-        tm.before();
-        k_zero_u64<<<(unsigned)((nw + 255) / 256), 256, 0, st>>>(xbuf, nw);
-        if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
-        tm.after();
+        if (!p.chunked) {  // (a chunked call's scan cleared it)
+            tm.before();
+            k_zero_u64<<<(unsigned)((nw + 255) / 256), 256, 0, st>>>(xbuf, nw);
+            if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
+            tm.after();
+        }
         const uint16_t* qb = (const uint16_t*)q;
         const uint16_t* kb = (const uint16_t*)k;
         const uint16_t* vb = (const uint16_t*)v;
@@ -531,7 +534,7 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, i
             r.kernels[n++] = LA_KERNEL_CHUNK_SCAN;
         }
         if (p.fuse_ok) {
-            r.kernels[n++] = LA_KERNEL_EXCHANGE_CLEAR;
+            if (!p.chunked) r.kernels[n++] = LA_KERNEL_EXCHANGE_CLEAR;
             r.kernels[n++] = LA_KERNEL_MAIN_GATED;
         } else {
             r.kernels[n++] = LA_KERNEL_MAIN;

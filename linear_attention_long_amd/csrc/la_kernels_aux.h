@@ -75,7 +75,16 @@ __global__ __launch_bounds__(256) void k_plan_chunks(const int32_t* __restrict__
 __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int64_t stride,
                                                     ItemMap map, int H, int D, int E,
                                                     const float* state_in, const float* z_in,
-                                                    float* state_out, float* z_out) {
+                                                    float* state_out, float* z_out,
+                                                    uint64_t* __restrict__ xclear, int64_t nclear) {
+    // the fused gate's exchange buffer (when the main pass that follows has
+    // one) is cleared here too, which saves a launch
+    if (xclear) {
+        const int64_t nthr = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+        const int64_t gid =
+            (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+        for (int64_t i = gid; i < nclear; i += nthr) xclear[i] = 0ull;
+    }
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= E) return;
     const int h = blockIdx.y, s = blockIdx.z;
@@ -88,11 +97,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
         if (e < DD) acc = state_in ? state_in[((size_t)row * H + h) * DD + e] : 0.f;
         else acc = z_in ? z_in[((size_t)row * H + h) * D + (e - DD)] : 0.f;
     }
-    for (int32_t i = 0; i < count; ++i) {
-        float* p = buf + ((size_t)(first + i) * H + h) * stride + e;
-        const float dlt = *p;
-        *p = acc;
-        acc += dlt;
+    // eight increments in flight at a time, then their prefixes in order
+    constexpr int U = 8;
+    for (int32_t i0 = 0; i0 < count; i0 += U) {
+        float dlt[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+            dlt[j] = i0 + j < count ? buf[((size_t)(first + i0 + j) * H + h) * stride + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if (i0 + j < count) buf[((size_t)(first + i0 + j) * H + h) * stride + e] = acc;
+            acc += dlt[j];
+        }
     }
     if (row < 0) return;
     if (e < DD) {
