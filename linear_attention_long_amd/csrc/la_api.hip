@@ -323,8 +323,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const uint16_t* xb = (const uint16_t*)x;
         int k16 = 16, spin = kSpinLimit, Hh = H;
         float eps = o.eps;
-        float* so = p.chunked ? nullptr : state_out;
-        float* zo = (p.chunked || !norm) ? nullptr : z_out;
+        float* so = state_out;  // written after each sequence's last chunk
+        float* zo = norm ? z_out : nullptr;
         const float* bufc = buf;
         int64_t stride = p.stride;
         OutT* outp = (OutT*)out;
@@ -350,8 +350,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const uint16_t* qb = (const uint16_t*)q;
         const uint16_t* kb = (const uint16_t*)k;
         const uint16_t* vb = (const uint16_t*)v;
-        float* so = p.chunked ? nullptr : state_out;
-        float* zo = p.chunked ? nullptr : z_out;
+        float* so = state_out;  // written after each sequence's last chunk
+        float* zo = z_out;
 #define LA_MF_MAIN(NN, YT, TBV) \
     mf::k_prefill_main<NN, YT, TBV><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
         if (p.block == 32) {
@@ -366,7 +366,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
 #define LA_VALU_MAIN(DD, YT, NN)                                                                \
     vk::k_valu_main<DD, InT, YT, NN><<<grid, vk::NT, 0, st>>>(                                  \
         (const InT*)q, (const InT*)k, (const InT*)v, map, H, p.block, buf, p.stride, state_in,  \
-        z_in, (YT*)ydst, p.chunked ? nullptr : state_out, p.chunked ? nullptr : z_out)
+        z_in, (YT*)ydst, state_out, z_out)
         if (d == 128) {
             if (y_is_f32) { if (norm) LA_VALU_MAIN(128, float, true); else LA_VALU_MAIN(128, float, false); }
             else { if (norm) LA_VALU_MAIN(128, uint16_t, true); else LA_VALU_MAIN(128, uint16_t, false); }

@@ -70,8 +70,10 @@ __global__ __launch_bounds__(256) void k_plan_chunks(const int32_t* __restrict__
 }
 
 // Exclusive prefix over the chunks of each sequence, in increasing chunk order
-// (deterministic): buf[item] <- init + sum of the earlier chunks' increments;
-// the full sum goes to state_out / z_out.  E = D*D (+ D with the normaliser).
+// (deterministic): buf[item] <- init + sum of the earlier chunks' increments.
+// The main pass writes each sequence's final state after its last chunk;
+// here only sequences without tokens get theirs (= init).  E = D*D (+ D with
+// the normaliser).
 __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int64_t stride,
                                                     ItemMap map, int H, int D, int E,
                                                     const float* state_in, const float* z_in,
@@ -97,20 +99,23 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
         if (e < DD) acc = state_in ? state_in[((size_t)row * H + h) * DD + e] : 0.f;
         else acc = z_in ? z_in[((size_t)row * H + h) * D + (e - DD)] : 0.f;
     }
-    // eight increments in flight at a time, then their prefixes in order
+    // eight increments in flight at a time, then their prefixes in order (the
+    // last chunk has no increment: the main pass writes the final state)
     constexpr int U = 8;
     for (int32_t i0 = 0; i0 < count; i0 += U) {
         float dlt[U];
 #pragma unroll
         for (int j = 0; j < U; ++j)
-            dlt[j] = i0 + j < count ? buf[((size_t)(first + i0 + j) * H + h) * stride + e] : 0.f;
+            dlt[j] = i0 + j < count - 1 ? buf[((size_t)(first + i0 + j) * H + h) * stride + e] : 0.f;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             if (i0 + j < count) buf[((size_t)(first + i0 + j) * H + h) * stride + e] = acc;
             acc += dlt[j];
         }
     }
-    if (row < 0) return;
+    // a sequence with no tokens has no main-pass item: its final state is its
+    // initial one
+    if (row < 0 || count > 0) return;
     if (e < DD) {
         if (state_out) state_out[((size_t)row * H + h) * DD + e] = acc;
     } else if (z_out) {

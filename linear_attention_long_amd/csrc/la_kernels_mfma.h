@@ -297,7 +297,9 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
 }
 
 // Per-chunk state increment dS = sum_{t in chunk} phi(k_t) phi(v_t)^T (and
-// dz = sum phi(k_t)), written to buf[item][h] = [dS (D*D) | dz (D)].
+// dz = sum phi(k_t)), written to buf[item][h] = [dS (D*D) | dz (D)].  The
+// last chunk of a sequence is skipped: no later chunk starts from it, and the
+// main pass writes the sequence's final state.
 // Software-pipelined over 32-token blocks with two LDS buffers: in step n
 // the workgroup stages block n+1 (SiLU + split, vector ALU) into one buffer
 // while the state update of block n (matrix cores) reads the other, with
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     (void)lane;
     const int h = blockIdx.y;
     Item it;
-    if (!decode_item(map, blockIdx.x, it)) return;
+    if (!decode_item(map, blockIdx.x, it) || it.last) return;
 
     f32x4_t S[8][2];
 #pragma unroll
@@ -540,9 +542,9 @@ __device__ __forceinline__ void stage_q(SM& sm, const uint4 (&rq)[NJ], int tid) 
 }
 
 // Main pass over one (chunk, head).  Starting state: prefix[item][h] if
-// prefix != nullptr, else state_in/z_in of the sequence (or zeros).  When the
-// chunk is a whole sequence (no prefix), the final state is written to
-// state_out/z_out (if given).  Unfused: Y goes to y[t][h*D + j].  Fused: the
+// prefix != nullptr, else state_in/z_in of the sequence (or zeros).  After the
+// last chunk of a sequence the final state is written to state_out/z_out (if
+// given).  Unfused: Y goes to y[t][h*D + j].  Fused: the
 // gated output goes there instead; the heads of the chunk exchange each
 // block's per-token sums of y^2 (tag = block number + 1).  k16 must be 16.
 template <bool NORM, bool FUSE, typename OutT, typename InT, int TB>
@@ -821,7 +823,7 @@ __device__ __forceinline__ void process_item(
                              ga.eps, rs, wave, g, c);
     }
 
-    if (!prefix && it.row >= 0) {
+    if (it.last && it.row >= 0) {
         if (state_out) {
             float* dst = state_out + ((size_t)it.row * H + h) * D * D;
 #pragma unroll

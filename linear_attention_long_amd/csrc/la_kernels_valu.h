@@ -57,7 +57,8 @@ __global__ __launch_bounds__(NT, 1) void k_valu_state(const InT* __restrict__ k,
     __shared__ SmemState<D> sm;
     const int tid = threadIdx.x, h = blockIdx.y;
     Item it;
-    if (!decode_item(map, blockIdx.x, it)) return;
+    // (the last chunk of a sequence: the main pass writes the final state)
+    if (!decode_item(map, blockIdx.x, it) || it.last) return;
     const int dv = tid % D, dk0 = tid / D;
     constexpr int DKS = NT / D;
     float s[PER];
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
             }
         }
     }
-    if (!prefix && it.row >= 0) {
+    if (it.last && it.row >= 0) {
         __syncthreads();
         if (state_out) {
             float* dst = state_out + ((size_t)it.row * H + h) * D * D;
