@@ -1,0 +1,105 @@
+"""The calls under HIP graph capture (torch.cuda.graph): decode, the fused and
+chunked prefill (cooperative launch), a packed prefill with state slots and a
+serving step are captured once and replayed several times, with eager work
+and synchronisation between replays; every replay must reproduce the eager
+result bit for bit.  (No call records a memset node: buffers that must start
+at zero are cleared by kernels.)"""
+import pytest
+import torch
+
+from linear_attention_long_amd import api, inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def rnd(shape, seed, scale=1.0, dtype=torch.bfloat16):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * scale).to(dtype)
+
+
+def capture(fn):
+    """Warm fn on a side stream, then capture it; returns (graph, outputs)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = fn()
+    return g, outs
+
+
+def replay_and_check(g, reset, outs, refs, n=4):
+    for r in range(n):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, ref in zip(outs, refs):
+            assert torch.equal(o, ref), "replay %d differs" % r
+        # eager work between replays
+        assert torch.isfinite(outs[0].float().sum() * 0.5).item()
+
+
+def test_graph_decode():
+    N, H, d = 8, 8, 128
+    q, k, v = rnd((N, H, d), 1), rnd((N, H, d), 2), rnd((N, H, d), 3)
+    S0 = rnd((N, H, d, d), 4, 0.01, torch.float32)
+    S_e = S0.clone()
+    y_e = api.la_decode_step(q, k, v, S_e)
+    S_g = S0.clone()
+    g, (y_g,) = capture(lambda: (api.la_decode_step(q, k, v, S_g),))
+    replay_and_check(g, lambda: S_g.copy_(S0), [y_g, S_g], [y_e, S_e])
+
+
+@pytest.mark.parametrize("T", [4096, 32768])
+def test_graph_prefill_fused_chunked(T):
+    H, d = 8, 128
+    q, k, v = (rnd((1, T, H, d), 10 + i, 128 ** -0.5) for i in range(3))
+    x = rnd((1, T, H * d), 13)
+    out_e, S_e, _ = api.la_prefill(q, k, v, x)
+    g, (out_g, S_g) = capture(lambda: api.la_prefill(q, k, v, x)[:2])
+    replay_and_check(g, lambda: out_g.zero_(), [out_g, S_g], [out_e, S_e])
+
+
+def test_graph_varlen_with_slots_and_serving_step():
+    H, d = 8, 128
+    lengths = [700, 1, 0, 2000, 64]
+    cu = inputs.cu_from_lengths(lengths).to(DEV)
+    total = int(cu[-1])
+    q, k, v = (rnd((total, H, d), 20 + i, 128 ** -0.5) for i in range(3))
+    x = rnd((total, H * d), 23)
+    pool0 = rnd((9, H, d, d), 24, 0.02, torch.float32)
+    slots = torch.tensor([4, 0, 7, 2, 8], dtype=torch.int32, device=DEV)
+    pool_e = pool0.clone()
+    out_e, _, _ = api.la_prefill_varlen(q, k, v, cu, max(lengths), x, None, pool_e,
+                                        state_slots=slots)
+    pool_g = pool0.clone()
+    g, (out_g,) = capture(lambda: (api.la_prefill_varlen(q, k, v, cu, max(lengths), x, None,
+                                                         pool_g, state_slots=slots)[0],))
+    replay_and_check(g, lambda: pool_g.copy_(pool0), [out_g, pool_g], [out_e, pool_e])
+
+    # a serving step: 3 decode tokens (rows 0..2), then chunks of 500 and 37 tokens
+    nd = 3
+    rows = nd + 537
+    dslots = torch.tensor([1, 3, 5], dtype=torch.int32, device=DEV)
+    pslots = torch.tensor([6, 0], dtype=torch.int32, device=DEV)
+    pcu = torch.tensor([0, 500, 537], dtype=torch.int32, device=DEV)
+    qs, ks, vs, xs = q[:rows], k[:rows], v[:rows], x[:rows]
+    cur = torch.cuda.current_stream()
+    pool_e = pool0.clone()
+    out_e = api.la_serve_step(qs, ks, vs, pool_e, dslots, pcu, pslots, 500, x=xs,
+                              decode_stream=cur, prefill_stream=cur)
+    pool_g = pool0.clone()
+
+    def step():
+        s = torch.cuda.current_stream()
+        return (api.la_serve_step(qs, ks, vs, pool_g, dslots, pcu, pslots, 500, x=xs,
+                                  decode_stream=s, prefill_stream=s),)
+
+    g, (out_g,) = capture(step)
+    replay_and_check(g, lambda: pool_g.copy_(pool0), [out_g, pool_g], [out_e, pool_e])
