@@ -26,6 +26,10 @@ constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
 constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
 constexpr int kSpinLimit = 1 << 22;     // bounded waits of the fused gate (~seconds)
+#ifndef LA_DECODE_SPLIT
+#define LA_DECODE_SPLIT 4
+#endif
+constexpr int kDecodeSplit = LA_DECODE_SPLIT;  // decode workgroups per (sequence, head), plain mode
 
 // Workgroups of `kernel` (256 threads) the current device keeps resident at
 // once, or 0 when cooperative launch is unavailable.
@@ -652,9 +656,15 @@ static la_status_t decode_step_impl(bool launch, const void* q, const void* k, c
     Timer tm(o, st);
     void* ydst = o.gated ? (need ? workspace : out) : out;
     const bool yf32 = o.gated || out_dtype == LA_DTYPE_F32;
+    // plain mode, d = 128: kDecodeSplit workgroups per (sequence, head), each
+    // owning 128 / kDecodeSplit state columns
     const unsigned grid = (unsigned)((int64_t)N * H);
-#define LA_DEC(DD, IT, OT, NN) \
-    k_decode<DD, IT, OT, NN><<<grid, 256, 0, st>>>((const IT*)q, (const IT*)k, (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H)
+#define LA_DEC(DD, IT, OT, NN)                                                                     \
+    do {                                                                                           \
+        constexpr int SP = (!(NN) && (DD) == 128) ? kDecodeSplit : 1;                              \
+        k_decode<DD, IT, OT, NN, SP><<<grid * SP, 256, 0, st>>>((const IT*)q, (const IT*)k,         \
+            (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H);                               \
+    } while (0)
 #define LA_DEC_OUT(DD, IT)                                                                  \
     do {                                                                                    \
         if (yf32) { if (o.normalized) LA_DEC(DD, IT, float, true); else LA_DEC(DD, IT, float, false); } \

@@ -248,27 +248,33 @@ __global__ __launch_bounds__(256) void k_gate4(const float* y, const XT* __restr
 // With a slot table (slots != nullptr) the state of sequence n is row
 // slots[n] of S and z (rows of them); a slot outside [0, rows) gives y = 0
 // and touches no state.
-template <int D, typename InT, typename OutT, bool NORM>
+template <int D, typename InT, typename OutT, bool NORM, int SPLIT>
 __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const InT* __restrict__ k,
                                                 const InT* __restrict__ v, float* __restrict__ S,
                                                 float* __restrict__ z, OutT* __restrict__ y,
                                                 const int32_t* __restrict__ slots, int32_t rows,
                                                 int H) {
-    constexpr int CQ = D / 4;      // threads per state row (float4 each)
+    // SPLIT workgroups per (sequence, head), each owning D / SPLIT value
+    // columns of the state (more, smaller workgroups stream better); the
+    // normaliser is shared by all columns, so the normalised mode is unsplit
+    static_assert(!NORM || SPLIT == 1, "the normalised mode updates z in one workgroup");
+    constexpr int DC = D / SPLIT;  // value columns of this workgroup
+    constexpr int CQ = DC / 4;     // threads per state row (float4 each)
     constexpr int RG = 256 / CQ;   // row groups
     constexpr int M = D / RG;      // rows per thread
-    __shared__ float fq[D], fk[D], fv[D];
+    __shared__ float fq[D], fk[D], fv[DC];
     __shared__ float4 part[RG][CQ];
     __shared__ float dpart[4];
     const int tid = threadIdx.x;
-    const size_t pair = blockIdx.x;  // sequence * H + head (token rows)
+    const size_t pair = blockIdx.x / SPLIT;  // sequence * H + head (token rows)
+    const int c0 = (int)(blockIdx.x % SPLIT) * DC;
     const size_t vb = pair * D;
     size_t spair = pair;             // row * H + head (state rows)
     if (slots) {
         const int n = (int)(pair / H), h = (int)(pair - (size_t)n * H);
         const int32_t r = slots[n];
         if (r < 0 || r >= rows) {
-            if (tid < D) store_from_f32<OutT>(y + vb + tid, 0.f);
+            if (tid < DC) store_from_f32<OutT>(y + vb + c0 + tid, 0.f);
             return;
         }
         spair = (size_t)r * H + h;
@@ -276,8 +282,8 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
     if (tid < D) {
         fq[tid] = silu(load_as_f32<InT>(q + vb + tid));
         fk[tid] = silu(load_as_f32<InT>(k + vb + tid));
-        fv[tid] = silu(load_as_f32<InT>(v + vb + tid));
     }
+    if (tid < DC) fv[tid] = silu(load_as_f32<InT>(v + vb + c0 + tid));
     __syncthreads();
     float den_part = 0.f;
     if (NORM && tid < D) {
@@ -287,10 +293,10 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
     }
     const int cq = tid % CQ, rg = tid / CQ;
     const float4 v4 = make_float4(fv[4 * cq], fv[4 * cq + 1], fv[4 * cq + 2], fv[4 * cq + 3]);
-    float4* S4 = (float4*)(S + spair * D * D);
+    float4* S4 = (float4*)(S + spair * D * D + c0);
     float4 s[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) s[m] = S4[(rg + RG * m) * CQ + cq];
+    for (int m = 0; m < M; ++m) s[m] = S4[(rg + RG * m) * (D / 4) + cq];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
         t.y += kk * v4.y;
         t.z += kk * v4.z;
         t.w += kk * v4.w;
-        S4[i * CQ + cq] = t;
+        S4[i * (D / 4) + cq] = t;
         acc.x += qq * t.x;
         acc.y += qq * t.y;
         acc.z += qq * t.z;
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
         if ((tid & 63) == 0) dpart[tid >> 6] = den_part;
     }
     __syncthreads();
-    if (tid < D) {
+    if (tid < DC) {
         const int c4 = tid >> 2, e = tid & 3;
         float a = 0.f;
 #pragma unroll
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
             a += e == 0 ? p.x : e == 1 ? p.y : e == 2 ? p.z : p.w;
         }
         if (NORM) a /= (dpart[0] + dpart[1] + dpart[2] + dpart[3]);
-        store_from_f32<OutT>(y + vb + tid, a);
+        store_from_f32<OutT>(y + vb + c0 + tid, a);
     }
 }
 
