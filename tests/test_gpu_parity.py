@@ -292,6 +292,38 @@ def test_fused_gate_varlen_device_chunking():
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
 
 
+@pytest.mark.parametrize("varlen", [True, False])
+def test_more_sequences_than_resident_teams(varlen):
+    """150 sequences with 8 heads: more teams than the device keeps resident,
+    so the gate runs as its own kernel after the main pass; every output and
+    final state against the oracle."""
+    banner("150 sequences, varlen=%s (gate not fused)" % varlen)
+    H, d = 8, 128
+    rng = np.random.default_rng(321)
+    lengths = rng.integers(0, 300, size=150).tolist() if varlen else [97] * 150
+    cu = inputs.cu_from_lengths(lengths)
+    total = int(cu[-1])
+    plan = fused_plan(varlen, len(lengths), total, max(lengths), H)
+    assert plan.fused_gate == 0 and plan.kernel_names()[-2:] == ["main", "gate"], plan.kernel_names()
+    s_ = 1.0 / np.sqrt(d)
+    q, k, v = (randn((total, H, d), 330 + i, s_, dtype=torch.bfloat16) for i in range(3))
+    x = randn((total, H * d), 333, dtype=torch.bfloat16)
+    S0 = randn((len(lengths), H, d, d), 334, 0.05)
+    if varlen:
+        out, S, _ = api.la_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(lengths),
+                                          x.to(DEV), None, S0.to(DEV))
+    else:
+        T = lengths[0]
+        out, S, _ = api.la_prefill(q.reshape(150, T, H, d).to(DEV), k.reshape(150, T, H, d).to(DEV),
+                                   v.reshape(150, T, H, d).to(DEV), x.reshape(150, T, H * d).to(DEV),
+                                   None, S0.to(DEV))
+        out = out.reshape(total, H * d)
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(q, k, v, x, None, cu_seqlens=cu.numpy(), state_in=S0, gated=True)
+    assert rel_err(np64(out), ref) <= TOL_BF16
+    assert rel_err(np64(S), Sref) <= TOL_BF16
+
+
 def test_unfused_gate_when_heads_exceed_fused_limit():
     banner("gate not fused: H=9 (unfused path), parity")
     T, H, d = 700, 9, 128
