@@ -110,6 +110,4 @@ __device__ __forceinline__ i16x4_t lds_read_tr4(const uint16_t* tile, int stride
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
-__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
-
 }  // namespace la

@@ -380,17 +380,6 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     if (NORM && tid < D) dst[D * D + tid] = zacc;
 }
 
-template <typename OutT> __device__ __forceinline__ void store4(OutT* p, f32x4_t v, float s);
-template <> __device__ __forceinline__ void store4<float>(float* p, f32x4_t v, float s) {
-    *(float4*)p = make_float4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-}
-template <> __device__ __forceinline__ void store4<uint16_t>(uint16_t* p, f32x4_t v, float s) {
-    uint2 u;
-    u.x = pack_bf16x2(v[0] * s, v[1] * s);
-    u.y = pack_bf16x2(v[2] * s, v[3] * s);
-    *(uint2*)p = u;
-}
-
 // Arguments of the fused gate (RMSNorm over all H heads of a token, times
 // w * sigmoid(x)), applied by the main pass when its workgroups run as
 // cooperative teams of H (one per head) that exchange per-token sums of y^2.
