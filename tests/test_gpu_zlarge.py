@@ -83,6 +83,38 @@ def test_prefill_1m_workload_sampled():
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
 
 
+def test_prefill_4m_past_32bit_offsets():
+    """One 4,194,307-token sequence (the pages' 4M-token inference context),
+    8 heads of 128, gated: each of q, k, v holds 4.29e9 elements, so the last
+    tokens lie past 2^32 elements and the tokens past 2,097,152 past 2^31 --
+    any 32-bit offset in a kernel would show.  Sampled as the 1M-token case,
+    plus every token of the first and last blocks and tokens around the 2^31
+    and 2^32 element marks."""
+    w = inputs.WORKLOADS["prefill_1m"]
+    T = (1 << 22) + 3
+    banner("prefill, T=%d (offsets past 2^32 elements)" % T)
+    q, k, v, x = inputs.prefill_inputs(w, T=T, device="cuda")
+    out, S, _ = api.la_prefill(q, k, v, x)
+    torch.cuda.synchronize()
+    C, dev = chunk_tokens(False, 1, T, T, w.H, w.d)
+    idx = sample_tokens([0], [T], C, 2048, 17, every64=dev)
+    marks = np.concatenate([np.arange(0, 64), np.arange(T - 64, T),
+                            np.arange((1 << 21) - 3, (1 << 21) + 3), np.arange((1 << 22) - 3, T)])
+    idx = np.union1d(idx, marks).astype(np.int64)
+    got = np64(out[0, torch.from_numpy(idx).cuda()])
+    S_got = np64(S)
+    del out, S
+    qc, kc, vc = (t[0].float().cpu() for t in (q, k, v))
+    xs = x[0, torch.from_numpy(idx).cuda()].float().cpu()
+    del q, k, v, x
+    torch.cuda.empty_cache()
+    y, S_ref, _ = O.prefill_sampled_f32(qc, kc, vc, idx, nthreads=w.H)
+    ref = O.gate(y.reshape(len(idx), w.H * w.d), xs, None, 0, 1e-6)
+    e_out, e_S = rel_err(got, ref), rel_err(S_got, S_ref)
+    print("prefill T=%d: %d sampled tokens, rel err out %.3e state %.3e" % (T, len(idx), e_out, e_S))
+    assert e_out <= TOL_BF16 and e_S <= TOL_BF16
+
+
 def test_varlen_512k_workload_sampled():
     w = inputs.WORKLOADS["varlen_512k"]
     banner("varlen_512k workload (sampled)")
