@@ -213,10 +213,10 @@ def bench_decode(args, torch, lib, _lib, inputs):
 
 
 def bench_other_prefill(args, torch, api, inputs):
-    """The 32K-token and packed-varlen workloads through the Python binding:
+    """The 32K-token, packed-varlen and 4M-token workloads through the Python binding:
     whole-call time (HIP events on the current stream), median over repeats."""
     res = {}
-    for name, reps in (("prefill_32k", 100), ("varlen_512k", 20)):
+    for name, reps in (("prefill_32k", 100), ("varlen_512k", 20), ("prefill_4m", 5)):
         w = inputs.WORKLOADS[name]
         if w.kind == "prefill":
             q, k, v, x = inputs.prefill_inputs(w, device="cuda")

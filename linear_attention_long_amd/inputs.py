@@ -67,6 +67,10 @@ WORKLOADS = {
     "prefill_1m": Workload("prefill_1m", "prefill", 1003, H=8, d=128, dtype="bf16",
                            T=1048576, scale=INV_SQRT128, gated=True, gen_device="cuda",
                            note="bf16, B=1 T=1048576 H=8 d=128, RMSNorm*sigmoid gate"),
+    # the pages' 4M-token inference context, same recipe (timing only)
+    "prefill_4m": Workload("prefill_4m", "prefill", 1007, H=8, d=128, dtype="bf16",
+                           T=4194304, scale=INV_SQRT128, gated=True, gen_device="cuda",
+                           note="bf16, B=1 T=4194304 H=8 d=128, RMSNorm*sigmoid gate"),
     # packed variable-length batch
     "varlen_512k": Workload("varlen_512k", "varlen", 1004, H=8, d=128, dtype="bf16",
                             total_T=524288, scale=INV_SQRT128, gated=True, gen_device="cuda",
