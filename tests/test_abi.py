@@ -144,6 +144,8 @@ def test_prefill_rejects_bad_arguments(lib):
     assert prefill(lib, T=-1) == INVALID
     assert prefill(lib, Bt=0) == INVALID
     assert prefill(lib, idt=7) == INVALID
+    assert prefill(lib, Bt=1 << 16, T=1 << 15) == INVALID                # Bt*T past int32 tokens
+    assert prefill(lib, H=1 << 15) == UNSUPPORTED                        # H*d past 2^20 features
     assert prefill(lib, o=opt(block_size=48)) == UNSUPPORTED
     assert prefill(lib, o=opt(normalized=2)) == INVALID
     assert prefill(lib, o=opt(gated=1)) == INVALID                         # no gate input
