@@ -1,4 +1,5 @@
-"""ctypes view of liblinattn.so (the C ABI declared in include/la.h)."""
+"""ctypes view of liblinattn.so (the C ABI declared in include/la.h and
+include/la_softmax.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -16,7 +17,7 @@ LA_ERR_HIP = 4
 LA_DTYPE_F32 = 0
 LA_DTYPE_BF16 = 1
 
-# every extern "C" function declared in include/la.h
+# every extern "C" function declared in include/la.h and include/la_softmax.h
 EXPORTS = (
     "la_default_options",
     "la_prefill",
@@ -30,6 +31,9 @@ EXPORTS = (
     "la_serve_step",
     "la_serve_step_workspace_bytes",
     "la_status_string",
+    "la_softmax_default_options",
+    "la_softmax_attention_varlen",
+    "la_softmax_workspace_bytes",
 )
 
 
@@ -59,6 +63,16 @@ KERNEL_NAMES = {
     7: "main_gated",
     8: "gate",
 }
+
+
+class SoftmaxOptions(ctypes.Structure):
+    _fields_ = [
+        ("rotary_dim", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("scale", ctypes.c_float),
+        ("timing_events", ctypes.c_void_p),
+        ("n_timing", ctypes.c_int32),
+    ]
 
 
 class Plan(ctypes.Structure):
@@ -152,6 +166,17 @@ def load() -> ctypes.CDLL:
         lib.la_serve_step_workspace_bytes.restype = _sz
         lib.la_serve_step_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                       ctypes.c_int, ctypes.c_int, _optp]
+        lib.la_softmax_default_options.restype = SoftmaxOptions
+        lib.la_softmax_default_options.argtypes = []
+        lib.la_softmax_attention_varlen.restype = ctypes.c_int
+        lib.la_softmax_attention_varlen.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                    _i32, _i32, ctypes.c_int, ctypes.c_int, _vp,
+                                                    _fp, ctypes.POINTER(SoftmaxOptions), _vp, _sz,
+                                                    _vp]
+        lib.la_softmax_workspace_bytes.restype = _sz
+        lib.la_softmax_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                   ctypes.c_int, ctypes.c_int,
+                                                   ctypes.POINTER(SoftmaxOptions)]
         _lib = lib
         return lib
 
@@ -172,6 +197,14 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     o.norm_group = int(norm_group)
     o.rms_eps = float(rms_eps)
     o.chunk_tokens = int(chunk_tokens)
+    return o
+
+
+def softmax_options(rotary_dim=-1, rope_base=10000.0, scale=0.0) -> SoftmaxOptions:
+    o = load().la_softmax_default_options()
+    o.rotary_dim = int(rotary_dim)
+    o.rope_base = float(rope_base)
+    o.scale = float(scale)
     return o
 
 

@@ -234,3 +234,39 @@ prefill_varlen = la_prefill_varlen
 decode_step = la_decode_step
 schedule_step = la_schedule_step
 serve_step = la_serve_step
+
+
+def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-1,
+                                rope_base=10000.0, scale=0.0, out_dtype=torch.bfloat16,
+                                return_lse=False, out=None, stream=None):
+    """Causal softmax attention with rotary embedding over a packed batch
+    (the hybrid model's softmax layer).  q: [total_T, H, d] bfloat16; k, v:
+    [total_T, H_kv, d] bfloat16 (H_kv divides H); cu_seqlens: int32
+    [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
+    rotary_dim -1 = d/2; scale 0 = 1/sqrt(d).  Returns (out [total_T, H, d],
+    lse [total_T, H] float32 or None)."""
+    lib = _lib.load()
+    total_T, H, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != total_T or k.shape[2] != d:
+        raise ValueError("k and v must be [total_T, H_kv, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must have the same dtype")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    num_seqs = cu_seqlens.numel() - 1
+    opt = _lib.softmax_options(rotary_dim, rope_base, scale)
+    in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
+    dev = q.device
+    if out is None:
+        out = torch.empty((total_T, H, d), dtype=out_dtype, device=dev)
+    lse = torch.empty((total_T, H), dtype=torch.float32, device=dev) if return_lse else None
+    nbytes = lib.la_softmax_workspace_bytes(num_seqs, total_T, int(max_seqlen), H, H_kv, d,
+                                            in_dt, out_dt, ctypes.byref(opt))
+    ws = _workspace(nbytes, dev)
+    st = lib.la_softmax_attention_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), num_seqs,
+                                         total_T, int(max_seqlen), H, H_kv, d, in_dt, out_dt,
+                                         _ptr(out), _ptr(lse), ctypes.byref(opt), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(stream))
+    _lib.check(st, "la_softmax_attention_varlen")
+    return out, lse

@@ -18,7 +18,7 @@ ARCH = "gfx950"
 
 
 def sources():
-    return [os.path.join(CSRC, "la_api.hip")]
+    return [os.path.join(CSRC, "la_api.hip"), os.path.join(CSRC, "sm_api.hip")]
 
 
 def build(verbose: bool = False) -> str:

@@ -1,0 +1,491 @@
+// sm_kernels.h -- the softmax attention layer of the hybrid model (one layer
+// in eight; the others are linear attention), head dim 128, bf16 inputs.
+//
+// Method: page "六十四：MiniMax-01" (LLM tutorial, lesson 64), sections 2-3:
+// softmax(Q K^T / sqrt(d)) V, causal; page "MiniMax-Text-01 405B
+// MoE模型架构与训练策略解析", section 2.2: rotary position embedding on half of
+// each head's dimensions (base 10,000, raised to 5M and 10M in section 4.1);
+// page "MiniMax-01系列大模型：超长上下文与多模态能力深度解析与部署指南",
+// section 2.1.3: packed variable-length sequences.  Inside the first `rot`
+// dimensions, dimension j pairs with j + rot/2 and turns by pos * base^(-2j/rot),
+// positions counting from each sequence's start; query head h reads key/value
+// head h / (H / Hkv).
+//
+// Three kernels per call:
+//  * k_sm_plan (packed batches of more than one sequence): one workgroup
+//    orders the (sequence, query tile) pairs by decreasing tile index, i.e.
+//    by decreasing causal work, so the longest tiles start first;
+//  * k_sm_rope: q and k are rotated once (angles reduced in fp64), q is also
+//    multiplied by scale * log2(e), and both are rounded to bf16 into the
+//    workspace; every workgroup of the main kernel then reads ready operands;
+//  * k_sm_attn: one workgroup = one (128-query tile, head); streaming softmax
+//    over 64-key blocks.
+//
+// gfx950 design of k_sm_attn:
+//  * 4 waves x 32 queries; a wave's rotated Q stays in registers as MFMA
+//    operands for the whole key loop;
+//  * the score tile is produced transposed, S^T = K Q^T
+//    (v_mfma_f32_16x16x32_bf16), so each lane holds 4 keys of one query: the
+//    running max needs only two cross-lane steps and the running sum none
+//    (each lane sums its own keys; the four partial sums are added once at
+//    the end);
+//  * the k index of every MFMA is permuted so a lane's 8 slots are keys
+//    {32s + 4g + i, 32s + 16 + 4g + i}: that is the order in which two
+//    adjacent 16-key score tiles sit in a lane's accumulators, so the
+//    probabilities feed O^T += V^T P^T straight from registers, converted to
+//    bf16;
+//  * K and V blocks are double-buffered in LDS (one barrier per block); the
+//    next block's loads are in flight while the current one computes.  K is
+//    read along rows (two 8-byte pieces per lane, merged into one
+//    ds_read2_b64, row stride 132 elements: conflict-free), V with
+//    transposing reads (ds_read_b64_tr_b16, row stride 144);
+//  * scores are in log2 units (q carries log2(e)), so probabilities are one
+//    v_exp_f32 each; the output rescale by exp2(m_old - m_new) is skipped for
+//    a query tile when no lane's maximum moved;
+//  * two workgroups per CU (69 KB of LDS each); the blockIdx -> (tile, head)
+//    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
+//    head's K and V share that XCD's L2.
+#pragma once
+
+#include "la_device.h"
+
+namespace la {
+namespace sm {
+
+constexpr int D = 128;    // head dim
+constexpr int NT = 256;   // threads per workgroup of the main kernel
+constexpr int BQ = 128;   // queries per workgroup (4 waves x 32)
+constexpr int BN = 64;    // keys per K/V block
+constexpr int KSK = 132;  // LDS row stride of K (row reads)
+constexpr int KSV = 144;  // LDS row stride of V (transposing reads)
+constexpr int PADE = 8;   // elements after each LDS array (see the linear kernels)
+
+struct __attribute__((aligned(16))) Smem {
+    __attribute__((aligned(16))) uint16_t k[2][BN * KSK + PADE];
+    __attribute__((aligned(16))) uint16_t v[2][BN * KSV + PADE];
+};
+
+// ------------------------------------------------------------------ plan --
+
+// Exclusive prefix sum over the 1024 threads of a workgroup; returns the sum
+// of the values of lower threads and sets `total` to the sum over all.
+__device__ __forceinline__ int block_excl_scan(int x, int& total, int* wsum /* [16] LDS */) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        const int sw = wsum[w];
+        before += w < wave ? sw : 0;
+        all += sw;
+    }
+    __syncthreads();
+    total = all;
+    return before + inc - x;
+}
+
+// Orders the (sequence, query tile) pairs of a packed batch by decreasing
+// tile index (ties in any order: each pair's result does not depend on when
+// it runs).  Tile i of a sequence of length L exists for i < ceil(L / BQ)
+// (clamped to ntmax); the number of sequences with a tile i is
+// cnt[i] = #{s : n_s > i}, the tiles with index i occupy table entries
+// [off[i], off[i] + cnt[i]) with off[i] = sum of cnt[i'] over i' > i.
+// One workgroup of 1024 threads.  Workspace arrays: hist [ntmax + 1],
+// off and cursor [ntmax], tcu [nseq + 1].
+__global__ __launch_bounds__(1024) void k_sm_plan(const int32_t* __restrict__ cu, int nseq,
+                                                  int ntmax, int32_t* __restrict__ hist,
+                                                  int32_t* __restrict__ off,
+                                                  int32_t* __restrict__ cursor,
+                                                  int32_t* __restrict__ tcu,
+                                                  int2* __restrict__ table,
+                                                  int32_t* __restrict__ ecount) {
+    __shared__ int wsum[16];
+    const int tid = threadIdx.x;
+    for (int i = tid; i <= ntmax; i += 1024) {
+        hist[i] = 0;
+        if (i < ntmax) cursor[i] = 0;
+    }
+    __threadfence();
+    __syncthreads();
+    auto ntiles = [&](int s) {
+        const int L = cu[s + 1] - cu[s];
+        const int n = L > 0 ? (L + BQ - 1) / BQ : 0;
+        return n < ntmax ? n : ntmax;
+    };
+    for (int s = tid; s < nseq; s += 1024) atomicAdd(&hist[ntiles(s)], 1);
+    __threadfence();
+    __syncthreads();
+    // cnt and off in decreasing i: with r = ntmax - 1 - i, cnt = sum of
+    // hist[n] over n >= ntmax - r (inclusive scan of hist read backwards),
+    // off = exclusive scan of cnt in the same order.
+    int carry_c = 0, carry_o = 0;
+    for (int r0 = 0; r0 < ntmax; r0 += 1024) {
+        const int r = r0 + tid;
+        const int hv = r < ntmax ? __atomic_load_n(&hist[ntmax - r], __ATOMIC_RELAXED) : 0;
+        int tot;
+        const int c = carry_c + block_excl_scan(hv, tot, wsum) + hv;
+        carry_c += tot;
+        int tot2;
+        const int o = carry_o + block_excl_scan(r < ntmax ? c : 0, tot2, wsum);
+        carry_o += tot2;
+        if (r < ntmax) off[ntmax - 1 - r] = o;
+    }
+    // per-sequence tile offsets (sequence order) for the flat enumeration
+    int carry = 0;
+    for (int s0 = 0; s0 < nseq; s0 += 1024) {
+        const int s = s0 + tid;
+        const int n = s < nseq ? ntiles(s) : 0;
+        int tot;
+        const int e = carry + block_excl_scan(n, tot, wsum);
+        if (s < nseq) tcu[s] = e;
+        carry += tot;
+    }
+    if (tid == 0) {
+        tcu[nseq] = carry;
+        *ecount = carry;
+    }
+    __threadfence();
+    __syncthreads();
+    const int E = carry;
+    for (int f = tid; f < E; f += 1024) {
+        int lo = 0, hi = nseq;  // largest s with tcu[s] <= f
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (tcu[mid] <= f) lo = mid; else hi = mid;
+        }
+        const int i = f - tcu[lo];
+        const int slot = off[i] + atomicAdd(&cursor[i], 1);
+        table[slot] = make_int2(lo, i);
+    }
+}
+
+// ------------------------------------------------------------------ rope --
+
+// Rotary embedding, scale and bf16 rounding of q and k.  16 threads per token
+// (thread u owns 8 dimensions), grid-stride over tokens; for each token the
+// rotations are computed once and applied to its H query heads and Hkv key
+// heads.  Thread u < rot/16 rotates dimensions [8u, 8u+8) with their partners
+// [8u + rot/2, ...); threads with 8u >= rot copy (q: scale) their 8
+// dimensions; the rest have no dimensions of their own.  The angle
+// pos * theta_j is formed and reduced to [-pi, pi] in fp64, then sin and cos
+// are taken in fp32.  rot is a multiple of 16 in [0, 128].
+__global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
+                                                 const uint16_t* __restrict__ k,
+                                                 const int32_t* __restrict__ cu, int nseq, int T,
+                                                 int H, int Hkv, int rot, double log2_base,
+                                                 float qscale, uint16_t* __restrict__ qr,
+                                                 uint16_t* __restrict__ kr) {
+    __shared__ double theta[64];
+    if ((int)threadIdx.x < rot / 2)
+        theta[threadIdx.x] = exp2(-(2.0 * (double)threadIdx.x / (double)rot) * log2_base);
+    __syncthreads();
+    const int u = threadIdx.x & 15;
+    const int half = rot / 2;
+    const bool pair = 8 * u < half;
+    const bool plain = 8 * u >= rot;
+    const double two_pi = 6.283185307179586476925;
+    for (int64_t t = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); t < T;
+         t += (int64_t)gridDim.x * 16) {
+        float cs[8], sn[8];
+        if (pair) {
+            int lo = 0, hi = nseq;  // sequence of token t: largest s with cu[s] <= t
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (cu[mid] <= t) lo = mid; else hi = mid;
+            }
+            const double pos = (double)(t - cu[lo]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double a = pos * theta[8 * u + e];
+                const double r = a - two_pi * rint(a * (1.0 / two_pi));
+                sincosf((float)r, &sn[e], &cs[e]);
+            }
+        }
+        for (int row = 0; row < H + Hkv; ++row) {
+            const bool isq = row < H;
+            const size_t base = isq ? ((size_t)t * H + row) * D : ((size_t)t * Hkv + (row - H)) * D;
+            const uint16_t* src = (isq ? q : k) + base;
+            uint16_t* dst = (isq ? qr : kr) + base;
+            const float sc = isq ? qscale : 1.0f;
+            if (pair) {
+                const uint4 wa = *(const uint4*)(src + 8 * u);
+                const uint4 wb = *(const uint4*)(src + 8 * u + half);
+                const uint32_t a32[4] = {wa.x, wa.y, wa.z, wa.w};
+                const uint32_t b32[4] = {wb.x, wb.y, wb.z, wb.w};
+                uint32_t oa[4], ob[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float a0 = bf16_lo_to_f32(a32[p]), a1 = bf16_hi_to_f32(a32[p]);
+                    const float b0 = bf16_lo_to_f32(b32[p]), b1 = bf16_hi_to_f32(b32[p]);
+                    const float c0 = cs[2 * p], s0 = sn[2 * p], c1 = cs[2 * p + 1], s1 = sn[2 * p + 1];
+                    oa[p] = cvt_pk_bf16((a0 * c0 - b0 * s0) * sc, (a1 * c1 - b1 * s1) * sc);
+                    ob[p] = cvt_pk_bf16((b0 * c0 + a0 * s0) * sc, (b1 * c1 + a1 * s1) * sc);
+                }
+                *(uint4*)(dst + 8 * u) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+                *(uint4*)(dst + 8 * u + half) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+            } else if (plain) {
+                const uint4 w = *(const uint4*)(src + 8 * u);
+                const uint32_t w32[4] = {w.x, w.y, w.z, w.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    o[p] = cvt_pk_bf16(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc);
+                *(uint4*)(dst + 8 * u) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- attention --
+
+template <typename OutT>
+__device__ __forceinline__ void store_out4(OutT* p, f32x4_t v, float s);
+template <>
+__device__ __forceinline__ void store_out4<float>(float* p, f32x4_t v, float s) {
+    *(f32x4_t*)p = v * s;
+}
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, f32x4_t v, float s) {
+    *(uint2*)p = make_uint2(cvt_pk_bf16(v[0] * s, v[1] * s), cvt_pk_bf16(v[2] * s, v[3] * s));
+}
+
+// Operand of 32 head dimensions of one LDS row for the permuted k order:
+// columns {k0 + 4g + i, k0 + 16 + 4g + i}; the literal 16 lets the compiler
+// merge the two 8-byte reads into one ds_read2_b64.
+__device__ __forceinline__ bf16x8_t k_operand(const uint16_t* tile, int row, int k0, int g) {
+    const uint16_t* p = tile + row * KSK + k0 + 4 * g;
+    return as_bf16x8(lds_read8(p), lds_read8(p + 16));
+}
+
+// Operand over 32 keys (rows of the row-major V tile) for the permuted k
+// order: lane (g, c) gets column c0 + c, rows {r0 + 4g + i, r0 + 16 + 4g + i}.
+__device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int c0, int g, int c) {
+    return as_bf16x8(lds_read_tr4(tile, KSV, r0 + 4 * g, c0, c),
+                     lds_read_tr4(tile, KSV, r0 + 16 + 4 * g, c0, c));
+}
+
+// One (128-query tile, query head) of causal softmax attention.
+//   qr [T, H, D] bf16: rotated q times scale * log2(e); kr [T, Hkv, D] bf16:
+//   rotated k; v [T, Hkv, D] bf16; out [T, H, D]; lse [T, H] (natural log)
+//   or null.  table/ecount: the plan (null for a single sequence, whose
+//   tiles then run last tile first).
+template <typename OutT>
+__global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ qr,
+                                                   const uint16_t* __restrict__ kr,
+                                                   const uint16_t* __restrict__ v,
+                                                   const int32_t* __restrict__ cu,
+                                                   const int2* __restrict__ table,
+                                                   const int32_t* __restrict__ ecount, int H,
+                                                   int Hkv, OutT* __restrict__ out,
+                                                   float* __restrict__ lse) {
+    __shared__ Smem sm;
+    const int G = H / Hkv;
+    const int b = blockIdx.x;
+    const int hk = b % Hkv;
+    const int rest = b / Hkv;
+    const int h = hk * G + rest % G;
+    const int e = rest / G;
+    int s, ti;
+    if (table == nullptr) {
+        const int L0 = cu[1] - cu[0];
+        const int nt = (L0 + BQ - 1) / BQ;
+        if (e >= nt) return;
+        s = 0;
+        ti = nt - 1 - e;
+    } else {
+        if (e >= *ecount) return;
+        const int2 it = table[e];
+        s = it.x;
+        ti = it.y;
+    }
+    const int start = cu[s];
+    const int L = cu[s + 1] - start;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c = lane & 15;
+    const int q0 = ti * BQ;
+    if (q0 >= L) return;  // (only if a length exceeds the plan's bound)
+    const int kv_end = min(L, q0 + BQ);
+    const int nblk = (kv_end + BN - 1) / BN;
+    const int wq0 = q0 + 32 * wave;          // this wave's first query
+    const bool has_q = wq0 < L;
+    const int wq_last = min(wq0 + 31, L - 1);
+
+    // Q^T operands: lane (g, c) holds query wq0 + 16 qt + c, dimensions
+    // {32 kk + 4g + i, 32 kk + 16 + 4g + i}.
+    bf16x8_t Qf[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        const int row = wq0 + 16 * qt + c;
+        const uint16_t* p = qr + ((size_t)(start + row) * H + h) * D + 4 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            i16x4_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+            if (row < L) {
+                lo = *(const i16x4_t*)(p + 32 * kk);
+                hi = *(const i16x4_t*)(p + 32 * kk + 16);
+            }
+            Qf[qt][kk] = as_bf16x8(lo, hi);
+        }
+    }
+
+    f32x4_t O[8][2];
+#pragma unroll
+    for (int ft = 0; ft < 8; ++ft)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) O[ft][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-1e30f, -1e30f};
+    float l[2] = {0.f, 0.f};
+
+    // staging: thread tid moves rows (tid >> 4) + 16 j, dimensions
+    // (tid & 15) * 8 .. + 7 of the 64-key block; keys at or past kv_end
+    // (after every query of the tile, so masked) are zeros.
+    const size_t rs = (size_t)Hkv * D;
+    const uint16_t* kb = kr + ((size_t)start * Hkv + hk) * D + (tid & 15) * 8;
+    const uint16_t* vb = v + ((size_t)start * Hkv + hk) * D + (tid & 15) * 8;
+    uint4 rk[4], rv[4];
+    auto load_kv = [&](int blk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = blk * BN + (tid >> 4) + 16 * j;
+            if (key < kv_end) {
+                rk[j] = *(const uint4*)(kb + (size_t)key * rs);
+                rv[j] = *(const uint4*)(vb + (size_t)key * rs);
+            } else {
+                rk[j] = make_uint4(0u, 0u, 0u, 0u);
+                rv[j] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    auto store_kv = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = (tid >> 4) + 16 * j;
+            uint2* pk = (uint2*)(sm.k[buf] + r * KSK + (tid & 15) * 8);
+            pk[0] = make_uint2(rk[j].x, rk[j].y);
+            pk[1] = make_uint2(rk[j].z, rk[j].w);
+            *(uint4*)(sm.v[buf] + r * KSV + (tid & 15) * 8) = rv[j];
+        }
+    };
+
+    load_kv(0);
+    store_kv(0);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int buf = blk & 1;
+        if (blk + 1 < nblk) load_kv(blk + 1);
+        const int kb0 = blk * BN;
+        if (has_q && kb0 <= wq_last) {
+            // S^T tiles: Sc[kt][qt], lane (g, c) = query wq0 + 16 qt + c,
+            // keys kb0 + 16 kt + 4g + i.
+            f32x4_t Sc[4][2];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) Sc[kt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const uint16_t* kt_ = sm.k[buf];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const bf16x8_t A = k_operand(kt_, 16 * kt + c, 32 * kk, g);
+#pragma unroll
+                    for (int qt = 0; qt < 2; ++qt)
+                        Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk], Sc[kt][qt]);
+                }
+            if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const int qi = wq0 + 16 * qt + c;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (kb0 + 16 * kt + 4 * g + i > qi) Sc[kt][qt][i] = -INFINITY;
+                }
+            }
+            // streaming softmax (log2 units)
+            bool moved = false;
+            float alpha[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+                float mx = Sc[0][qt][0];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, Sc[kt][qt][i]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mn = fmaxf(m[qt], mx);
+                alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);
+                moved |= mn > m[qt];
+                m[qt] = mn;
+                float ls = 0.f;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - mn);
+                        Sc[kt][qt][i] = p;
+                        ls += p;
+                    }
+                l[qt] = l[qt] * alpha[qt] + ls;
+            }
+            if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                for (int ft = 0; ft < 8; ++ft)
+#pragma unroll
+                    for (int qt = 0; qt < 2; ++qt) O[ft][qt] *= alpha[qt];
+            }
+            // P^T operands: keys {32 ks + 4g + i} from tile 2ks, {32 ks + 16 + 4g + i}
+            // from tile 2ks + 1.
+            bf16x8_t Pf[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const f32x4_t a = Sc[2 * ks][qt], bq = Sc[2 * ks + 1][qt];
+                    Pf[ks][qt] = as_bf16x8(make_uint4(cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]),
+                                                      cvt_pk_bf16(bq[0], bq[1]),
+                                                      cvt_pk_bf16(bq[2], bq[3])));
+                }
+            const uint16_t* vt_ = sm.v[buf];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int ft = 0; ft < 8; ++ft) {
+                    const bf16x8_t A = v_operand(vt_, 32 * ks, 16 * ft, g, c);
+#pragma unroll
+                    for (int qt = 0; qt < 2; ++qt) O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
+                }
+        }
+        if (blk + 1 < nblk) store_kv(buf ^ 1);
+        __syncthreads();
+    }
+
+    // normalise and store: lane (g, c) holds features 16 ft + 4g + i of query
+    // wq0 + 16 qt + c.
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        float lt = l[qt] + __shfl_xor(l[qt], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int row = wq0 + 16 * qt + c;
+        if (row < L) {
+            const float inv = 1.0f / lt;
+            OutT* op = out + ((size_t)(start + row) * H + h) * D + 4 * g;
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) store_out4<OutT>(op + 16 * ft, O[ft][qt], inv);
+            if (lse != nullptr && g == 0)
+                lse[(size_t)(start + row) * H + h] = (m[qt] + __log2f(lt)) * 0.69314718055994530942f;
+        }
+    }
+}
+
+}  // namespace sm
+}  // namespace la

@@ -18,6 +18,10 @@ Recipe (every workload):
   * variable lengths: numpy ``PCG64`` seeded with ``seed``, lengths
     ``round(exp(U(ln 1024, ln 131072)))`` drawn until their sum reaches the
     target; the last one is clipped to the remainder.
+  * softmax-layer workloads (kind "softmax"): q [T, H, d], k and v
+    [T, Hkv, d], N(0,1) in bf16 (unit-spread scores after the 1/sqrt(d)
+    scale), index order q=0, k=1, v=2; packed lengths as above, drawn with
+    the seed of the linear-attention workload of the same packing.
 """
 from __future__ import annotations
 
@@ -87,6 +91,24 @@ WORKLOADS = {
                                 state_std=0.01, gen_device="cuda",
                                 note="serving step, 64 decode tokens + a 32704-token prompt "
                                      "chunk, H=8 d=128, gated, state pool N(0,0.01)"),
+    # the softmax attention layer of the hybrid model on the same shapes:
+    # one GPU's 8 heads, rotary embedding on half of d = 128, the
+    # long-context base 1e7, Hkv = H
+    "softmax_32k": Workload("softmax_32k", "softmax", 1008, H=8, d=128, dtype="bf16", T=32768,
+                            extra={"Hkv": 8, "rotary_dim": 64, "rope_base": 1e7},
+                            note="softmax layer, bf16, T=32768 H=8 Hkv=8 d=128, RoPE on 64 "
+                                 "dims, base 1e7"),
+    "softmax_varlen_512k": Workload("softmax_varlen_512k", "softmax", 1009, H=8, d=128,
+                                    dtype="bf16", total_T=524288, gen_device="cuda",
+                                    extra={"Hkv": 8, "rotary_dim": 64, "rope_base": 1e7,
+                                           "length_seed": 1004},
+                                    note="softmax layer, bf16 packed, lengths of varlen_512k, "
+                                         "H=8 Hkv=8 d=128, RoPE on 64 dims, base 1e7"),
+    "softmax_1m": Workload("softmax_1m", "softmax", 1010, H=8, d=128, dtype="bf16", T=1048576,
+                           gen_device="cuda",
+                           extra={"Hkv": 8, "rotary_dim": 64, "rope_base": 1e7},
+                           note="softmax layer, bf16, T=1048576 H=8 Hkv=8 d=128, RoPE on 64 "
+                                "dims, base 1e7"),
 }
 
 
@@ -197,3 +219,22 @@ def decode_token(w: Workload, step: int, N: int | None = None, H: int | None = N
         t.mul_(float(w.scale))
     t = t.to(dt)
     return t[0], t[1], t[2]
+
+
+def softmax_inputs(w: Workload, device: str | None = None, Hkv: int | None = None):
+    """q [total, H, d], k and v [total, Hkv, d] (bf16) and cu_seqlens (int32,
+    CPU) of a softmax-layer workload: one sequence of w.T tokens, or the
+    packed lengths of ``extra["length_seed"]`` summing to w.total_T."""
+    dev = w.gen_device if device is None else device
+    dt = DTYPES[w.dtype]
+    Hkv = w.extra.get("Hkv", w.H) if Hkv is None else Hkv
+    if w.total_T:
+        total = w.total_T
+        cu = cu_from_lengths(varlen_lengths(w.extra.get("length_seed", w.seed), total))
+    else:
+        total = w.T
+        cu = torch.tensor([0, total], dtype=torch.int32)
+    q = normal((total, w.H, w.d), w.seed, 0, w.scale, dt, dev)
+    k = normal((total, Hkv, w.d), w.seed, 1, w.scale, dt, dev)
+    v = normal((total, Hkv, w.d), w.seed, 2, w.scale, dt, dev)
+    return q, k, v, cu

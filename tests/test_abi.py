@@ -1,5 +1,6 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/la.h declares, and rejects invalid calls on the host.
+include/la.h and include/la_softmax.h declare, and rejects invalid calls on
+the host.
 
 Every call below fails host validation, so none of them reaches a HIP call;
 the fake device addresses are never dereferenced.
@@ -13,7 +14,7 @@ import pytest
 from linear_attention_long_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "la.h")
+HEADERS = [os.path.join(ROOT, "include", "la.h"), os.path.join(ROOT, "include", "la_softmax.h")]
 
 F32, BF16 = _lib.LA_DTYPE_F32, _lib.LA_DTYPE_BF16
 INVALID, UNSUPPORTED, WS_SMALL = (_lib.LA_ERR_INVALID_ARGUMENT, _lib.LA_ERR_UNSUPPORTED,
@@ -34,7 +35,7 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+[\s\*]+(la_[a-z_]+)\s*\(", text, re.M)))
 
 
@@ -200,3 +201,66 @@ def test_decode_rejects_bad_arguments(lib):
     g = opt(gated=1)
     assert call(o=g, x=A[6], odt=BF16) == INVALID        # bf16 gated output needs workspace
     assert call(o=g, x=A[6], odt=BF16, ws=A[7], wsb=16) == WS_SMALL
+
+
+def test_softmax_default_options(lib):
+    o = lib.la_softmax_default_options()
+    assert (o.rotary_dim, o.rope_base, o.scale, o.n_timing) == (-1, 10000.0, 0.0, 0)
+
+
+def test_softmax_workspace_bytes(lib):
+    o = _lib.softmax_options()
+    # one sequence: rotated q and k only (bf16), each rounded up to 256 bytes
+    assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
+                                          ctypes.byref(o)) == 1000 * 4 * 256 + 1000 * 2 * 256
+    # packed: plus the count, the order table and the plan's arrays
+    nb = lib.la_softmax_workspace_bytes(3, 1000, 600, 4, 4, 128, BF16, BF16, ctypes.byref(o))
+    assert nb > 2 * 1000 * 4 * 256
+    assert lib.la_softmax_workspace_bytes(1, 0, 0, 4, 4, 128, BF16, F32, ctypes.byref(o)) == 0
+    # rejected arguments report SIZE_MAX
+    assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 3, 128, BF16, F32, ctypes.byref(o)) == SIZE_MAX
+    assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 64, BF16, F32, ctypes.byref(o)) == SIZE_MAX
+    assert lib.la_softmax_workspace_bytes(1, 16, 17, 4, 4, 128, BF16, F32, ctypes.byref(o)) == SIZE_MAX
+    # the base is not used (nor checked) without rotation
+    o0 = _lib.softmax_options(rotary_dim=0, rope_base=0.0)
+    assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o0)) > 0
+    o1 = _lib.softmax_options(rope_base=0.0)
+    assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o1)) == SIZE_MAX
+
+
+def test_softmax_rejects_bad_arguments(lib):
+    def call(q=A[0], k=A[1], v=A[2], cu=A[9], nseq=2, total=100, maxlen=60, H=4, Hkv=2, d=128,
+             idt=BF16, odt=F32, out=A[3], lse=None, ws=A[8], wsb=1 << 40, **kw):
+        o = _lib.softmax_options(**kw)
+        return lib.la_softmax_attention_varlen(q, k, v, cu, nseq, total, maxlen, H, Hkv, d, idt,
+                                               odt, out, lse, ctypes.byref(o), ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(q=ctypes.c_void_p(0x10000008)) == INVALID          # misaligned
+    assert call(nseq=0) == INVALID
+    assert call(total=-1) == INVALID
+    assert call(maxlen=101) == INVALID                             # above total_T
+    assert call(maxlen=0) == INVALID                               # tokens but no length bound
+    assert call(Hkv=3) == INVALID                                  # does not divide H
+    assert call(H=0) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(idt=F32) == UNSUPPORTED
+    assert call(idt=7) == INVALID
+    assert call(H=1 << 14, Hkv=1) == UNSUPPORTED                   # H*d past 2^20
+    assert call(rotary_dim=3) == INVALID
+    assert call(rotary_dim=130) == INVALID
+    assert call(rotary_dim=24) == UNSUPPORTED                      # not a multiple of 16
+    assert call(rope_base=0.0) == INVALID
+    assert call(rope_base=float("inf")) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(out=A[0]) == INVALID                               # out overlaps q
+    assert call(lse=ctypes.c_void_p(A[3].value + 64)) == INVALID   # lse overlaps out
+    assert call(ws=None) == INVALID
+    assert call(ws=ctypes.c_void_p(0x10000010)) == INVALID         # workspace not 256-aligned
+    need = lib.la_softmax_workspace_bytes(2, 100, 60, 4, 2, 128, BF16, F32,
+                                          ctypes.byref(_lib.softmax_options()))
+    assert call(wsb=need - 1) == WS_SMALL
+    # an empty batch is accepted with no pointers and launches nothing
+    assert call(q=None, k=None, v=None, cu=None, out=None, total=0, maxlen=0, ws=None, wsb=0) == 0

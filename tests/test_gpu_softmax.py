@@ -1,0 +1,210 @@
+"""GPU parity of the softmax attention layer (include/la_softmax.h) against
+its CPU oracle (oracle/softmax.py), element by element on seeded inputs.
+
+Method: page "六十四：MiniMax-01" sections 2-3 (softmax(QK^T/sqrt(d))V),
+page "MiniMax-Text-01 405B MoE模型架构与训练策略解析" sections 2.2 and 4.1
+(rotary embedding on half the dimensions, bases 1e4 / 5e6 / 1e7), page
+"MiniMax-01系列大模型：超长上下文与多模态能力深度解析与部署指南" section 2.1.3
+(packed variable-length sequences).
+
+Tolerance.  The kernel rounds the rotated, scaled q and the rotated k to
+bf16 (unit roundoff u = 2^-8) and the probabilities to bf16 before the
+product with V; everything else is fp32.  For scores of unit spread
+(q, k ~ N(0,1), scale 1/sqrt(d)) a score's error has rms about
+u * sqrt(2d/3) / sqrt(d) = 3.2e-3, a probability's rounding u / sqrt(3) =
+2.3e-3, and an output element, a weighted mean of value rows, errs by about
+sqrt(3.2e-3^2 + 2.3e-3^2) * rms(v) = 4e-3 rms(v) at most (rows with one or
+two keys), far less for long rows.  Five standard deviations over ~1e6
+elements: max|err| <= 2e-2 * rms(v), the bound used below; lse (a weighted
+mean of the score errors) within 1e-2.  The output is compared against the
+value scale, not its own rms: a row's output shrinks like sqrt(sum p^2) as
+its keys grow while its first rows keep the full value scale.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_long_amd import api, inputs
+from oracle import softmax as SO
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+LSE_TOL = 1e-2
+DEV = "cuda"
+
+
+def bf16_normal(shape, seed, std=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(torch.bfloat16)
+
+
+def packed(lengths, H, Hkv, seed, d=128, qstd=1.0):
+    T = int(sum(lengths))
+    q = bf16_normal((T, H, d), seed, qstd)
+    k = bf16_normal((T, Hkv, d), seed + 1)
+    v = bf16_normal((T, Hkv, d), seed + 2)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    return q, k, v, cu
+
+
+def run(q, k, v, cu, max_seqlen=None, **kw):
+    max_seqlen = int((cu[1:] - cu[:-1]).max()) if max_seqlen is None else max_seqlen
+    out, lse = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV),
+                                               max_seqlen, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def check(got, ref, v, lse=None, lref=None, tol=TOL):
+    vs = float(np.sqrt(np.mean(v.double().numpy() ** 2)))
+    err = float(np.abs(got - ref).max()) / vs
+    assert np.all(np.isfinite(got))
+    assert err <= tol, "max|err|/rms(v) = %.3e" % err
+    if lse is not None:
+        lerr = float(np.abs(lse - lref).max())
+        assert lerr <= LSE_TOL, "lse max|err| = %.3e" % lerr
+    return err
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (4, 2), (8, 1)])
+def test_packed_ragged_lengths(H, Hkv):
+    # empty, single-token, tile-ragged (127/128/129) and multi-tile sequences
+    lengths = [0, 1, 127, 128, 129, 300, 64, 65, 0, 1000]
+    q, k, v, cu = packed(lengths, H, Hkv, 11 + H + Hkv)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e4)
+    ref, lref = SO.attention(q, k, v, cu, rope_base=1e4)
+    print("packed H=%d Hkv=%d: max|err|/rms(v) %.2e" % (H, Hkv, check(got, ref, v, lse, lref)))
+
+
+@pytest.mark.parametrize("rot,base,odt", [(0, 1e4, torch.float32), (32, 5e6, torch.bfloat16),
+                                          (128, 1e7, torch.float32), (64, 1e7, torch.bfloat16),
+                                          (16, 1e4, torch.bfloat16)])
+def test_rotary_dims_bases_and_output_dtypes(rot, base, odt):
+    lengths = [700, 1, 333]
+    q, k, v, cu = packed(lengths, 2, 2, 21 + rot)
+    got, lse = run(q, k, v, cu, out_dtype=odt, rotary_dim=rot, rope_base=base)
+    ref, lref = SO.attention(q, k, v, cu, rotary_dim=rot, rope_base=base)
+    # a bf16 output adds its own rounding, u * |out| <= 2^-8 * max|v|
+    check(got, ref, v, lse, lref, tol=TOL + (2.0 ** -8 * 5 if odt == torch.bfloat16 else 0))
+
+
+def test_scale_option_and_wider_score_spread():
+    # scores of spread ~2 (q std 2): the rounding error of the scores doubles
+    q, k, v, cu = packed([513, 255], 2, 1, 31, qstd=2.0)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, scale=0.05)
+    ref, lref = SO.attention(q, k, v, cu, scale=0.05)
+    check(got, ref, v, lse, lref)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32)
+    ref, lref = SO.attention(q, k, v, cu)
+    vs = float(np.sqrt(np.mean(v.double().numpy() ** 2)))
+    assert float(np.abs(got - ref).max()) / vs <= 2 * TOL
+    assert float(np.abs(lse - lref).max()) <= 2 * LSE_TOL
+
+
+def test_single_sequence_sampled_rows():
+    # one sequence (no ordering pass: tiles run last first), 4096 tokens;
+    # every row of the first and last tiles and 200 random rows in between
+    T, H = 4096, 4
+    q, k, v, cu = packed([T], H, H, 41)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7)
+    r = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(T - 128, T),
+                                     r.integers(0, T, 200)]))
+    rr = np.repeat(rows, H)
+    hh = np.tile(np.arange(H), len(rows))
+    ref, lref = SO.attention(q, k, v, cu, rope_base=1e7, rows=rr, heads=hh)
+    check(got[rr, hh], ref, v, lse[rr, hh], lref)
+
+
+def test_many_short_sequences():
+    # 600 sequences of 1..200 tokens: the ordering pass places ~1000 tiles
+    r = np.random.default_rng(3)
+    lengths = r.integers(1, 201, 600)
+    q, k, v, cu = packed(lengths, 2, 1, 51)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32)
+    ref, lref = SO.attention(q, k, v, cu)
+    check(got, ref, v, lse, lref)
+
+
+def test_max_seqlen_above_the_longest_and_repeat_is_identical():
+    q, k, v, cu = packed([200, 90], 2, 2, 61)
+    a, la = run(q, k, v, cu, max_seqlen=290, out_dtype=torch.float32)
+    b, lb = run(q, k, v, cu, max_seqlen=290, out_dtype=torch.float32)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+    ref, lref = SO.attention(q, k, v, cu)
+    check(a, ref, v, la, lref)
+
+
+def test_empty_batch_is_a_no_op():
+    q = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device=DEV)
+    cu = torch.zeros(3, dtype=torch.int32, device=DEV)
+    out, lse = api.la_softmax_attention_varlen(q, q, q, cu, 0, return_lse=True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 128) and lse.shape == (0, 2)
+
+
+def oracle_rows(q, k, v, cu, rows, heads, rot, base):
+    """Oracle at (token, head) pairs of a long input: each pair's sequence
+    prefix and its key/value head only, widened to fp64 one slice at a time."""
+    cu = np.asarray(cu, dtype=np.int64)
+    H, Hkv = q.shape[1], k.shape[1]
+    out = np.zeros((len(rows), q.shape[2]))
+    lse = np.zeros(len(rows))
+    groups = {}
+    for i, (t, h) in enumerate(zip(rows, heads)):
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        groups.setdefault((s, int(h)), []).append(i)
+    for (s, h), idx in groups.items():
+        a = int(cu[s])
+        hk = h // (H // Hkv)
+        end = max(int(rows[i]) for i in idx) + 1
+        o, l = SO.attention(q[a:end, h:h + 1].cpu(), k[a:end, hk:hk + 1].cpu(),
+                            v[a:end, hk:hk + 1].cpu(), None, rotary_dim=rot, rope_base=base,
+                            rows=[int(rows[i]) - a for i in idx], heads=[0] * len(idx))
+        out[idx] = o
+        lse[idx] = l
+    return out, lse
+
+
+def sample_pairs(cu, H, n, seed):
+    """(token, head) pairs: each sequence's first and last token, tokens at
+    tile edges of the longest sequence, and random tokens."""
+    r = np.random.default_rng(seed)
+    cu = np.asarray(cu, dtype=np.int64)
+    toks = []
+    for s in range(len(cu) - 1):
+        if cu[s + 1] > cu[s]:
+            toks += [cu[s], cu[s + 1] - 1]
+    s_long = int(np.argmax(cu[1:] - cu[:-1]))
+    for e in (127, 128, 129, 4095, 4096):
+        if cu[s_long] + e < cu[s_long + 1]:
+            toks.append(cu[s_long] + e)
+    toks += list(r.integers(0, cu[-1], n))
+    toks = np.array(toks, dtype=np.int64)
+    heads = r.integers(0, H, len(toks))
+    return toks, heads
+
+
+@pytest.mark.parametrize("name", ["softmax_32k", "softmax_varlen_512k"])
+def test_workload_sampled(name):
+    w = inputs.WORKLOADS[name]
+    q, k, v, cu = inputs.softmax_inputs(w, device=DEV)
+    rot, base = w.extra["rotary_dim"], w.extra["rope_base"]
+    maxlen = int((cu[1:] - cu[:-1]).max())
+    out, lse = api.la_softmax_attention_varlen(q, k, v, cu.to(DEV), maxlen, rotary_dim=rot,
+                                               rope_base=base, out_dtype=torch.float32,
+                                               return_lse=True)
+    torch.cuda.synchronize()
+    rows, heads = sample_pairs(cu.numpy(), w.H, 48, 5)
+    got = out[torch.from_numpy(rows).to(DEV), torch.from_numpy(heads).to(DEV)].double().cpu().numpy()
+    gl = lse[torch.from_numpy(rows).to(DEV), torch.from_numpy(heads).to(DEV)].double().cpu().numpy()
+    ref, lref = oracle_rows(q, k, v, cu.numpy(), rows, heads, rot, base)
+    vs = float(torch.sqrt(torch.mean(v.float() ** 2)))
+    err = float(np.abs(got - ref).max()) / vs
+    lerr = float(np.abs(gl - lref).max())
+    print("%s: %d sampled rows, max|err|/rms(v) %.2e, lse %.2e" % (name, len(rows), err, lerr))
+    assert err <= TOL and lerr <= LSE_TOL
