@@ -26,9 +26,11 @@
 //    operands for the whole key loop;
 //  * the score tile is produced transposed, S^T = K Q^T
 //    (v_mfma_f32_16x16x32_bf16), so each lane holds 4 keys of one query: the
-//    running max needs only two cross-lane steps and the running sum none
-//    (each lane sums its own keys; the four partial sums are added once at
-//    the end);
+//    running max needs only two cross-lane steps;
+//  * the running sum of the probabilities comes from the matrix cores: an
+//    all-ones operand times P^T gives each query's sum of the same
+//    bf16-rounded weights that multiply V (no vector adds, and numerator and
+//    denominator agree);
 //  * the k index of every MFMA is permuted so a lane's 8 slots are keys
 //    {32s + 4g + i, 32s + 16 + 4g + i}: that is the order in which two
 //    adjacent 16-key score tiles sit in a lane's accumulators, so the
@@ -40,8 +42,11 @@
 //    ds_read2_b64, row stride 132 elements: conflict-free), V with
 //    transposing reads (ds_read_b64_tr_b16, row stride 144);
 //  * scores are in log2 units (q carries log2(e)), so probabilities are one
-//    v_exp_f32 each; the output rescale by exp2(m_old - m_new) is skipped for
-//    a query tile when no lane's maximum moved;
+//    v_exp_f32 each; the reference maximum m of a query is raised only when a
+//    score exceeds it by more than 8 (probabilities then stay below 2^8), so
+//    the rescale of the accumulators by exp2(m_old - m_new) is rare;
+//  * K and V blocks arrive through buffer loads whose range ends at the
+//    tile's last key (zeros past it, no per-lane bounds arithmetic);
 //  * two workgroups per CU (69 KB of LDS each); the blockIdx -> (tile, head)
 //    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
 //    head's K and V share that XCD's L2.
@@ -335,32 +340,47 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
         }
     }
 
-    f32x4_t O[8][2];
+    // O^T accumulators; Lc[qt] is the row sum of the bf16 probabilities,
+    // produced by the matrix cores from an all-ones operand (every row of a
+    // lane's 4 holds the same sum), so numerator and denominator see the
+    // same rounded weights.
+    f32x4_t O[8][2], Lc[2];
 #pragma unroll
-    for (int ft = 0; ft < 8; ++ft)
+    for (int qt = 0; qt < 2; ++qt) {
+        Lc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) O[ft][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int ft = 0; ft < 8; ++ft) O[ft][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    // Reference maximum per query (log2 units).  Probabilities are exp2(s - m)
+    // with m raised only when a score exceeds it by more than kLazy, so the
+    // accumulators are rescaled rarely; they stay below 2^kLazy.
+    constexpr float kLazy = 8.0f;
     float m[2] = {-1e30f, -1e30f};
-    float l[2] = {0.f, 0.f};
 
     // staging: thread tid moves rows (tid >> 4) + 16 j, dimensions
-    // (tid & 15) * 8 .. + 7 of the 64-key block; keys at or past kv_end
-    // (after every query of the tile, so masked) are zeros.
-    const size_t rs = (size_t)Hkv * D;
-    const uint16_t* kb = kr + ((size_t)start * Hkv + hk) * D + (tid & 15) * 8;
-    const uint16_t* vb = v + ((size_t)start * Hkv + hk) * D + (tid & 15) * 8;
+    // (tid & 15) * 8 .. + 7 of the 64-key block through buffer loads whose
+    // range ends at kv_end: keys past it (after every query of the tile,
+    // so masked) read as zeros.
+    const uint32_t rs = (uint32_t)(Hkv * D);
+    const uint16_t* kseq = kr + ((size_t)start * Hkv + hk) * D;
+    const uint16_t* vseq = v + ((size_t)start * Hkv + hk) * D;
+    const uint32_t voff = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
     uint4 rk[4], rv[4];
     auto load_kv = [&](int blk) {
+        const int nvalid = kv_end - blk * BN;
+        const int32_t bytes = (int32_t)((uint32_t)(min(nvalid, BN) - 1) * rs * 2u + 2u * D);
+        const size_t base = (size_t)blk * BN * rs;
+        const __amdgpu_buffer_rsrc_t rsk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kseq + base), (short)0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vseq + base), (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int key = blk * BN + (tid >> 4) + 16 * j;
-            if (key < kv_end) {
-                rk[j] = *(const uint4*)(kb + (size_t)key * rs);
-                rv[j] = *(const uint4*)(vb + (size_t)key * rs);
-            } else {
-                rk[j] = make_uint4(0u, 0u, 0u, 0u);
-                rv[j] = make_uint4(0u, 0u, 0u, 0u);
-            }
+            rk[j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsk, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
+            rv[j] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
         }
     };
     auto store_kv = [&](int buf) {
@@ -385,13 +405,16 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
             // S^T tiles: Sc[kt][qt], lane (g, c) = query wq0 + 16 qt + c,
             // keys kb0 + 16 kt + 4g + i.
             f32x4_t Sc[4][2];
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) Sc[kt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             const uint16_t* kt_ = sm.k[buf];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+            for (int kt = 0; kt < 4; ++kt) {
+                const bf16x8_t A = k_operand(kt_, 16 * kt + c, 0, g);
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt)
+                    Sc[kt][qt] = mfma16x16x32(A, Qf[qt][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int kk = 1; kk < 4; ++kk)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     const bf16x8_t A = k_operand(kt_, 16 * kt + c, 32 * kk, g);
@@ -411,38 +434,37 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
                 }
             }
             // streaming softmax (log2 units)
-            bool moved = false;
-            float alpha[2];
+            float mx[2];
+            bool raise = false;
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                float mx = Sc[0][qt][0];
+                float x = Sc[0][qt][0];
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, Sc[kt][qt][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mn = fmaxf(m[qt], mx);
-                alpha[qt] = __builtin_amdgcn_exp2f(m[qt] - mn);
-                moved |= mn > m[qt];
-                m[qt] = mn;
-                float ls = 0.f;
+                    for (int i = 0; i < 4; ++i) x = fmaxf(x, Sc[kt][qt][i]);
+                x = fmaxf(x, __shfl_xor(x, 16, 64));
+                mx[qt] = fmaxf(x, __shfl_xor(x, 32, 64));
+                raise |= mx[qt] > m[qt] + kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) {
+                    const float mn = mx[qt] > m[qt] + kLazy ? mx[qt] : m[qt];
+                    const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
+                    m[qt] = mn;
+                    Lc[qt] *= alpha;
+#pragma unroll
+                    for (int ft = 0; ft < 8; ++ft) O[ft][qt] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float p = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - mn);
-                        Sc[kt][qt][i] = p;
-                        ls += p;
-                    }
-                l[qt] = l[qt] * alpha[qt] + ls;
-            }
-            if (__builtin_amdgcn_ballot_w64(moved)) {
-#pragma unroll
-                for (int ft = 0; ft < 8; ++ft)
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) O[ft][qt] *= alpha[qt];
-            }
+                    for (int i = 0; i < 4; ++i)
+                        Sc[kt][qt][i] = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - m[qt]);
             // P^T operands: keys {32 ks + 4g + i} from tile 2ks, {32 ks + 16 + 4g + i}
             // from tile 2ks + 1.
             bf16x8_t Pf[2][2];
@@ -457,13 +479,16 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
                 }
             const uint16_t* vt_ = sm.v[buf];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
                 for (int ft = 0; ft < 8; ++ft) {
                     const bf16x8_t A = v_operand(vt_, 32 * ks, 16 * ft, g, c);
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt) O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
                 }
+#pragma unroll
+                for (int qt = 0; qt < 2; ++qt) Lc[qt] = mfma16x16x32(ones, Pf[ks][qt], Lc[qt]);
+            }
         }
         if (blk + 1 < nblk) store_kv(buf ^ 1);
         __syncthreads();
@@ -473,8 +498,7 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
     // wq0 + 16 qt + c.
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        float lt = l[qt] + __shfl_xor(l[qt], 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
+        const float lt = Lc[qt][0];
         const int row = wq0 + 16 * qt + c;
         if (row < L) {
             const float inv = 1.0f / lt;
