@@ -6,8 +6,11 @@ One step = one gated bf16 prefill of the long-context workload
 feature map, blocking, chunk states and prefix, intra- and inter-block
 products, state carry and the fused gate, i.e. every stage of the path, on
 seeded synthetic inputs already resident in HBM.  The same run also times
-the decode step (64 sequences x 64 heads x d=128, fp32 state, 1000 steps)
-and the CPU oracle on a bounded sample of the prefill workload.
+the decode step (64 sequences x 64 heads x d=128, fp32 state, 1000 steps),
+the CPU oracle on a bounded sample of the prefill workload, and the hybrid
+model's softmax attention layer (32K tokens, a packed 512K-token batch and
+1M tokens; 8 heads, rotary embedding on half of d = 128) with its own
+matrix-core roofline and oracle baseline under "softmax_layer".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line on stdout; progress goes to stderr.
@@ -384,6 +387,103 @@ def bench_serving(args, torch, api, inputs, reps=50):
     return res
 
 
+SOFTMAX_WORKLOADS = (("softmax_32k", 20), ("softmax_varlen_512k", 5), ("softmax_1m", 2))
+
+
+def softmax_flops(cu):
+    """Algorithmic flops of causal attention per head-independent unit: QK^T and
+    P V over the d features for every (query, key <= query) pair of each
+    sequence, 4 d flops per pair and head."""
+    L = (cu[1:] - cu[:-1]).to(dtype=__import__("torch").int64)
+    return int((L * (L + 1) // 2).sum())
+
+
+def bench_softmax(args, torch, lib, _lib, inputs):
+    """The hybrid model's softmax attention layer (include/la_softmax.h) on its
+    workloads: per-kernel times from HIP events on the call's stream."""
+    res = {}
+    for name, reps in SOFTMAX_WORKLOADS:
+        if name == "softmax_1m" and args.no_softmax_1m:
+            continue
+        w = inputs.WORKLOADS[name]
+        q, k, v, cu = inputs.softmax_inputs(w, device="cuda")
+        cud = cu.cuda()
+        T, H, d = q.shape
+        Hkv = k.shape[1]
+        nseq = cu.numel() - 1
+        maxlen = int((cu[1:] - cu[:-1]).max())
+        pairs = softmax_flops(cu)
+        flops = 4.0 * d * H * pairs
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+        opt = _lib.softmax_options(w.extra["rotary_dim"], w.extra["rope_base"], 0.0)
+        nbytes = lib.la_softmax_workspace_bytes(nseq, T, maxlen, H, Hkv, d, _lib.LA_DTYPE_BF16,
+                                                _lib.LA_DTYPE_BF16, ctypes.byref(opt))
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+        names = (["plan"] if nseq > 1 else []) + ["rotate", "attention"]
+        nk = len(names)
+        ev = HipEvents(2 * nk * (reps + 1))
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(i):
+            opt.timing_events = ev.ptr(2 * nk * i)
+            opt.n_timing = nk
+            st = lib.la_softmax_attention_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 cud.data_ptr(), nseq, T, maxlen, H, Hkv, d,
+                                                 _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_BF16,
+                                                 out.data_ptr(), None, ctypes.byref(opt),
+                                                 ws.data_ptr(), ws.numel(), ctypes.c_void_p(stream))
+            _lib.check(st, "la_softmax_attention_varlen")
+
+        call(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(1, reps + 1):
+            call(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        per = {}
+        for j, kn in enumerate(names):
+            per[kn] = sum(ev.elapsed_ms(2 * nk * i + 2 * j, 2 * nk * i + 2 * j + 1)
+                          for i in range(1, reps + 1)) / reps
+        att = per["attention"]
+        res[name] = {"tokens": T, "sequences": nseq, "max_seqlen": maxlen, "H": H, "Hkv": Hkv,
+                     "d": d, "rotary_dim": w.extra["rotary_dim"], "rope_base": w.extra["rope_base"],
+                     "ms_per_call": ms, "per_kernel_ms": per, "algorithmic_flops": flops,
+                     "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
+                     "call_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                     "tokens_per_s": T / (ms * 1e-3), "reps": reps}
+        log("softmax %s: %.3f ms/call (attention kernel %.3f ms, %.0f TFLOP/s = %.1f%% of "
+            "the bf16 peak)" % (name, ms, att, res[name]["attention_TFLOPs"],
+                                100 * res[name]["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS))
+        del q, k, v, cud, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_softmax(inputs, rows=256):
+    """The softmax-layer oracle (plain fp64 C) on the last `rows` tokens of the
+    32K-token workload, every head: algorithmic TFLOP/s."""
+    import numpy as np
+
+    from oracle import softmax as SO
+
+    w = inputs.WORKLOADS["softmax_32k"]
+    q, k, v, cu = inputs.softmax_inputs(w, device="cpu")
+    T, H, d = q.shape
+    toks = np.repeat(np.arange(T - rows, T), H)
+    heads = np.tile(np.arange(H), rows)
+    threads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    SO.attention(q, k, v, cu, rotary_dim=w.extra["rotary_dim"], rope_base=w.extra["rope_base"],
+                 rows=toks, heads=heads, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * d * float((toks + 1).sum())
+    log("cpu baseline (softmax layer): %.2f s for %d token-heads" % (dt, len(toks)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "last %d tokens x %d heads of softmax_32k (each over its %d-%d keys); fp64 "
+                      "per-pair loops; %.1f s" % (rows, H, T - rows + 1, T, dt)}
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
     """Device-to-device copy rate (read + write bytes per second) on this GPU."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
@@ -423,12 +523,13 @@ SOURCES = os.path.join(ROOT, "linear_attention_long_amd", "csrc")
 
 
 def source_digest() -> str:
-    """sha256 over the library's HIP sources (names and contents)."""
+    """sha256 over the linear-attention kernels' HIP sources (names and
+    contents of csrc/la_*)."""
     import hashlib
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(SOURCES)):
-        if name.endswith((".h", ".hip")):
+        if name.startswith("la_") and name.endswith((".h", ".hip")):
             h.update(name.encode())
             h.update(open(os.path.join(SOURCES, name), "rb").read())
     return h.hexdigest()
@@ -445,6 +546,35 @@ def measured_traffic():
             key, val = line.strip().strip("`").split(":", 1)
             vals[key.strip()] = val.strip().strip("`")
     if vals.get("source_sha256") != source_digest() or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+SOFTMAX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_attention_32k_traffic.md")
+
+
+def softmax_source_digest() -> str:
+    """sha256 over the sources the softmax kernels are built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("la_device.h", "sm_api.hip", "sm_kernels.h"):
+        h.update(name.encode())
+        h.update(open(os.path.join(SOURCES, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_softmax_traffic():
+    """HBM bytes per launch of the softmax attention kernel (32K workload) from
+    the committed counter summary, or None when its sources changed."""
+    if not os.path.exists(SOFTMAX_TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(SOFTMAX_TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith(("source_sha256", "hbm_bytes_per_launch")):
+            key, val = line.strip().strip("`").split(":", 1)
+            vals[key.strip()] = val.strip().strip("`")
+    if vals.get("source_sha256") != softmax_source_digest() or "hbm_bytes_per_launch" not in vals:
         return None
     return float(vals["hbm_bytes_per_launch"])
 
@@ -483,6 +613,13 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 32K-token and varlen timings and the copy-bandwidth reference")
     ap.add_argument("--cpu-tokens", type=int, default=262144)
+    ap.add_argument("--no-softmax", action="store_true",
+                    help="skip the softmax attention layer's workloads")
+    ap.add_argument("--no-softmax-1m", action="store_true",
+                    help="skip its 1M-token workload (about 2 s per call)")
+    ap.add_argument("--softmax-only", action="store_true",
+                    help="only time the softmax layer's workloads (for profiling its kernels); "
+                         "prints their JSON instead of the benchmark line")
     ap.add_argument("--block", type=int, default=0, help="block size (0 = library default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps times "
@@ -509,6 +646,10 @@ def main():
         return
     lib = _lib.load()
     log("device: %s" % torch.cuda.get_device_name(0))
+    if args.softmax_only:
+        print(json.dumps({"softmax_layer": bench_softmax(args, torch, lib, _lib, inputs)}),
+              flush=True)
+        return
 
     pre = bench_prefill(args, torch, lib, _lib, inputs)
     dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
@@ -525,6 +666,25 @@ def main():
                 dec[key]["device_copy_GBps"] = cgbs
                 dec[key]["frac_of_copy"] = dec[key]["GBps"] / cgbs
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, inputs)
+    soft = None
+    if not args.no_softmax:
+        soft = bench_softmax(args, torch, lib, _lib, inputs)
+        lead = soft["softmax_32k"]
+        att_ms = lead["per_kernel_ms"]["attention"]
+        soft_traffic = measured_softmax_traffic()
+        soft = {
+            "workloads": soft,
+            "roofline": {"bound": "mfma", "kernel": "attention (k_sm_attn), softmax_32k",
+                         "achieved": lead["attention_TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": lead["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS,
+                         "traffic": soft_traffic,
+                         "algorithmic_flops_per_launch": lead["algorithmic_flops"],
+                         "avg_launch_ms": att_ms},
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_softmax(inputs),
+        }
+        if "softmax_1m" in soft["workloads"] and args.workload == "prefill_1m":
+            soft["softmax_over_linear_1m"] = (soft["workloads"]["softmax_1m"]["ms_per_call"]
+                                              / pre["ms_per_step"])
 
     th = pre["token_heads"]
     if pre["fused_gate"]:
@@ -581,6 +741,7 @@ def main():
         "decode": dec,
         "other_prefill": other,
         "serving_step": serve,
+        "softmax_layer": soft,
     }
     print(json.dumps(line), flush=True)
 
