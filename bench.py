@@ -387,7 +387,9 @@ def bench_serving(args, torch, api, inputs, reps=50):
     return res
 
 
-SOFTMAX_WORKLOADS = (("softmax_32k", 20), ("softmax_varlen_512k", 5), ("softmax_1m", 2))
+# (workload, timed calls, precision option: 0 single bf16 operands, 1 split)
+SOFTMAX_WORKLOADS = (("softmax_32k", 20, 0), ("softmax_varlen_512k", 5, 0), ("softmax_1m", 2, 0),
+                     ("softmax_32k", 10, 1), ("softmax_varlen_512k", 3, 1))
 
 
 def softmax_flops(cu):
@@ -402,9 +404,10 @@ def bench_softmax(args, torch, lib, _lib, inputs):
     """The hybrid model's softmax attention layer (include/la_softmax.h) on its
     workloads: per-kernel times from HIP events on the call's stream."""
     res = {}
-    for name, reps in SOFTMAX_WORKLOADS:
+    for name, reps, prec in SOFTMAX_WORKLOADS:
         if name == "softmax_1m" and args.no_softmax_1m:
             continue
+        key = name + ("_split" if prec else "")
         w = inputs.WORKLOADS[name]
         q, k, v, cu = inputs.softmax_inputs(w, device="cuda")
         cud = cu.cuda()
@@ -415,7 +418,7 @@ def bench_softmax(args, torch, lib, _lib, inputs):
         pairs = softmax_flops(cu)
         flops = 4.0 * d * H * pairs
         out = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
-        opt = _lib.softmax_options(w.extra["rotary_dim"], w.extra["rope_base"], 0.0)
+        opt = _lib.softmax_options(w.extra["rotary_dim"], w.extra["rope_base"], 0.0, prec)
         nbytes = lib.la_softmax_workspace_bytes(nseq, T, maxlen, H, Hkv, d, _lib.LA_DTYPE_BF16,
                                                 _lib.LA_DTYPE_BF16, ctypes.byref(opt))
         ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
@@ -446,15 +449,16 @@ def bench_softmax(args, torch, lib, _lib, inputs):
             per[kn] = sum(ev.elapsed_ms(2 * nk * i + 2 * j, 2 * nk * i + 2 * j + 1)
                           for i in range(1, reps + 1)) / reps
         att = per["attention"]
-        res[name] = {"tokens": T, "sequences": nseq, "max_seqlen": maxlen, "H": H, "Hkv": Hkv,
-                     "d": d, "rotary_dim": w.extra["rotary_dim"], "rope_base": w.extra["rope_base"],
-                     "ms_per_call": ms, "per_kernel_ms": per, "algorithmic_flops": flops,
-                     "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
-                     "call_TFLOPs": flops / (ms * 1e-3) / 1e12,
-                     "tokens_per_s": T / (ms * 1e-3), "reps": reps}
+        res[key] = {"tokens": T, "sequences": nseq, "max_seqlen": maxlen, "H": H, "Hkv": Hkv,
+                    "d": d, "rotary_dim": w.extra["rotary_dim"], "rope_base": w.extra["rope_base"],
+                    "precision": "split bf16 hi+lo operands" if prec else "single bf16 operands",
+                    "ms_per_call": ms, "per_kernel_ms": per, "algorithmic_flops": flops,
+                    "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
+                    "call_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                    "tokens_per_s": T / (ms * 1e-3), "reps": reps}
         log("softmax %s: %.3f ms/call (attention kernel %.3f ms, %.0f TFLOP/s = %.1f%% of "
-            "the bf16 peak)" % (name, ms, att, res[name]["attention_TFLOPs"],
-                                100 * res[name]["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS))
+            "the bf16 peak)" % (key, ms, att, res[key]["attention_TFLOPs"],
+                                100 * res[key]["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS))
         del q, k, v, cud, out, ws
         torch.cuda.empty_cache()
     return res

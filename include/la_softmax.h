@@ -27,11 +27,15 @@
  * by a fixed permutation of q's and k's features and gives the same scores
  * when both are permuted.)
  *
- * Precision: the rotated, scaled q and the rotated k are rounded to bf16
- * once, the scores and the softmax are fp32, the probabilities are rounded
- * to bf16 for the product with V, accumulation is fp32.  Against fp64 the
- * output error is a few 1e-3 of its rms for scores of unit spread; it grows
- * with the spread of the scores.
+ * Precision (default mode): the rotated, scaled q and the rotated k are
+ * rounded to bf16 once, the scores and the softmax are fp32, the
+ * probabilities are rounded to bf16 for the product with V (the same rounded
+ * weights give the denominator), accumulation is fp32.  Against fp64 the
+ * output error is a few 1e-3 of the values' rms for scores of unit spread
+ * (it grows with the spread of the scores); since a row's output shrinks as
+ * its keys grow, that is far more than 1e-2 of the output's own rms for long
+ * sequences.  The split mode (options.precision = 1) keeps ~16 significant
+ * bits in both products and meets 1e-2 of the output's rms.
  *
  * Conventions as in la.h: device pointers to contiguous row-major data
  * (q, k, v, out 16-byte aligned, lse 4-byte aligned); the caller owns every
@@ -63,13 +67,21 @@ extern "C" {
  *               instrumentation, as in la_options_t: events[2i] and
  *               events[2i+1] are recorded around the i-th kernel launched on
  *               hip_stream, i < n_timing.  Kernels in launch order: [plan]
- *               (only when num_seqs > 1), rotate, attention.              */
+ *               (only when num_seqs > 1), rotate, attention.
+ *   precision   0 (default): single bf16 operands for both products (the
+ *               usual attention kernel; error against fp64 about 1e-3 of the
+ *               values' scale, see "Precision" above).  1: split operands --
+ *               q, k and the probabilities each carried as bf16 hi + lo, three
+ *               products for the scores and two for P V -- about 1e-4 of the
+ *               output's rms at 2.5x the matrix-core work.  Other values:
+ *               LA_ERR_INVALID_ARGUMENT.                                    */
 typedef struct {
     int32_t rotary_dim;
     double rope_base;
     float scale;
     void* timing_events;
     int32_t n_timing;
+    int32_t precision;
 } la_softmax_options_t;
 
 la_softmax_options_t la_softmax_default_options(void);
@@ -89,7 +101,8 @@ la_softmax_options_t la_softmax_default_options(void);
  *   in_dtype = LA_DTYPE_BF16 (LA_DTYPE_F32 inputs: LA_ERR_UNSUPPORTED),
  *   H * d <= 2^20.
  *   workspace   device scratch of at least la_softmax_workspace_bytes(...)
- *               bytes, 256-byte aligned: the rotated q and k (bf16) and, for
+ *               bytes, 256-byte aligned: the rotated q and k (bf16; in the
+ *               split mode also their bf16 remainders) and, for
  *               num_seqs > 1, the work order.
  * `out` and `lse` must not overlap each other, the inputs or the workspace. */
 la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void* v,

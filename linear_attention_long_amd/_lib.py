@@ -72,6 +72,7 @@ class SoftmaxOptions(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("timing_events", ctypes.c_void_p),
         ("n_timing", ctypes.c_int32),
+        ("precision", ctypes.c_int32),
     ]
 
 
@@ -200,11 +201,12 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     return o
 
 
-def softmax_options(rotary_dim=-1, rope_base=10000.0, scale=0.0) -> SoftmaxOptions:
+def softmax_options(rotary_dim=-1, rope_base=10000.0, scale=0.0, precision=0) -> SoftmaxOptions:
     o = load().la_softmax_default_options()
     o.rotary_dim = int(rotary_dim)
     o.rope_base = float(rope_base)
     o.scale = float(scale)
+    o.precision = int(precision)
     return o
 
 

@@ -237,13 +237,15 @@ serve_step = la_serve_step
 
 
 def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-1,
-                                rope_base=10000.0, scale=0.0, out_dtype=torch.bfloat16,
-                                return_lse=False, out=None, stream=None):
+                                rope_base=10000.0, scale=0.0, precision=0,
+                                out_dtype=torch.bfloat16, return_lse=False, out=None,
+                                stream=None):
     """Causal softmax attention with rotary embedding over a packed batch
     (the hybrid model's softmax layer).  q: [total_T, H, d] bfloat16; k, v:
     [total_T, H_kv, d] bfloat16 (H_kv divides H); cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
-    rotary_dim -1 = d/2; scale 0 = 1/sqrt(d).  Returns (out [total_T, H, d],
+    rotary_dim -1 = d/2; scale 0 = 1/sqrt(d); precision 0 = single bf16
+    operands, 1 = split (hi + lo) operands.  Returns (out [total_T, H, d],
     lse [total_T, H] float32 or None)."""
     lib = _lib.load()
     total_T, H, d = q.shape
@@ -255,7 +257,7 @@ def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     num_seqs = cu_seqlens.numel() - 1
-    opt = _lib.softmax_options(rotary_dim, rope_base, scale)
+    opt = _lib.softmax_options(rotary_dim, rope_base, scale, precision)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
     if out is None:

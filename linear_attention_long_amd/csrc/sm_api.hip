@@ -18,6 +18,7 @@ namespace {
 
 struct SmOpts {
     int rot;
+    bool split;
     double base;
     float scale;
     hipEvent_t* events;
@@ -28,7 +29,7 @@ struct SmLayout {
     int ntmax;        // query tiles of the longest sequence
     int64_t emax;     // bound of the (sequence, tile) pairs
     bool planned;     // num_seqs > 1: the plan kernel orders the tiles
-    size_t off_qr, off_kr, off_count, off_table, off_hist, off_off, off_cursor, off_tcu, total;
+    size_t off_qr, off_kr, off_qrl, off_krl, off_count, off_table, off_hist, off_off, off_cursor, off_tcu, total;
 };
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -56,6 +57,8 @@ la_status_t sm_parse(const la_softmax_options_t* opt, int d, SmOpts& o) {
     if (x.n_timing < 0 || (x.n_timing > 0 && !x.timing_events)) return LA_ERR_INVALID_ARGUMENT;
     o.events = (hipEvent_t*)x.timing_events;
     o.n_events = x.timing_events ? x.n_timing : 0;
+    if (x.precision != 0 && x.precision != 1) return LA_ERR_INVALID_ARGUMENT;
+    o.split = x.precision == 1;
     return LA_OK;
 }
 
@@ -74,7 +77,7 @@ la_status_t sm_check(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int3
 }
 
 la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
-                      int32_t H_kv, SmLayout& p) {
+                      int32_t H_kv, bool split, SmLayout& p) {
     p.ntmax = (max_seqlen + sm::BQ - 1) / sm::BQ;
     p.planned = num_seqs > 1;
     const int64_t bound = ((int64_t)total_T + (int64_t)num_seqs * (sm::BQ - 1)) / sm::BQ;
@@ -86,6 +89,13 @@ la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int
     o = a256(o + (size_t)total_T * H * sm::D * 2);
     p.off_kr = o;
     o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
+    p.off_qrl = p.off_krl = o;
+    if (split) {  // bf16 remainders of the rotated q and k
+        p.off_qrl = o;
+        o = a256(o + (size_t)total_T * H * sm::D * 2);
+        p.off_krl = o;
+        o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
+    }
     p.off_count = p.off_table = p.off_hist = p.off_off = p.off_cursor = p.off_tcu = o;
     if (p.planned) {
         p.off_count = o;
@@ -130,6 +140,7 @@ la_softmax_options_t la_softmax_default_options(void) {
     o.scale = 0.f;
     o.timing_events = nullptr;
     o.n_timing = 0;
+    o.precision = 0;
     return o;
 }
 
@@ -141,7 +152,7 @@ size_t la_softmax_workspace_bytes(int32_t num_seqs, int32_t total_T, int32_t max
     SmOpts o;
     if (sm_parse(opt, d, o) != LA_OK) return (size_t)-1;
     SmLayout p;
-    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, p) != LA_OK) return (size_t)-1;
+    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, p) != LA_OK) return (size_t)-1;
     return p.total;
 }
 
@@ -162,7 +173,7 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         !is_aligned(cu_seqlens, 4) || (lse && !is_aligned(lse, 4)))
         return LA_ERR_INVALID_ARGUMENT;
     SmLayout p;
-    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, p)) != LA_OK) return st;
+    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, p)) != LA_OK) return st;
     const size_t nq = (size_t)total_T * H * d * 2, nkv = (size_t)total_T * H_kv * d * 2;
     const size_t nout = (size_t)total_T * H * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
     const size_t nlse = lse ? (size_t)total_T * H * 4 : 0;
@@ -187,6 +198,8 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     char* ws = (char*)workspace;
     uint16_t* qr = (uint16_t*)(ws + p.off_qr);
     uint16_t* kr = (uint16_t*)(ws + p.off_kr);
+    uint16_t* qrl = o.split ? (uint16_t*)(ws + p.off_qrl) : nullptr;
+    uint16_t* krl = o.split ? (uint16_t*)(ws + p.off_krl) : nullptr;
     const int2* table = nullptr;
     const int32_t* count = nullptr;
     if (p.planned) {
@@ -209,20 +222,23 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         tm.before();
         sm::k_sm_rope<<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, cu_seqlens,
                                                 num_seqs, total_T, H, H_kv, o.rot,
-                                                o.rot > 0 ? std::log2(o.base) : 0.0, qscale, qr, kr);
+                                                o.rot > 0 ? std::log2(o.base) : 0.0, qscale, qr, kr,
+                                                qrl, krl);
         tm.after();
     }
     const unsigned grid = (unsigned)(p.emax * H);
     tm.before();
     if (grid > 0) {
-        if (out_dtype == LA_DTYPE_BF16)
-            sm::k_sm_attn<uint16_t><<<grid, sm::NT, 0, stream>>>(qr, kr, (const uint16_t*)v,
-                                                                 cu_seqlens, table, count, H, H_kv,
-                                                                 (uint16_t*)out, lse);
-        else
-            sm::k_sm_attn<float><<<grid, sm::NT, 0, stream>>>(qr, kr, (const uint16_t*)v,
-                                                              cu_seqlens, table, count, H, H_kv,
-                                                              (float*)out, lse);
+#define SM_ATTN(OT, SP)                                                                        \
+    sm::k_sm_attn<OT, SP><<<grid, sm::NT, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v,   \
+                                                       cu_seqlens, table, count, H, H_kv,      \
+                                                       (OT*)out, lse)
+        if (out_dtype == LA_DTYPE_BF16) {
+            if (o.split) SM_ATTN(uint16_t, true); else SM_ATTN(uint16_t, false);
+        } else {
+            if (o.split) SM_ATTN(float, true); else SM_ATTN(float, false);
+        }
+#undef SM_ATTN
     }
     tm.after();
     return hipGetLastError() == hipSuccess ? LA_OK : LA_ERR_HIP;

@@ -65,8 +65,12 @@ constexpr int KSK = 132;  // LDS row stride of K (row reads)
 constexpr int KSV = 144;  // LDS row stride of V (transposing reads)
 constexpr int PADE = 8;   // elements after each LDS array (see the linear kernels)
 
+// Double-buffered K and V blocks; with split operands also the bf16
+// remainders of K.
+template <bool SPLIT>
 struct __attribute__((aligned(16))) Smem {
     __attribute__((aligned(16))) uint16_t k[2][BN * KSK + PADE];
+    __attribute__((aligned(16))) uint16_t kl[SPLIT ? 2 : 1][SPLIT ? BN * KSK + PADE : 8];
     __attribute__((aligned(16))) uint16_t v[2][BN * KSV + PADE];
 };
 
@@ -186,7 +190,9 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                                                  const int32_t* __restrict__ cu, int nseq, int T,
                                                  int H, int Hkv, int rot, double log2_base,
                                                  float qscale, uint16_t* __restrict__ qr,
-                                                 uint16_t* __restrict__ kr) {
+                                                 uint16_t* __restrict__ kr,
+                                                 uint16_t* __restrict__ qrl,
+                                                 uint16_t* __restrict__ krl) {
     __shared__ double theta[64];
     if ((int)threadIdx.x < rot / 2)
         theta[threadIdx.x] = exp2(-(2.0 * (double)threadIdx.x / (double)rot) * log2_base);
@@ -218,31 +224,38 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
             const size_t base = isq ? ((size_t)t * H + row) * D : ((size_t)t * Hkv + (row - H)) * D;
             const uint16_t* src = (isq ? q : k) + base;
             uint16_t* dst = (isq ? qr : kr) + base;
+            uint16_t* dlo = isq ? qrl : krl;  // bf16 remainders, or none
+            if (dlo) dlo += base;
             const float sc = isq ? qscale : 1.0f;
             if (pair) {
                 const uint4 wa = *(const uint4*)(src + 8 * u);
                 const uint4 wb = *(const uint4*)(src + 8 * u + half);
                 const uint32_t a32[4] = {wa.x, wa.y, wa.z, wa.w};
                 const uint32_t b32[4] = {wb.x, wb.y, wb.z, wb.w};
-                uint32_t oa[4], ob[4];
+                uint32_t oa[4], ob[4], la[4], lb[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     const float a0 = bf16_lo_to_f32(a32[p]), a1 = bf16_hi_to_f32(a32[p]);
                     const float b0 = bf16_lo_to_f32(b32[p]), b1 = bf16_hi_to_f32(b32[p]);
                     const float c0 = cs[2 * p], s0 = sn[2 * p], c1 = cs[2 * p + 1], s1 = sn[2 * p + 1];
-                    oa[p] = cvt_pk_bf16((a0 * c0 - b0 * s0) * sc, (a1 * c1 - b1 * s1) * sc);
-                    ob[p] = cvt_pk_bf16((b0 * c0 + a0 * s0) * sc, (b1 * c1 + a1 * s1) * sc);
+                    split2_keep((a0 * c0 - b0 * s0) * sc, (a1 * c1 - b1 * s1) * sc, oa[p], la[p]);
+                    split2_keep((b0 * c0 + a0 * s0) * sc, (b1 * c1 + a1 * s1) * sc, ob[p], lb[p]);
                 }
                 *(uint4*)(dst + 8 * u) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
                 *(uint4*)(dst + 8 * u + half) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+                if (dlo) {
+                    *(uint4*)(dlo + 8 * u) = make_uint4(la[0], la[1], la[2], la[3]);
+                    *(uint4*)(dlo + 8 * u + half) = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+                }
             } else if (plain) {
                 const uint4 w = *(const uint4*)(src + 8 * u);
                 const uint32_t w32[4] = {w.x, w.y, w.z, w.w};
-                uint32_t o[4];
+                uint32_t o[4], lo[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p)
-                    o[p] = cvt_pk_bf16(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc);
+                    split2_keep(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc, o[p], lo[p]);
                 *(uint4*)(dst + 8 * u) = make_uint4(o[0], o[1], o[2], o[3]);
+                if (dlo) *(uint4*)(dlo + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             }
         }
     }
@@ -281,16 +294,23 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
 //   rotated k; v [T, Hkv, D] bf16; out [T, H, D]; lse [T, H] (natural log)
 //   or null.  table/ecount: the plan (null for a single sequence, whose
 //   tiles then run last tile first).
-template <typename OutT>
-__global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ qr,
+// SPLIT: qrl, krl hold the bf16 remainders (x - bf16(x)) of the rotated q and
+// k; the scores take three products (hi.hi + lo.hi + hi.lo) and the
+// probabilities are split into bf16 hi + lo for two products with V, which
+// keeps ~16 significant bits in both contractions (one workgroup per CU:
+// the remainders need the registers and LDS of the second).
+template <typename OutT, bool SPLIT>
+__global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
+                                                   const uint16_t* __restrict__ qrl,
+                                                   const uint16_t* __restrict__ krl,
                                                    const uint16_t* __restrict__ v,
                                                    const int32_t* __restrict__ cu,
                                                    const int2* __restrict__ table,
                                                    const int32_t* __restrict__ ecount, int H,
                                                    int Hkv, OutT* __restrict__ out,
                                                    float* __restrict__ lse) {
-    __shared__ Smem sm;
+    __shared__ Smem<SPLIT> sm;
     const int G = H / Hkv;
     const int b = blockIdx.x;
     const int hk = b % Hkv;
@@ -324,19 +344,27 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
 
     // Q^T operands: lane (g, c) holds query wq0 + 16 qt + c, dimensions
     // {32 kk + 4g + i, 32 kk + 16 + 4g + i}.
-    bf16x8_t Qf[2][4];
+    bf16x8_t Qf[2][4], Ql[SPLIT ? 2 : 1][4];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         const int row = wq0 + 16 * qt + c;
-        const uint16_t* p = qr + ((size_t)(start + row) * H + h) * D + 4 * g;
+        const size_t off = ((size_t)(start + row) * H + h) * D + 4 * g;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             i16x4_t lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
             if (row < L) {
-                lo = *(const i16x4_t*)(p + 32 * kk);
-                hi = *(const i16x4_t*)(p + 32 * kk + 16);
+                lo = *(const i16x4_t*)(qr + off + 32 * kk);
+                hi = *(const i16x4_t*)(qr + off + 32 * kk + 16);
             }
             Qf[qt][kk] = as_bf16x8(lo, hi);
+            if constexpr (SPLIT) {
+                i16x4_t lo2 = {0, 0, 0, 0}, hi2 = {0, 0, 0, 0};
+                if (row < L) {
+                    lo2 = *(const i16x4_t*)(qrl + off + 32 * kk);
+                    hi2 = *(const i16x4_t*)(qrl + off + 32 * kk + 16);
+                }
+                Ql[qt][kk] = as_bf16x8(lo2, hi2);
+            }
         }
     }
 
@@ -365,8 +393,9 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
     const uint32_t rs = (uint32_t)(Hkv * D);
     const uint16_t* kseq = kr + ((size_t)start * Hkv + hk) * D;
     const uint16_t* vseq = v + ((size_t)start * Hkv + hk) * D;
+    const uint16_t* klseq = SPLIT ? krl + ((size_t)start * Hkv + hk) * D : nullptr;
     const uint32_t voff = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
-    uint4 rk[4], rv[4];
+    uint4 rk[4], rv[4], rkl[SPLIT ? 4 : 1];
     auto load_kv = [&](int blk) {
         const int nvalid = kv_end - blk * BN;
         const int32_t bytes = (int32_t)((uint32_t)(min(nvalid, BN) - 1) * rs * 2u + 2u * D);
@@ -382,6 +411,14 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
             rv[j] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
         }
+        if constexpr (SPLIT) {
+            const __amdgpu_buffer_rsrc_t rskl =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(klseq + base), (short)0, bytes, 0x00020000);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                rkl[j] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rskl, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
+        }
     };
     auto store_kv = [&](int buf) {
 #pragma unroll
@@ -391,6 +428,11 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
             pk[0] = make_uint2(rk[j].x, rk[j].y);
             pk[1] = make_uint2(rk[j].z, rk[j].w);
             *(uint4*)(sm.v[buf] + r * KSV + (tid & 15) * 8) = rv[j];
+            if constexpr (SPLIT) {
+                uint2* pl = (uint2*)(sm.kl[buf] + r * KSK + (tid & 15) * 8);
+                pl[0] = make_uint2(rkl[j].x, rkl[j].y);
+                pl[1] = make_uint2(rkl[j].z, rkl[j].w);
+            }
         }
     };
 
@@ -407,20 +449,22 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
             f32x4_t Sc[4][2];
             const uint16_t* kt_ = sm.k[buf];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                const bf16x8_t A = k_operand(kt_, 16 * kt + c, 0, g);
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    Sc[kt][qt] = mfma16x16x32(A, Qf[qt][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-            }
-#pragma unroll
-            for (int kk = 1; kk < 4; ++kk)
+            for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     const bf16x8_t A = k_operand(kt_, 16 * kt + c, 32 * kk, g);
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt)
-                        Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk], Sc[kt][qt]);
+                        Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk],
+                                                  kk == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Sc[kt][qt]);
+                    if constexpr (SPLIT) {  // + k_lo . q_hi + k_hi . q_lo
+                        const bf16x8_t Al = k_operand(sm.kl[buf], 16 * kt + c, 32 * kk, g);
+#pragma unroll
+                        for (int qt = 0; qt < 2; ++qt) {
+                            Sc[kt][qt] = mfma16x16x32(Al, Qf[qt][kk], Sc[kt][qt]);
+                            Sc[kt][qt] = mfma16x16x32(A, Ql[qt][kk], Sc[kt][qt]);
+                        }
+                    }
                 }
             if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
 #pragma unroll
@@ -467,15 +511,26 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
                         Sc[kt][qt][i] = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - m[qt]);
             // P^T operands: keys {32 ks + 4g + i} from tile 2ks, {32 ks + 16 + 4g + i}
             // from tile 2ks + 1.
-            bf16x8_t Pf[2][2];
+            bf16x8_t Pf[2][2], Pl[SPLIT ? 2 : 1][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const f32x4_t a = Sc[2 * ks][qt], bq = Sc[2 * ks + 1][qt];
-                    Pf[ks][qt] = as_bf16x8(make_uint4(cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]),
-                                                      cvt_pk_bf16(bq[0], bq[1]),
-                                                      cvt_pk_bf16(bq[2], bq[3])));
+                    if constexpr (SPLIT) {
+                        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+                        split2(a[0], a[1], h0, l0);
+                        split2(a[2], a[3], h1, l1);
+                        split2(bq[0], bq[1], h2, l2);
+                        split2(bq[2], bq[3], h3, l3);
+                        Pf[ks][qt] = as_bf16x8(make_uint4(h0, h1, h2, h3));
+                        Pl[ks][qt] = as_bf16x8(make_uint4(l0, l1, l2, l3));
+                    } else {
+                        Pf[ks][qt] = as_bf16x8(make_uint4(cvt_pk_bf16(a[0], a[1]),
+                                                          cvt_pk_bf16(a[2], a[3]),
+                                                          cvt_pk_bf16(bq[0], bq[1]),
+                                                          cvt_pk_bf16(bq[2], bq[3])));
+                    }
                 }
             const uint16_t* vt_ = sm.v[buf];
 #pragma unroll
@@ -484,10 +539,16 @@ __global__ __launch_bounds__(NT, 2) void k_sm_attn(const uint16_t* __restrict__ 
                 for (int ft = 0; ft < 8; ++ft) {
                     const bf16x8_t A = v_operand(vt_, 32 * ks, 16 * ft, g, c);
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
+                    for (int qt = 0; qt < 2; ++qt) {
+                        O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
+                        if constexpr (SPLIT) O[ft][qt] = mfma16x16x32(A, Pl[ks][qt], O[ft][qt]);
+                    }
                 }
 #pragma unroll
-                for (int qt = 0; qt < 2; ++qt) Lc[qt] = mfma16x16x32(ones, Pf[ks][qt], Lc[qt]);
+                for (int qt = 0; qt < 2; ++qt) {
+                    Lc[qt] = mfma16x16x32(ones, Pf[ks][qt], Lc[qt]);
+                    if constexpr (SPLIT) Lc[qt] = mfma16x16x32(ones, Pl[ks][qt], Lc[qt]);
+                }
             }
         }
         if (blk + 1 < nblk) store_kv(buf ^ 1);

@@ -221,6 +221,10 @@ def test_softmax_workspace_bytes(lib):
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 3, 128, BF16, F32, ctypes.byref(o)) == SIZE_MAX
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 64, BF16, F32, ctypes.byref(o)) == SIZE_MAX
     assert lib.la_softmax_workspace_bytes(1, 16, 17, 4, 4, 128, BF16, F32, ctypes.byref(o)) == SIZE_MAX
+    # the split mode adds the bf16 remainders of the rotated q and k
+    osp = _lib.softmax_options(precision=1)
+    assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
+                                          ctypes.byref(osp)) == 2 * (1000 * 4 * 256 + 1000 * 2 * 256)
     # the base is not used (nor checked) without rotation
     o0 = _lib.softmax_options(rotary_dim=0, rope_base=0.0)
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o0)) > 0
@@ -255,6 +259,7 @@ def test_softmax_rejects_bad_arguments(lib):
     assert call(rope_base=0.0) == INVALID
     assert call(rope_base=float("inf")) == INVALID
     assert call(scale=-1.0) == INVALID
+    assert call(precision=2) == INVALID
     assert call(out=A[0]) == INVALID                               # out overlaps q
     assert call(lse=ctypes.c_void_p(A[3].value + 64)) == INVALID   # lse overlaps out
     assert call(ws=None) == INVALID
