@@ -16,6 +16,15 @@ using namespace la;
 
 namespace {
 
+#ifndef LA_SM_WAVES
+#define LA_SM_WAVES 8
+#endif
+// Waves per attention workgroup: single-operand mode LA_SM_WAVES (32 queries
+// each), split mode 4 (its registers allow one workgroup of 4 waves per CU).
+constexpr int kWavesPlain = LA_SM_WAVES;
+constexpr int kWavesSplit = 4;
+inline int tile_queries(bool split) { return 32 * (split ? kWavesSplit : kWavesPlain); }
+
 struct SmOpts {
     int rot;
     bool split;
@@ -26,6 +35,7 @@ struct SmOpts {
 };
 
 struct SmLayout {
+    int bq;           // queries per tile
     int ntmax;        // query tiles of the longest sequence
     int64_t emax;     // bound of the (sequence, tile) pairs
     bool planned;     // num_seqs > 1: the plan kernel orders the tiles
@@ -78,9 +88,11 @@ la_status_t sm_check(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int3
 
 la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
                       int32_t H_kv, bool split, SmLayout& p) {
-    p.ntmax = (max_seqlen + sm::BQ - 1) / sm::BQ;
+    const int BQ = tile_queries(split);
+    p.bq = BQ;
+    p.ntmax = (max_seqlen + BQ - 1) / BQ;
     p.planned = num_seqs > 1;
-    const int64_t bound = ((int64_t)total_T + (int64_t)num_seqs * (sm::BQ - 1)) / sm::BQ;
+    const int64_t bound = ((int64_t)total_T + (int64_t)num_seqs * (BQ - 1)) / BQ;
     const int64_t dense = (int64_t)num_seqs * p.ntmax;
     p.emax = p.planned ? (dense < bound ? dense : bound) : p.ntmax;
     if (p.emax * H > INT32_MAX) return LA_ERR_UNSUPPORTED;
@@ -204,7 +216,7 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     const int32_t* count = nullptr;
     if (p.planned) {
         tm.before();
-        sm::k_sm_plan<<<1, 1024, 0, stream>>>(cu_seqlens, num_seqs, p.ntmax,
+        sm::k_sm_plan<<<1, 1024, 0, stream>>>(cu_seqlens, num_seqs, p.bq, p.ntmax,
                                                (int32_t*)(ws + p.off_hist),
                                                (int32_t*)(ws + p.off_off),
                                                (int32_t*)(ws + p.off_cursor),
@@ -229,14 +241,16 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     const unsigned grid = (unsigned)(p.emax * H);
     tm.before();
     if (grid > 0) {
-#define SM_ATTN(OT, SP)                                                                        \
-    sm::k_sm_attn<OT, SP><<<grid, sm::NT, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v,   \
-                                                       cu_seqlens, table, count, H, H_kv,      \
-                                                       (OT*)out, lse)
+#define SM_ATTN(OT, SP, W)                                                                     \
+    sm::k_sm_attn<OT, SP, W><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
+                                                          cu_seqlens, table, count, H, H_kv,   \
+                                                          (OT*)out, lse)
         if (out_dtype == LA_DTYPE_BF16) {
-            if (o.split) SM_ATTN(uint16_t, true); else SM_ATTN(uint16_t, false);
+            if (o.split) SM_ATTN(uint16_t, true, kWavesSplit);
+            else SM_ATTN(uint16_t, false, kWavesPlain);
         } else {
-            if (o.split) SM_ATTN(float, true); else SM_ATTN(float, false);
+            if (o.split) SM_ATTN(float, true, kWavesSplit);
+            else SM_ATTN(float, false, kWavesPlain);
         }
 #undef SM_ATTN
     }

@@ -18,12 +18,16 @@
 //  * k_sm_rope: q and k are rotated once (angles reduced in fp64), q is also
 //    multiplied by scale * log2(e), and both are rounded to bf16 into the
 //    workspace; every workgroup of the main kernel then reads ready operands;
-//  * k_sm_attn: one workgroup = one (128-query tile, head); streaming softmax
+//  * k_sm_attn: one workgroup = one (query tile, head); streaming softmax
 //    over 64-key blocks.
 //
 // gfx950 design of k_sm_attn:
-//  * 4 waves x 32 queries; a wave's rotated Q stays in registers as MFMA
-//    operands for the whole key loop;
+//  * W waves x 32 queries: 8 waves (256-query tiles, one workgroup per CU)
+//    with single bf16 operands, 4 waves (128-query tiles) with split
+//    operands, whose registers allow only one 4-wave workgroup per CU; either
+//    way two waves share a SIMD.  Each staged K/V block serves all W waves.
+//    A wave's rotated Q stays in registers as MFMA operands for the whole
+//    key loop;
 //  * the score tile is produced transposed, S^T = K Q^T
 //    (v_mfma_f32_16x16x32_bf16), so each lane holds 4 keys of one query: the
 //    running max needs only two cross-lane steps;
@@ -47,7 +51,10 @@
 //    the rescale of the accumulators by exp2(m_old - m_new) is rare;
 //  * K and V blocks arrive through buffer loads whose range ends at the
 //    tile's last key (zeros past it, no per-lane bounds arithmetic);
-//  * two workgroups per CU (69 KB of LDS each); the blockIdx -> (tile, head)
+//  * the matrix-core sections run at raised wave priority (s_setprio 1), so a
+//    SIMD issues one wave's MFMA stream first and fills its gaps with the
+//    other wave's vector work;
+//  * 69 KB of LDS per workgroup (104.5 KB with split operands); the blockIdx -> (tile, head)
 //    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
 //    head's K and V share that XCD's L2.
 #pragma once
@@ -58,8 +65,14 @@ namespace la {
 namespace sm {
 
 constexpr int D = 128;    // head dim
-constexpr int NT = 256;   // threads per workgroup of the main kernel
-constexpr int BQ = 128;   // queries per workgroup (4 waves x 32)
+// The attention kernel runs W waves of 32 queries each per workgroup: 64 W
+// threads, a tile of 32 W queries.
+template <int W>
+struct Waves {
+    static constexpr int NT = 64 * W;   // threads
+    static constexpr int BQ = 32 * W;   // queries per tile
+    static constexpr int RP = NT / 16;  // K/V rows staged per pass (16 threads per row)
+};
 constexpr int BN = 64;    // keys per K/V block
 constexpr int KSK = 132;  // LDS row stride of K (row reads)
 constexpr int KSV = 144;  // LDS row stride of V (transposing reads)
@@ -102,14 +115,14 @@ __device__ __forceinline__ int block_excl_scan(int x, int& total, int* wsum /* [
 
 // Orders the (sequence, query tile) pairs of a packed batch by decreasing
 // tile index (ties in any order: each pair's result does not depend on when
-// it runs).  Tile i of a sequence of length L exists for i < ceil(L / BQ)
+// it runs).  Tile i of a sequence of length L exists for i < ceil(L / bq)
 // (clamped to ntmax); the number of sequences with a tile i is
 // cnt[i] = #{s : n_s > i}, the tiles with index i occupy table entries
 // [off[i], off[i] + cnt[i]) with off[i] = sum of cnt[i'] over i' > i.
 // One workgroup of 1024 threads.  Workspace arrays: hist [ntmax + 1],
 // off and cursor [ntmax], tcu [nseq + 1].
 __global__ __launch_bounds__(1024) void k_sm_plan(const int32_t* __restrict__ cu, int nseq,
-                                                  int ntmax, int32_t* __restrict__ hist,
+                                                  int bq, int ntmax, int32_t* __restrict__ hist,
                                                   int32_t* __restrict__ off,
                                                   int32_t* __restrict__ cursor,
                                                   int32_t* __restrict__ tcu,
@@ -125,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_sm_plan(const int32_t* __restrict__ cu
     __syncthreads();
     auto ntiles = [&](int s) {
         const int L = cu[s + 1] - cu[s];
-        const int n = L > 0 ? (L + BQ - 1) / BQ : 0;
+        const int n = L > 0 ? (L + bq - 1) / bq : 0;
         return n < ntmax ? n : ntmax;
     };
     for (int s = tid; s < nseq; s += 1024) atomicAdd(&hist[ntiles(s)], 1);
@@ -299,8 +312,8 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
 // probabilities are split into bf16 hi + lo for two products with V, which
 // keeps ~16 significant bits in both contractions (one workgroup per CU:
 // the remainders need the registers and LDS of the second).
-template <typename OutT, bool SPLIT>
-__global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
+template <typename OutT, bool SPLIT, int W>
+__global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
                                                    const uint16_t* __restrict__ qrl,
                                                    const uint16_t* __restrict__ krl,
@@ -311,6 +324,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
                                                    int Hkv, OutT* __restrict__ out,
                                                    float* __restrict__ lse) {
     __shared__ Smem<SPLIT> sm;
+    constexpr int BQ = Waves<W>::BQ, RP = Waves<W>::RP, NJ = BN / RP;
     const int G = H / Hkv;
     const int b = blockIdx.x;
     const int hk = b % Hkv;
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
     const uint16_t* vseq = v + ((size_t)start * Hkv + hk) * D;
     const uint16_t* klseq = SPLIT ? krl + ((size_t)start * Hkv + hk) * D : nullptr;
     const uint32_t voff = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
-    uint4 rk[4], rv[4], rkl[SPLIT ? 4 : 1];
+    uint4 rk[NJ], rv[NJ], rkl[SPLIT ? NJ : 1];
     auto load_kv = [&](int blk) {
         const int nvalid = kv_end - blk * BN;
         const int32_t bytes = (int32_t)((uint32_t)(min(nvalid, BN) - 1) * rs * 2u + 2u * D);
@@ -405,25 +419,25 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
         const __amdgpu_buffer_rsrc_t rsv =
             __builtin_amdgcn_make_buffer_rsrc((void*)(vseq + base), (short)0, bytes, 0x00020000);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             rk[j] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsk, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsk, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
             rv[j] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
         }
         if constexpr (SPLIT) {
             const __amdgpu_buffer_rsrc_t rskl =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(klseq + base), (short)0, bytes, 0x00020000);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
                 rkl[j] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rskl, voff + (uint32_t)(16 * j) * rs * 2u, 0, 0));
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rskl, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
         }
     };
     auto store_kv = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = (tid >> 4) + 16 * j;
+        for (int j = 0; j < NJ; ++j) {
+            const int r = (tid >> 4) + RP * j;
             uint2* pk = (uint2*)(sm.k[buf] + r * KSK + (tid & 15) * 8);
             pk[0] = make_uint2(rk[j].x, rk[j].y);
             pk[1] = make_uint2(rk[j].z, rk[j].w);
@@ -448,6 +462,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
             // keys kb0 + 16 kt + 4g + i.
             f32x4_t Sc[4][2];
             const uint16_t* kt_ = sm.k[buf];
+            __builtin_amdgcn_s_setprio(1);  // matrix-core section (see below)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -466,6 +481,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
                         }
                     }
                 }
+            __builtin_amdgcn_s_setprio(0);
             if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
@@ -533,6 +549,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
                     }
                 }
             const uint16_t* vt_ = sm.v[buf];
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -550,6 +567,7 @@ __global__ __launch_bounds__(NT, SPLIT ? 1 : 2) void k_sm_attn(const uint16_t* _
                     if constexpr (SPLIT) Lc[qt] = mfma16x16x32(ones, Pl[ks][qt], Lc[qt]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (blk + 1 < nblk) store_kv(buf ^ 1);
         __syncthreads();
