@@ -19,7 +19,7 @@
 //    multiplied by scale * log2(e), and both are rounded to bf16 into the
 //    workspace; every workgroup of the main kernel then reads ready operands;
 //  * k_sm_attn: one workgroup = one (query tile, head); streaming softmax
-//    over 64-key blocks.
+//    over blocks of 128 keys (64 with split operands).
 //
 // gfx950 design of k_sm_attn:
 //  * W waves x 32 queries: 8 waves (256-query tiles, one workgroup per CU)
@@ -54,7 +54,7 @@
 //  * the matrix-core sections run at raised wave priority (s_setprio 1), so a
 //    SIMD issues one wave's MFMA stream first and fills its gaps with the
 //    other wave's vector work;
-//  * 69 KB of LDS per workgroup (104.5 KB with split operands); the blockIdx -> (tile, head)
+//  * 138 KB of LDS per workgroup (104.5 KB with split operands); the blockIdx -> (tile, head)
 //    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
 //    head's K and V share that XCD's L2.
 #pragma once
@@ -73,14 +73,18 @@ struct Waves {
     static constexpr int BQ = 32 * W;   // queries per tile
     static constexpr int RP = NT / 16;  // K/V rows staged per pass (16 threads per row)
 };
-constexpr int BN = 64;    // keys per K/V block
+#ifndef LA_SM_BLOCK
+#define LA_SM_BLOCK 128
+#endif
+constexpr int kBlockPlain = LA_SM_BLOCK;  // keys per K/V block, single bf16 operands
+constexpr int kBlockSplit = 64;           // keys per K/V block, split operands
 constexpr int KSK = 132;  // LDS row stride of K (row reads)
 constexpr int KSV = 144;  // LDS row stride of V (transposing reads)
 constexpr int PADE = 8;   // elements after each LDS array (see the linear kernels)
 
 // Double-buffered K and V blocks; with split operands also the bf16
 // remainders of K.
-template <bool SPLIT>
+template <bool SPLIT, int BN>
 struct __attribute__((aligned(16))) Smem {
     __attribute__((aligned(16))) uint16_t k[2][BN * KSK + PADE];
     __attribute__((aligned(16))) uint16_t kl[SPLIT ? 2 : 1][SPLIT ? BN * KSK + PADE : 8];
@@ -323,7 +327,10 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                                                    const int32_t* __restrict__ ecount, int H,
                                                    int Hkv, OutT* __restrict__ out,
                                                    float* __restrict__ lse) {
-    __shared__ Smem<SPLIT> sm;
+    constexpr int BN = SPLIT ? kBlockSplit : kBlockPlain;  // keys per K/V block
+    constexpr int NKT = BN / 16;  // 16-key score tiles per block
+    constexpr int NKS = BN / 32;  // 32-key steps of the P V product
+    __shared__ Smem<SPLIT, BN> sm;
     constexpr int BQ = Waves<W>::BQ, RP = Waves<W>::RP, NJ = BN / RP;
     const int G = H / Hkv;
     const int b = blockIdx.x;
@@ -460,13 +467,13 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
         if (has_q && kb0 <= wq_last) {
             // S^T tiles: Sc[kt][qt], lane (g, c) = query wq0 + 16 qt + c,
             // keys kb0 + 16 kt + 4g + i.
-            f32x4_t Sc[4][2];
+            f32x4_t Sc[NKT][2];
             const uint16_t* kt_ = sm.k[buf];
             __builtin_amdgcn_s_setprio(1);  // matrix-core section (see below)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
+                for (int kt = 0; kt < NKT; ++kt) {
                     const bf16x8_t A = k_operand(kt_, 16 * kt + c, 32 * kk, g);
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt)
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                 for (int qt = 0; qt < 2; ++qt) {
                     const int qi = wq0 + 16 * qt + c;
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
+                    for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (kb0 + 16 * kt + 4 * g + i > qi) Sc[kt][qt][i] = -INFINITY;
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             for (int qt = 0; qt < 2; ++qt) {
                 float x = Sc[0][qt][0];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) x = fmaxf(x, Sc[kt][qt][i]);
                 x = fmaxf(x, __shfl_xor(x, 16, 64));
@@ -521,15 +528,15 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         Sc[kt][qt][i] = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - m[qt]);
             // P^T operands: keys {32 ks + 4g + i} from tile 2ks, {32 ks + 16 + 4g + i}
             // from tile 2ks + 1.
-            bf16x8_t Pf[2][2], Pl[SPLIT ? 2 : 1][2];
+            bf16x8_t Pf[NKS][2], Pl[SPLIT ? NKS : 1][2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
                     const f32x4_t a = Sc[2 * ks][qt], bq = Sc[2 * ks + 1][qt];
@@ -551,7 +558,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             const uint16_t* vt_ = sm.v[buf];
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
                 for (int ft = 0; ft < 8; ++ft) {
                     const bf16x8_t A = v_operand(vt_, 32 * ks, 16 * ft, g, c);
