@@ -1,6 +1,6 @@
 """The calls under HIP graph capture (torch.cuda.graph): decode, the fused and
-chunked prefill (cooperative launch), a packed prefill with state slots and a
-serving step are captured once and replayed several times, with eager work
+chunked prefill (cooperative launch), a packed prefill with state slots, a
+serving step and the softmax attention layer are captured once and replayed several times, with eager work
 and synchronisation between replays; every replay must reproduce the eager
 result bit for bit.  (No call records a memset node: buffers that must start
 at zero are cleared by kernels.)"""
@@ -103,3 +103,17 @@ def test_graph_varlen_with_slots_and_serving_step():
 
     g, (out_g,) = capture(step)
     replay_and_check(g, lambda: pool_g.copy_(pool0), [out_g, pool_g], [out_e, pool_e])
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_graph_softmax_packed(precision):
+    # the softmax layer on a packed batch: ordering pass (atomics), rotation and
+    # attention kernels captured together
+    lengths = [700, 1, 300, 2048]
+    T, H, Hkv, d = sum(lengths), 8, 2, 128
+    q, k, v = rnd((T, H, d), 11), rnd((T, Hkv, d), 12), rnd((T, Hkv, d), 13)
+    cu = torch.tensor([0, 700, 701, 1001, T], dtype=torch.int32, device=DEV)
+    kw = dict(rope_base=1e7, out_dtype=torch.float32, return_lse=True, precision=precision)
+    o_e, l_e = api.la_softmax_attention_varlen(q, k, v, cu, 2048, **kw)
+    g, (o_g, l_g) = capture(lambda: api.la_softmax_attention_varlen(q, k, v, cu, 2048, **kw))
+    replay_and_check(g, lambda: (o_g.zero_(), l_g.zero_()), [o_g, l_g], [o_e, l_e])
