@@ -301,3 +301,19 @@ def test_workload_1m_sampled():
     lerr = float(np.abs(gl - lref).max())
     print("softmax_1m: %d sampled rows, max|err|/rms(v) %.2e, lse %.2e" % (len(rows), err, lerr))
     assert err <= TOL and lerr <= LSE_TOL
+
+
+def test_many_heads_grouped_and_without_lse():
+    # 64 query heads over 8 key/value heads (groups of 8), lengths at and
+    # around the 256-query tile; the call without an lse output writes the
+    # same out
+    lengths = [256, 512, 255, 257, 1]
+    q, k, v, cu = packed(lengths, 64, 8, 91)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7)
+    ref, lref = SO.attention(q, k, v, cu, rope_base=1e7)
+    check(got, ref, v, lse, lref)
+    out2, none = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 512,
+                                                 out_dtype=torch.float32, rope_base=1e7)
+    torch.cuda.synchronize()
+    assert none is None
+    np.testing.assert_array_equal(out2.double().cpu().numpy(), got)
