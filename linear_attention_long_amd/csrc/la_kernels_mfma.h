@@ -130,10 +130,13 @@ __device__ __forceinline__ const uint16_t* head_row(const uint16_t* p, int64_t t
 
 // Buffer resource over the rows [0, nvalid) of one head's tile starting at
 // `blk` (row stride rs elements): loads past the last valid row return zero
-// with no memory access (nvalid <= 0: every load does).  Word 3 is the gfx9
-// raw-buffer configuration (32-bit data format, no swizzle).
+// with no memory access (nvalid <= 0: every load does).  A tile has at most
+// 64 rows, so the range is capped there (it then fits the 32-bit size field
+// for any row stride the library accepts).  Word 3 is the gfx9 raw-buffer
+// configuration (32-bit data format, no swizzle).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* blk, uint32_t rs,
                                                             int nvalid) {
+    nvalid = min(nvalid, 64);
     const int32_t bytes = nvalid > 0 ? (int32_t)((uint32_t)(nvalid - 1) * rs * 2u + 2u * D) : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void*)blk, (short)0, bytes, 0x00020000);
 }
@@ -594,9 +597,10 @@ __device__ __forceinline__ void process_item(
     const uint16_t* kb = head_row(k, it.t0, H, h);
     const uint16_t* vb = head_row(v, it.t0, H, h);
     uint4 rq[L::NJ], rk[L::NJ], rv[L::NJ];
-    load_tile<L::NJ>(rq, qb, rs, min(TB, it.len), tid);
-    load_tile<L::NJ>(rk, kb, rs, min(TB, it.len), tid);
-    load_tile<L::NJ>(rv, vb, rs, min(TB, it.len), tid);
+    const int nv0 = min(TB, it.len);
+    load_tile_buf<L::NJ>(rq, tile_rsrc(qb, rs, nv0), rs, tid);
+    load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, nv0), rs, tid);
+    load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, nv0), rs, tid);
     __syncthreads();  // z (normalised mode) is set
     // the Q tile of block n is staged at the end of block n-1 (here, block 0)
     stage_q<NORM, L::NJ>(sm, rq, tid);
@@ -617,9 +621,9 @@ __device__ __forceinline__ void process_item(
             qb += (size_t)TB * rs;
             kb += (size_t)TB * rs;
             vb += (size_t)TB * rs;
-            load_tile<L::NJ>(rq, qb, rs, nv1, tid);
-            load_tile<L::NJ>(rk, kb, rs, nv1, tid);
-            load_tile<L::NJ>(rv, vb, rs, nv1, tid);
+            load_tile_buf<L::NJ>(rq, tile_rsrc(qb, rs, nv1), rs, tid);
+            load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, nv1), rs, tid);
+            load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, nv1), rs, tid);
         }
         __syncthreads();
         if (NORM && tid < D)  // read again only after the next block's first barrier
