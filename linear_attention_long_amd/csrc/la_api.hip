@@ -20,6 +20,16 @@ using namespace la;
 
 namespace {
 
+// Whether a dtype argument holds one of its declared values, read from its
+// bytes: a C caller may pass any integer, and loading an out-of-range value
+// through the enum type is undefined in C++.
+inline bool dtype_arg_ok(const la_dtype_t& t) {
+    static_assert(sizeof(la_dtype_t) == sizeof(int), "C enum size");
+    int v;
+    std::memcpy(&v, &t, sizeof v);
+    return v == LA_DTYPE_F32 || v == LA_DTYPE_BF16;
+}
+
 constexpr int kMfmaDefaultBlock = 32;   // bf16 d=128: two workgroups per CU
 constexpr int kValuDefaultBlock = 64;
 constexpr int kMinAutoChunk = 512;
@@ -470,7 +480,9 @@ la_options_t la_default_options(void) {
 }
 
 const char* la_status_string(la_status_t s) {
-    switch (s) {
+    int v;  // any integer may arrive: read the bytes, not the enum
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
         case LA_OK: return "ok";
         case LA_ERR_INVALID_ARGUMENT: return "invalid argument";
         case LA_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -482,6 +494,7 @@ const char* la_status_string(la_status_t s) {
 
 size_t la_prefill_workspace_bytes(int32_t Bt, int32_t T, int32_t H, int32_t d, la_dtype_t in_dtype,
                                   la_dtype_t out_dtype, const la_options_t* opt) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return (size_t)-1;
     Opts o;
     if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return (size_t)-1;
     if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
@@ -492,6 +505,7 @@ size_t la_prefill_workspace_bytes(int32_t Bt, int32_t T, int32_t H, int32_t d, l
 size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int32_t max_seqlen,
                                          int32_t H, int32_t d, la_dtype_t in_dtype,
                                          la_dtype_t out_dtype, const la_options_t* opt) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return (size_t)-1;
     Opts o;
     if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T) return (size_t)-1;
     if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
@@ -501,6 +515,7 @@ size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int3
 
 size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out_dtype,
                                  const la_options_t* opt) {
+    if (!dtype_arg_ok(out_dtype)) return (size_t)-1;
     Opts o;
     if (N < 0) return (size_t)-1;
     if (check_shape(H, d, LA_DTYPE_BF16, out_dtype) != LA_OK) return (size_t)-1;
@@ -512,6 +527,7 @@ size_t la_decode_workspace_bytes(int32_t N, int32_t H, int32_t d, la_dtype_t out
 la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, int32_t max_seqlen,
                             int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
                             int32_t has_state_out, const la_options_t* opt, la_plan_t* plan) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     if (!plan) return LA_ERR_INVALID_ARGUMENT;
     if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T)
         return LA_ERR_INVALID_ARGUMENT;
@@ -556,6 +572,7 @@ la_status_t la_prefill(const void* q, const void* k, const void* v, const void* 
                        int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
                        const la_options_t* opt, void* workspace, size_t workspace_bytes,
                        void* hip_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     la_status_t s = check_shape(H, d, in_dtype, out_dtype);
     if (s != LA_OK) return s;
     if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return LA_ERR_INVALID_ARGUMENT;
@@ -610,6 +627,7 @@ la_status_t la_prefill_varlen(const void* q, const void* k, const void* v, const
                               int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
                               const la_options_t* opt, void* workspace, size_t workspace_bytes,
                               void* hip_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     return prefill_varlen_impl(true, q, k, v, x_gate, rms_weight, cu_seqlens, num_seqs, total_T,
                                max_seqlen, state_in, z_in, out, state_out, z_out, H, d, in_dtype,
                                out_dtype, opt, workspace, workspace_bytes, hip_stream);
@@ -707,6 +725,7 @@ la_status_t la_decode_step(const void* q, const void* k, const void* v, const vo
                            int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
                            const la_options_t* opt, void* workspace, size_t workspace_bytes,
                            void* hip_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     return decode_step_impl(true, q, k, v, x_gate, rms_weight, state, z, out, N, H, d, in_dtype,
                             out_dtype, opt, workspace, workspace_bytes, hip_stream);
 }
@@ -778,6 +797,7 @@ size_t la_serve_step_workspace_bytes(int32_t num_decode, int32_t num_prefill,
                                      int32_t prefill_tokens, int32_t max_chunk, int32_t H,
                                      int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
                                      const la_options_t* opt) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return (size_t)-1;
     if (num_decode < 0 || num_prefill < 0 || prefill_tokens < 0) return (size_t)-1;
     return serve_ws(num_decode, num_prefill, prefill_tokens, max_chunk, H, d, in_dtype, out_dtype,
                     opt).total;
@@ -791,6 +811,7 @@ la_status_t la_serve_step(const void* q, const void* k, const void* v, const voi
                           void* out, int32_t H, int32_t d, la_dtype_t in_dtype,
                           la_dtype_t out_dtype, const la_options_t* opt, void* workspace,
                           size_t workspace_bytes, void* decode_stream, void* prefill_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     la_status_t s = check_shape(H, d, in_dtype, out_dtype);
     if (s != LA_OK) return s;
     if (num_decode < 0 || num_prefill < 0 || prefill_tokens < 0 || state_rows < 1 || !state_pool)

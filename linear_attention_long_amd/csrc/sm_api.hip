@@ -9,12 +9,23 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "sm_kernels.h"
 
 using namespace la;
 
 namespace {
+
+// Whether a dtype argument holds one of its declared values, read from its
+// bytes: a C caller may pass any integer, and loading an out-of-range value
+// through the enum type is undefined in C++.
+inline bool dtype_arg_ok(const la_dtype_t& t) {
+    static_assert(sizeof(la_dtype_t) == sizeof(int), "C enum size");
+    int v;
+    std::memcpy(&v, &t, sizeof v);
+    return v == LA_DTYPE_F32 || v == LA_DTYPE_BF16;
+}
 
 #ifndef LA_SM_WAVES
 #define LA_SM_WAVES 8
@@ -159,6 +170,7 @@ la_softmax_options_t la_softmax_default_options(void) {
 size_t la_softmax_workspace_bytes(int32_t num_seqs, int32_t total_T, int32_t max_seqlen,
                                   int32_t H, int32_t H_kv, int32_t d, la_dtype_t in_dtype,
                                   la_dtype_t out_dtype, const la_softmax_options_t* opt) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return (size_t)-1;
     if (sm_check(num_seqs, total_T, max_seqlen, H, H_kv, d, in_dtype, out_dtype) != LA_OK)
         return (size_t)-1;
     SmOpts o;
@@ -175,6 +187,7 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
                                         la_dtype_t out_dtype, void* out, float* lse,
                                         const la_softmax_options_t* opt, void* workspace,
                                         size_t workspace_bytes, void* hip_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
     la_status_t st = sm_check(num_seqs, total_T, max_seqlen, H, H_kv, d, in_dtype, out_dtype);
     if (st != LA_OK) return st;
     SmOpts o;
