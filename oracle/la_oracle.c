@@ -30,6 +30,12 @@
  *     token), eps inside the square root, then times weight w, then times
  *     sigmoid(x) elementwise.
  *
+ * The `flags` argument of every entry point: bit 0 (LAO_NORMALIZED) selects
+ * the normalised output; bit 1 (LAO_FEATURES_GIVEN) says that q, k and v are
+ * already feature vectors phi(.) -- the feature map applied by whoever
+ * produced them, e.g. in the epilogue of the projection that computes them
+ * ([Arch] 2.1 writes Q, K, V = SiLU(X W)) -- so it is not applied again here.
+ *
  * Functions return 0 on success, -1 on an invalid argument.
  */
 #include <math.h>
@@ -41,23 +47,28 @@
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+enum { LAO_NORMALIZED = 1, LAO_FEATURES_GIVEN = 2 };
+
+/* The feature map phi of one input value under `flags`. */
+static double feature(double x, int flags) { return (flags & LAO_FEATURES_GIVEN) ? x : silu(x); }
+
 /* One token of the recurrence for one (sequence, head) pair, in place.
  * [Tut] 3: S <- S + phi(k) phi(v)^T, z <- z + phi(k); then
  * y = phi(q)^T S, optionally divided by phi(q)^T z.
  * S is d x d row-major, S[i*d + j] pairs key feature i with value feature j. */
 static void recurrent_token(const double* qt, const double* kt, const double* vt,
-                            int d, int normalized, double* S, double* z,
+                            int d, int flags, double* S, double* z,
                             double* a, double* b, double* c, double* yt)
 {
     for (int i = 0; i < d; i++) {
-        a[i] = silu(qt[i]);
-        b[i] = silu(kt[i]);
-        c[i] = silu(vt[i]);
+        a[i] = feature(qt[i], flags);
+        b[i] = feature(kt[i], flags);
+        c[i] = feature(vt[i], flags);
     }
     for (int i = 0; i < d; i++)
         for (int j = 0; j < d; j++)
             S[(size_t)i * d + j] += b[i] * c[j];
-    if (normalized)
+    if (flags & LAO_NORMALIZED)
         for (int i = 0; i < d; i++) z[i] += b[i];
     if (!yt) return;
     for (int j = 0; j < d; j++) {
@@ -65,7 +76,7 @@ static void recurrent_token(const double* qt, const double* kt, const double* vt
         for (int i = 0; i < d; i++) acc += a[i] * S[(size_t)i * d + j];
         yt[j] = acc;
     }
-    if (normalized) {
+    if (flags & LAO_NORMALIZED) {
         double den = 0.0;
         for (int i = 0; i < d; i++) den += a[i] * z[i];
         for (int j = 0; j < d; j++) yt[j] /= den;
@@ -79,7 +90,7 @@ typedef struct {
     const double *q, *k, *v;
     const float *qf, *kf, *vf;  /* float inputs (widened exactly) instead of q, k, v */
     const int64_t* cu;
-    int32_t nseq, H, d, normalized;
+    int32_t nseq, H, d, flags;
     const double *state_in, *z_in;
     double *y, *state_out, *z_out;
     const int64_t* sample_idx; /* sorted global token indices, or NULL */
@@ -138,9 +149,9 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
                 kt[i] = (double)J->kf[off + i];
                 vt[i] = (double)J->vf[off + i];
             }
-            recurrent_token(qt, kt, vt, d, J->normalized, S, z, a, b, c, dst);
+            recurrent_token(qt, kt, vt, d, J->flags, S, z, a, b, c, dst);
         } else {
-            recurrent_token(J->q + off, J->k + off, J->v + off, d, J->normalized, S, z, a, b, c, dst);
+            recurrent_token(J->q + off, J->k + off, J->v + off, d, J->flags, S, z, a, b, c, dst);
         }
         if (J->sample_idx && dst) {
             /* several equal sample indices all receive this token's output */
@@ -187,9 +198,9 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
             for (int r = 0; r < n; r++)                                             \
                 for (int e = 0; e < d; e++) {                                       \
                     const size_t off = ((size_t)(b0 + r) * H + h) * d + e;          \
-                    fq[r * d + e] = (T_)silu(J->q[off]);                            \
-                    fk[r * d + e] = (T_)silu(J->k[off]);                            \
-                    fv[r * d + e] = (T_)silu(J->v[off]);                            \
+                    fq[r * d + e] = (T_)feature(J->q[off], J->flags);               \
+                    fk[r * d + e] = (T_)feature(J->k[off], J->flags);               \
+                    fv[r * d + e] = (T_)feature(J->v[off], J->flags);               \
                 }                                                                   \
             for (int r = 0; r < n; r++)                                             \
                 for (int c2 = 0; c2 < n; c2++) {                                    \
@@ -201,7 +212,7 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
             for (int r = 0; r < n; r++) {                                           \
                 double* yr = J->y + ((size_t)(b0 + r) * H + h) * d;                 \
                 T_ den = 0;                                                         \
-                if (J->normalized) {                                                \
+                if (J->flags & LAO_NORMALIZED) {                                                \
                     for (int c2 = 0; c2 <= r; c2++) den += P[r * B + c2];           \
                     for (int e = 0; e < d; e++) den += fq[r * d + e] * z[e];        \
                 }                                                                   \
@@ -210,7 +221,7 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
                     for (int c2 = 0; c2 <= r; c2++) intra += P[r * B + c2] * fv[c2 * d + j]; \
                     for (int i = 0; i < d; i++) inter += fq[r * d + i] * S[(size_t)i * d + j]; \
                     T_ yv = intra + inter;                                          \
-                    if (J->normalized) yv /= den;                                   \
+                    if (J->flags & LAO_NORMALIZED) yv /= den;                                   \
                     yr[j] = (double)yv;                                             \
                 }                                                                   \
             }                                                                       \
@@ -220,7 +231,7 @@ static int run_pair_recurrent(job_t* J, int32_t s, int32_t h)
                     for (int r = 0; r < n; r++) acc += fk[r * d + i] * fv[r * d + j]; \
                     S[(size_t)i * d + j] += acc;                                    \
                 }                                                                   \
-            if (J->normalized)                                                      \
+            if (J->flags & LAO_NORMALIZED)                                                      \
                 for (int i = 0; i < d; i++) {                                       \
                     T_ acc = 0;                                                     \
                     for (int r = 0; r < n; r++) acc += fk[r * d + i];               \
@@ -302,7 +313,7 @@ static int check_cu(const int64_t* cu, int32_t nseq)
  * state_out, z_out: final state per (sequence, head) or NULL. */
 int lao_prefill(const double* q, const double* k, const double* v,
                 const int64_t* cu_seqlens, int32_t nseq, int32_t H, int32_t d,
-                const double* state_in, const double* z_in, int32_t normalized,
+                const double* state_in, const double* z_in, int32_t flags,
                 double* y, double* state_out, double* z_out,
                 const int64_t* sample_idx, int64_t nsample, int32_t nthreads)
 {
@@ -313,7 +324,7 @@ int lao_prefill(const double* q, const double* k, const double* v,
             if (i && sample_idx[i] < sample_idx[i - 1]) return -1;
         }
     }
-    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, flags, state_in, z_in,
                y, state_out, z_out, sample_idx, nsample, nthreads, 0, 0};
     return run_job(&J);
 }
@@ -322,7 +333,7 @@ int lao_prefill(const double* q, const double* k, const double* v,
  * exactly to double as it is used: for inputs too large to hold in double. */
 int lao_prefill_f32in(const float* q, const float* k, const float* v,
                       const int64_t* cu_seqlens, int32_t nseq, int32_t H, int32_t d,
-                      const double* state_in, const double* z_in, int32_t normalized,
+                      const double* state_in, const double* z_in, int32_t flags,
                       double* y, double* state_out, double* z_out,
                       const int64_t* sample_idx, int64_t nsample, int32_t nthreads)
 {
@@ -333,7 +344,7 @@ int lao_prefill_f32in(const float* q, const float* k, const float* v,
             if (i && sample_idx[i] < sample_idx[i - 1]) return -1;
         }
     }
-    job_t J = {NULL, NULL, NULL, q, k, v, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+    job_t J = {NULL, NULL, NULL, q, k, v, cu_seqlens, nseq, H, d, flags, state_in, z_in,
                y, state_out, z_out, sample_idx, nsample, nthreads, 0, 0};
     return run_job(&J);
 }
@@ -342,12 +353,12 @@ int lao_prefill_f32in(const float* q, const float* k, const float* v,
  * same arguments as lao_prefill without sampling. */
 int lao_prefill_blocked(const double* q, const double* k, const double* v,
                         const int64_t* cu_seqlens, int32_t nseq, int32_t H, int32_t d,
-                        const double* state_in, const double* z_in, int32_t normalized,
+                        const double* state_in, const double* z_in, int32_t flags,
                         double* y, double* state_out, double* z_out,
                         int32_t block, int32_t fp32, int32_t nthreads)
 {
     if (!q || !k || !v || !y || H < 1 || d < 1 || block < 1 || check_cu(cu_seqlens, nseq)) return -1;
-    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, normalized, state_in, z_in,
+    job_t J = {q, k, v, NULL, NULL, NULL, cu_seqlens, nseq, H, d, flags, state_in, z_in,
                y, state_out, z_out, NULL, 0, nthreads, block, fp32 ? 1 : 0};
     return run_job(&J);
 }
@@ -356,10 +367,11 @@ int lao_prefill_blocked(const double* q, const double* k, const double* v,
  * updates S and z and reads its output from them).
  * q, k, v, y: [N, H, d]; S: [N, H, d, d] and z: [N, H, d] updated in place. */
 int lao_decode_step(const double* q, const double* k, const double* v,
-                    int32_t N, int32_t H, int32_t d, int32_t normalized,
+                    int32_t N, int32_t H, int32_t d, int32_t flags,
                     double* S, double* z, double* y)
 {
-    if (!q || !k || !v || !S || !y || (normalized && !z) || N < 0 || H < 1 || d < 1) return -1;
+    if (!q || !k || !v || !S || !y || ((flags & LAO_NORMALIZED) && !z) || N < 0 || H < 1 || d < 1)
+        return -1;
     double* a = (double*)malloc((size_t)d * sizeof(double));
     double* b = (double*)malloc((size_t)d * sizeof(double));
     double* c = (double*)malloc((size_t)d * sizeof(double));
@@ -367,8 +379,8 @@ int lao_decode_step(const double* q, const double* k, const double* v,
     if (!a || !b || !c || !zdummy) { free(a); free(b); free(c); free(zdummy); return -1; }
     for (int64_t p = 0; p < (int64_t)N * H; p++) {
         const size_t off = (size_t)p * d;
-        recurrent_token(q + off, k + off, v + off, d, normalized, S + (size_t)p * d * d,
-                        normalized ? z + off : zdummy, a, b, c, y + off);
+        recurrent_token(q + off, k + off, v + off, d, flags, S + (size_t)p * d * d,
+                        (flags & LAO_NORMALIZED) ? z + off : zdummy, a, b, c, y + off);
     }
     free(a); free(b); free(c); free(zdummy);
     return 0;

@@ -104,6 +104,12 @@ def _nthreads(n):
     return int(n) if n else max(1, os.cpu_count() or 1)
 
 
+def _flags(normalized, featurized):
+    """The C oracle's flags word: bit 0 normalised output, bit 1 the inputs
+    are already feature vectors (the feature map is not applied again)."""
+    return (1 if normalized else 0) | (2 if featurized else 0)
+
+
 def _cu_array(cu_seqlens, total):
     if cu_seqlens is None:
         return np.array([0, total], dtype=np.int64)
@@ -113,14 +119,16 @@ def _cu_array(cu_seqlens, total):
 
 
 def prefill(q, k, v, cu_seqlens=None, state_in=None, z_in=None, normalized=False,
-            sample_idx=None, nthreads=None):
+            featurized=False, sample_idx=None, nthreads=None):
     """Recurrent form, token by token, of the causal linear attention.
 
     q, k, v: [total_T, H, d] pre-activation values (a single sequence when
     ``cu_seqlens`` is None).  Returns (y, state_out, z_out) in fp64: y is
     [total_T, H, d], or [len(sample_idx), H, d] when ``sample_idx`` (sorted
     global token indices) is given; state_out [nseq, H, d, d]; z_out
-    [nseq, H, d] (zeros unless normalized or z_in given).
+    [nseq, H, d] (zeros unless normalized or z_in given).  With
+    ``featurized`` q, k, v are taken as feature vectors phi(.) already (the
+    feature map was applied where they were produced) and used as given.
     """
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -137,7 +145,7 @@ def prefill(q, k, v, cu_seqlens=None, state_in=None, z_in=None, normalized=False
     so = np.zeros((nseq, H, d, d))
     zo = np.zeros((nseq, H, d))
     rc = lib.lao_prefill(_ptr(q), _ptr(k), _ptr(v), cu.ctypes.data_as(_i64p), nseq, H, d,
-                         _ptr(si), _ptr(zi), int(bool(normalized)), _ptr(y), _ptr(so), _ptr(zo),
+                         _ptr(si), _ptr(zi), _flags(normalized, featurized), _ptr(y), _ptr(so), _ptr(zo),
                          None if sample_idx is None else sample_idx.ctypes.data_as(_i64p),
                          0 if sample_idx is None else len(sample_idx), _nthreads(nthreads))
     if rc != 0:
@@ -146,7 +154,7 @@ def prefill(q, k, v, cu_seqlens=None, state_in=None, z_in=None, normalized=False
 
 
 def prefill_blocked(q, k, v, block, cu_seqlens=None, state_in=None, z_in=None,
-                    normalized=False, fp32=False, nthreads=None):
+                    normalized=False, featurized=False, fp32=False, nthreads=None):
     """Blocked form (masked quadratic within blocks of ``block`` tokens, the
     carried state across blocks), in fp64 or fp32 arithmetic.  Same returns as
     :func:`prefill`.  Used to check block-size invariance."""
@@ -159,7 +167,7 @@ def prefill_blocked(q, k, v, block, cu_seqlens=None, state_in=None, z_in=None,
     so = np.zeros((nseq, H, d, d))
     zo = np.zeros((nseq, H, d))
     rc = lib.lao_prefill_blocked(_ptr(q), _ptr(k), _ptr(v), cu.ctypes.data_as(_i64p), nseq, H, d,
-                                 _ptr(_f64(state_in)), _ptr(_f64(z_in)), int(bool(normalized)),
+                                 _ptr(_f64(state_in)), _ptr(_f64(z_in)), _flags(normalized, featurized),
                                  _ptr(y), _ptr(so), _ptr(zo), int(block), int(bool(fp32)),
                                  _nthreads(nthreads))
     if rc != 0:
@@ -167,7 +175,7 @@ def prefill_blocked(q, k, v, block, cu_seqlens=None, state_in=None, z_in=None,
     return y, so, zo
 
 
-def decode_step(q, k, v, S, z=None, normalized=False):
+def decode_step(q, k, v, S, z=None, normalized=False, featurized=False):
     """One decode token per sequence.  q, k, v: [N, H, d]; S: [N, H, d, d];
     z: [N, H, d].  Returns (y, S_new, z_new); the inputs are not modified."""
     lib = _load()
@@ -176,7 +184,7 @@ def decode_step(q, k, v, S, z=None, normalized=False):
     S = _f64(S).copy()
     z = np.zeros((N, H, d)) if z is None else _f64(z).copy()
     y = np.zeros((N, H, d))
-    rc = lib.lao_decode_step(_ptr(q), _ptr(k), _ptr(v), N, H, d, int(bool(normalized)),
+    rc = lib.lao_decode_step(_ptr(q), _ptr(k), _ptr(v), N, H, d, _flags(normalized, featurized),
                              _ptr(S), _ptr(z), _ptr(y))
     if rc != 0:
         raise ValueError("lao_decode_step rejected its arguments")
@@ -203,10 +211,11 @@ def gate(y, x, w=None, group=0, eps=1e-6):
 
 
 def forward(q, k, v, x=None, w=None, cu_seqlens=None, state_in=None, z_in=None,
-            normalized=False, gated=False, norm_group=0, eps=1e-6, nthreads=None):
+            normalized=False, featurized=False, gated=False, norm_group=0, eps=1e-6, nthreads=None):
     """Whole path: recurrence, then (if gated) the RMSNorm * sigmoid gate.
     Returns (out [total_T, H*d], state_out, z_out) in fp64."""
-    y, so, zo = prefill(q, k, v, cu_seqlens, state_in, z_in, normalized, nthreads=nthreads)
+    y, so, zo = prefill(q, k, v, cu_seqlens, state_in, z_in, normalized, featurized,
+                        nthreads=nthreads)
     total, H, d = y.shape
     y = y.reshape(total, H * d)
     if gated:
@@ -227,7 +236,7 @@ def _f32(a):
 
 
 def prefill_sampled_f32(q, k, v, sample_idx, cu_seqlens=None, state_in=None, z_in=None,
-                        normalized=False, nthreads=None):
+                        normalized=False, featurized=False, nthreads=None):
     """:func:`prefill` at the listed tokens for float32-valued inputs (bf16 or
     fp32 values), widened to double one token at a time inside the oracle."""
     lib = _load()
@@ -241,7 +250,7 @@ def prefill_sampled_f32(q, k, v, sample_idx, cu_seqlens=None, state_in=None, z_i
     zo = np.zeros((nseq, H, d))
     fp = lambda a: a.ctypes.data_as(_fp32)
     rc = lib.lao_prefill_f32in(fp(q), fp(k), fp(v), cu.ctypes.data_as(_i64p), nseq, H, d,
-                               _ptr(_f64(state_in)), _ptr(_f64(z_in)), int(bool(normalized)),
+                               _ptr(_f64(state_in)), _ptr(_f64(z_in)), _flags(normalized, featurized),
                                _ptr(y), _ptr(so), _ptr(zo), sample_idx.ctypes.data_as(_i64p),
                                len(sample_idx), _nthreads(nthreads))
     if rc != 0:
@@ -250,13 +259,13 @@ def prefill_sampled_f32(q, k, v, sample_idx, cu_seqlens=None, state_in=None, z_i
 
 
 def forward_sampled(q, k, v, sample_idx, x=None, w=None, cu_seqlens=None, state_in=None,
-                    z_in=None, normalized=False, gated=False, norm_group=0, eps=1e-6,
+                    z_in=None, normalized=False, featurized=False, gated=False, norm_group=0, eps=1e-6,
                     nthreads=None):
     """The path's output only at the listed tokens (sorted global indices),
     for inputs too long to hold every fp64 output.  Returns (out [n, H*d],
     state_out, z_out)."""
     sample_idx = np.asarray(sample_idx, dtype=np.int64)
-    y, so, zo = prefill(q, k, v, cu_seqlens, state_in, z_in, normalized,
+    y, so, zo = prefill(q, k, v, cu_seqlens, state_in, z_in, normalized, featurized,
                         sample_idx=sample_idx, nthreads=nthreads)
     n, H, d = y.shape
     y = y.reshape(n, H * d)
