@@ -88,7 +88,10 @@ def inputs_digest(torch, tensors, span=4 << 20):
     return res
 
 
-def bench_prefill(args, torch, lib, _lib, inputs):
+def bench_prefill(args, torch, lib, _lib, inputs, featurized=False):
+    """The prefill step.  With ``featurized`` the same q, k, v values are
+    passed as feature vectors already (the library's features-given mode: the
+    feature map applied where they were produced), so the call skips SiLU."""
     w = inputs.WORKLOADS[args.workload]
     T, H, d = w.T, w.H, w.d
     log("generating %s inputs on the GPU (%s)" % (w.name, w.note))
@@ -97,7 +100,7 @@ def bench_prefill(args, torch, lib, _lib, inputs):
     dev = q.device
     out = torch.empty((1, T, H * d), dtype=torch.float32, device=dev)
     state_out = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
-    opt = _lib.options(block_size=args.block, gated=True)
+    opt = _lib.options(block_size=args.block, gated=True, featurized=featurized)
     nbytes = lib.la_prefill_workspace_bytes(1, T, H, d, _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32,
                                             ctypes.byref(opt))
     ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
@@ -117,7 +120,8 @@ def bench_prefill(args, torch, lib, _lib, inputs):
                             ws.data_ptr(), ws.numel(), ctypes.c_void_p(stream))
         _lib.check(st, "la_prefill")
 
-    log("prefill: chunk %d tokens, kernels %s; %d warmup + %d timed steps" % (chunk, names, W, K))
+    tag = "prefill (features given)" if featurized else "prefill"
+    log("%s: chunk %d tokens, kernels %s; %d warmup + %d timed steps" % (tag, chunk, names, W, K))
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
@@ -134,8 +138,8 @@ def bench_prefill(args, torch, lib, _lib, inputs):
             base = 2 * nk * i
             tot += ev.elapsed_ms(base + 2 * j, base + 2 * j + 1)
         per_kernel[name] = tot / K
-    log("prefill: %.3f ms/step; kernels (ms): %s" %
-        (ms_step, ", ".join("%s %.3f" % kv for kv in per_kernel.items())))
+    log("%s: %.3f ms/step; kernels (ms): %s" %
+        (tag, ms_step, ", ".join("%s %.3f" % kv for kv in per_kernel.items())))
     th = T * H
     res = {
         "T": T, "H": H, "d": d, "chunk": chunk, "block": plan.block_size,
@@ -605,6 +609,25 @@ def cpu_baseline(args, inputs):
                       "token-by-token recurrence; %.1f s" % (T, w.name, w.H, dt)}
 
 
+def features_given_summary(feat, main_name):
+    """The same workload with q, k, v passed as features (SiLU applied where
+    they were produced, e.g. in the projection's epilogue): per-kernel times
+    and the main pass's HBM fraction on the same algorithmic bytes."""
+    th = feat["token_heads"]
+    unit = 4 * 256 + 512 if main_name == "main_gated" else 3 * 256 + 512
+    nbytes = th * unit
+    if feat["T"] > feat["chunk"]:
+        nbytes += feat["main_workgroups"] * feat["d"] * feat["d"] * 4
+    ms = feat["per_kernel_ms"].get(main_name)
+    gbs = None if not ms else nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_step": feat["ms_per_step"], "tokens_per_s": feat["tokens_per_s"],
+            "per_kernel_ms": feat["per_kernel_ms"], "main_GBps": gbs,
+            "main_hbm_frac": None if gbs is None else gbs / HBM_PEAK_GBS,
+            "note": "same inputs taken as feature vectors: no SiLU in the path, exact single "
+                    "bf16 products for phi(q).phi(k), P.V's value side, Q.S's query side and "
+                    "the state update"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -613,6 +636,8 @@ def main():
     ap.add_argument("--workload", default="prefill_1m", choices=["prefill_1m", "prefill_32k"])
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-featurized", action="store_true",
+                    help="skip the prefill with inputs given as features")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 32K-token and varlen timings and the copy-bandwidth reference")
@@ -656,6 +681,8 @@ def main():
         return
 
     pre = bench_prefill(args, torch, lib, _lib, inputs)
+    feat = None if args.no_featurized else bench_prefill(args, torch, lib, _lib, inputs,
+                                                         featurized=True)
     dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
     other = serve = None
     if not args.no_extra:
@@ -746,6 +773,7 @@ def main():
         "other_prefill": other,
         "serving_step": serve,
         "softmax_layer": soft,
+        "features_given_prefill": None if feat is None else features_given_summary(feat, main_name),
     }
     print(json.dumps(line), flush=True)
 

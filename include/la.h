@@ -102,7 +102,15 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               e.g. a pool of per-request states updated in place (state_out
  *               = state_in).  Slots of one call must be distinct (not
  *               checked); a slot outside [0, state_rows) makes that sequence
- *               start from zero and write no state (decode: y = 0).          */
+ *               start from zero and write no state (decode: y = 0).
+ *   featurized  0 (default): q, k, v are pre-activations and the feature map
+ *               SiLU is applied inside ([Arch] 2.1).  1: q, k, v are feature
+ *               vectors already -- SiLU applied where they were produced,
+ *               e.g. in the epilogue of the projection GEMM -- and are used
+ *               as given.  Supported by the decode step and by the bf16
+ *               d = 128 prefill with block 32; other prefill configurations
+ *               return LA_ERR_UNSUPPORTED.  The gate's sigmoid(x) is the same
+ *               in both modes.                                               */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -114,6 +122,7 @@ typedef struct {
     int32_t n_timing;
     const int32_t* state_slots;
     int32_t state_rows;
+    int32_t featurized;
 } la_options_t;
 
 la_options_t la_default_options(void);

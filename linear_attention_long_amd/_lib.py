@@ -49,6 +49,7 @@ class Options(ctypes.Structure):
         ("n_timing", ctypes.c_int32),
         ("state_slots", ctypes.c_void_p),
         ("state_rows", ctypes.c_int32),
+        ("featurized", ctypes.c_int32),
     ]
 
 
@@ -190,7 +191,7 @@ def status_string(status: int) -> str:
 
 
 def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
-            chunk_tokens=0) -> Options:
+            chunk_tokens=0, featurized=False) -> Options:
     o = load().la_default_options()
     o.block_size = int(block_size)
     o.normalized = int(bool(normalized))
@@ -198,6 +199,7 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     o.norm_group = int(norm_group)
     o.rms_eps = float(rms_eps)
     o.chunk_tokens = int(chunk_tokens)
+    o.featurized = int(bool(featurized))
     return o
 
 

@@ -46,13 +46,15 @@ def _workspace(nbytes: int, device) -> torch.Tensor | None:
 
 def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=False,
                block_size=0, norm_group=0, rms_eps=1e-6, chunk_tokens=0,
-               out_dtype=torch.float32, return_state=True, stream=None):
+               out_dtype=torch.float32, return_state=True, featurized=False, stream=None):
     """Prefill of Bt equal-length sequences.
 
     q, k, v: [Bt, T, H, d] (or [T, H, d]) pre-activation, float32 or bfloat16.
     x: gate pre-activation [Bt, T, H*d] (same dtype) -> gated output, or None.
     w: RMSNorm weight [H*d] float32 or None.  state_in [Bt, H, d, d], z_in
     [Bt, H, d] float32 or None.  Returns (out [Bt, T, H*d], state_out, z_out).
+    ``featurized``: q, k, v are feature vectors already (SiLU applied where
+    they were produced); bfloat16 with d = 128 and block 32 only.
     """
     lib = _lib.load()
     squeeze = q.dim() == 3
@@ -68,7 +70,8 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
     if k.shape != q.shape or v.shape != q.shape or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must have the same shape and dtype")
     gated = x is not None
-    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens)
+    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens,
+                       featurized)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
     out = torch.empty((Bt, T, H * d), dtype=out_dtype, device=dev)
@@ -105,7 +108,7 @@ def _slots(opt, state_slots, pool):
 def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=None, z_in=None,
                       *, normalized=False, block_size=0, norm_group=0, rms_eps=1e-6,
                       chunk_tokens=0, out_dtype=torch.float32, return_state=True,
-                      state_slots=None, out=None, stream=None):
+                      state_slots=None, out=None, featurized=False, stream=None):
     """Prefill of a packed batch.  q, k, v: [total_T, H, d]; cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
     Returns (out [total_T, H*d], state_out [num_seqs, H, d, d], z_out).
@@ -118,7 +121,8 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
     if cu_seqlens.dtype != torch.int32:
         raise TypeError("cu_seqlens must be int32")
     gated = x is not None
-    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens)
+    opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens,
+                       featurized)
     _slots(opt, state_slots, state_in)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
@@ -145,7 +149,7 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
 
 def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, norm_group=0,
                    rms_eps=1e-6, out_dtype=torch.float32, out=None, workspace=None,
-                   state_slots=None, stream=None):
+                   state_slots=None, featurized=False, stream=None):
     """One decode token per sequence.  q, k, v: [N, H, d]; state [N, H, d, d]
     float32 and z [N, H, d] (normalised mode) are updated in place (with
     ``state_slots``, int32 [N] on the GPU: pools [rows, H, d, d] / [rows, H, d]
@@ -154,7 +158,7 @@ def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, 
     lib = _lib.load()
     N, H, d = q.shape
     gated = x is not None
-    opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0)
+    opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0, featurized)
     _slots(opt, state_slots, state)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     if out is None:

@@ -64,6 +64,7 @@ struct Opts {
     int n_events;
     const int32_t* slots;  // state row per sequence (device), or nullptr
     int rows;              // rows of the state arrays when slots is given
+    bool feat;             // q, k, v are feature vectors already (no SiLU inside)
 };
 
 // Records the caller's timing events around each launched kernel.
@@ -132,6 +133,8 @@ la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
     o.slots = x.state_slots;
     o.rows = x.state_slots ? x.state_rows : 0;
     if (x.state_slots && (x.state_rows < 1 || !aligned(x.state_slots, 4))) return LA_ERR_INVALID_ARGUMENT;
+    if (x.featurized != 0 && x.featurized != 1) return LA_ERR_INVALID_ARGUMENT;
+    o.feat = x.featurized == 1;
     return LA_OK;
 }
 
@@ -157,6 +160,19 @@ int64_t items_for(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_se
     return varlen ? total_T / C + num_seqs : num_seqs * ((max_seqlen + C - 1) / C);
 }
 
+// The fused main pass + gate for these options (32-token blocks).
+const void* fused_kernel(bool norm, bool f32_out, bool feat) {
+    if (feat)
+        return norm ? (f32_out ? (const void*)mf::k_prefill_fused<true, float, 32, true>
+                               : (const void*)mf::k_prefill_fused<true, uint16_t, 32, true>)
+                    : (f32_out ? (const void*)mf::k_prefill_fused<false, float, 32, true>
+                               : (const void*)mf::k_prefill_fused<false, uint16_t, 32, true>);
+    return norm ? (f32_out ? (const void*)mf::k_prefill_fused<true, float, 32>
+                           : (const void*)mf::k_prefill_fused<true, uint16_t, 32>)
+                : (f32_out ? (const void*)mf::k_prefill_fused<false, float, 32>
+                           : (const void*)mf::k_prefill_fused<false, uint16_t, 32>);
+}
+
 Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqlen, int H, int d,
                la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o) {
     Plan p{};
@@ -171,8 +187,7 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
     // (the fused gate normalises over all H*d features of a token)
     const bool fusable = o.gated && o.group == H * d && p.mfma && p.block == 32 &&
                          H <= mf::FUSE_HMAX && total_T > 0;
-    const void* fk = o.normalized ? (const void*)mf::k_prefill_fused<true, float, 32>
-                                  : (const void*)mf::k_prefill_fused<false, float, 32>;
+    const void* fk = fused_kernel(o.normalized, true, o.feat);
     const int64_t cap = fusable ? resident_capacity(fk) : 0;
     if (cap >= H) {
         const int64_t teams = cap / H;
@@ -293,8 +308,9 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     if (p.chunked) {
         tm.before();
         if (p.mfma) {
-            if (norm) mf::k_chunk_state<true><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
-            else mf::k_chunk_state<false><<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            const auto ck = norm ? (o.feat ? mf::k_chunk_state<true, true> : mf::k_chunk_state<true, false>)
+                                 : (o.feat ? mf::k_chunk_state<false, true> : mf::k_chunk_state<false, false>);
+            ck<<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
         } else if (d == 128) {
             if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
             else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
@@ -319,10 +335,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     // fused gate: one cooperative launch, every (chunk, head) workgroup resident
     if (p.fuse_ok) {
         const bool f32o = std::is_same<OutT, float>::value;
-        const void* kern = norm ? (f32o ? (const void*)mf::k_prefill_fused<true, float, 32>
-                                        : (const void*)mf::k_prefill_fused<true, uint16_t, 32>)
-                                : (f32o ? (const void*)mf::k_prefill_fused<false, float, 32>
-                                        : (const void*)mf::k_prefill_fused<false, uint16_t, 32>);
+        const void* kern = fused_kernel(norm, f32o, o.feat);
         uint64_t* xbuf = (uint64_t*)(ws + p.off_xbuf);
         const int64_t nw = p.xbuf_words;
         if (!p.chunked) {  // (a chunked call's scan cleared it)
@@ -368,7 +381,12 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         float* zo = z_out;
 #define LA_MF_MAIN(NN, YT, TBV) \
     mf::k_prefill_main<NN, YT, TBV><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
-        if (p.block == 32) {
+#define LA_MF_MAIN_F(NN, YT) \
+    mf::k_prefill_main<NN, YT, 32, true><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
+        if (o.feat) {  // (the plan admits block 32 only)
+            if (y_is_f32) { if (norm) LA_MF_MAIN_F(true, float); else LA_MF_MAIN_F(false, float); }
+            else { if (norm) LA_MF_MAIN_F(true, uint16_t); else LA_MF_MAIN_F(false, uint16_t); }
+        } else if (p.block == 32) {
             if (y_is_f32) { if (norm) LA_MF_MAIN(true, float, 32); else LA_MF_MAIN(false, float, 32); }
             else { if (norm) LA_MF_MAIN(true, uint16_t, 32); else LA_MF_MAIN(false, uint16_t, 32); }
         } else {
@@ -376,6 +394,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
             else { if (norm) LA_MF_MAIN(true, uint16_t, 64); else LA_MF_MAIN(false, uint16_t, 64); }
         }
 #undef LA_MF_MAIN
+#undef LA_MF_MAIN_F
     } else {
 #define LA_VALU_MAIN(DD, YT, NN)                                                                \
     vk::k_valu_main<DD, InT, YT, NN><<<grid, vk::NT, 0, st>>>(                                  \
@@ -422,11 +441,18 @@ la_status_t launch_prefill(const Plan& p, const Opts& o, la_dtype_t in_dtype, la
 }
 
 // Checks shared by both prefill entry points.
+// Inputs given as features are taken by the bf16 d = 128 matrix-core prefill
+// with 32-token blocks only (the library default there).
+bool feat_unsupported(const Opts& o, la_dtype_t in_dtype, int d) {
+    return o.feat && !(in_dtype == LA_DTYPE_BF16 && d == 128 && (o.block == 0 || o.block == 32));
+}
+
 la_status_t check_prefill_common(const void* q, const void* k, const void* v, const void* x_gate,
                                  const float* rms_weight, const float* state_in, const float* z_in,
                                  void* out, float* state_out, float* z_out, int64_t nseq,
                                  int64_t total_T, int H, int d, la_dtype_t in_dtype,
                                  la_dtype_t out_dtype, const Opts& o) {
+    if (feat_unsupported(o, in_dtype, d)) return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !out) return LA_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return LA_ERR_INVALID_ARGUMENT;
     if (o.gated && (!x_gate || !aligned(x_gate, 16))) return LA_ERR_INVALID_ARGUMENT;
@@ -476,6 +502,7 @@ la_options_t la_default_options(void) {
     o.n_timing = 0;
     o.state_slots = nullptr;
     o.state_rows = 0;
+    o.featurized = 0;
     return o;
 }
 
@@ -498,7 +525,7 @@ size_t la_prefill_workspace_bytes(int32_t Bt, int32_t T, int32_t H, int32_t d, l
     Opts o;
     if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return (size_t)-1;
     if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
-    if (parse_options(opt, H, d, o) != LA_OK) return (size_t)-1;
+    if (parse_options(opt, H, d, o) != LA_OK || feat_unsupported(o, in_dtype, d)) return (size_t)-1;
     return make_plan(false, Bt, (int64_t)Bt * T, T, H, d, in_dtype, out_dtype, o).total;
 }
 
@@ -509,7 +536,7 @@ size_t la_prefill_varlen_workspace_bytes(int32_t total_T, int32_t num_seqs, int3
     Opts o;
     if (num_seqs < 1 || total_T < 0 || max_seqlen < 0 || max_seqlen > total_T) return (size_t)-1;
     if (check_shape(H, d, in_dtype, out_dtype) != LA_OK) return (size_t)-1;
-    if (parse_options(opt, H, d, o) != LA_OK) return (size_t)-1;
+    if (parse_options(opt, H, d, o) != LA_OK || feat_unsupported(o, in_dtype, d)) return (size_t)-1;
     return make_plan(true, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o).total;
 }
 
@@ -537,6 +564,7 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, i
     Opts o;
     s = parse_options(opt, H, d, o);
     if (s != LA_OK) return s;
+    if (feat_unsupported(o, in_dtype, d)) return LA_ERR_UNSUPPORTED;
     const Plan p = make_plan(varlen != 0, num_seqs, total_T, max_seqlen, H, d, in_dtype, out_dtype, o);
     la_plan_t r;
     std::memset(&r, 0, sizeof(r));
@@ -681,7 +709,7 @@ static la_status_t decode_step_impl(bool launch, const void* q, const void* k, c
     do {                                                                                           \
         constexpr int SP = (!(NN) && (DD) == 128) ? kDecodeSplit : 1;                              \
         k_decode<DD, IT, OT, NN, SP><<<grid * SP, 256, 0, st>>>((const IT*)q, (const IT*)k,         \
-            (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H);                               \
+            (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H, o.feat ? 1 : 0);               \
     } while (0)
 #define LA_DEC_OUT(DD, IT)                                                                  \
     do {                                                                                    \

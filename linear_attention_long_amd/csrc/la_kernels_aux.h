@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
                                                 const InT* __restrict__ v, float* __restrict__ S,
                                                 float* __restrict__ z, OutT* __restrict__ y,
                                                 const int32_t* __restrict__ slots, int32_t rows,
-                                                int H) {
+                                                int H, int feat) {
     // SPLIT workgroups per (sequence, head), each owning D / SPLIT value
     // columns of the state (more, smaller workgroups stream better); the
     // normaliser is shared by all columns, so the normalised mode is unsplit
@@ -279,11 +279,16 @@ __global__ __launch_bounds__(256) void k_decode(const InT* __restrict__ q, const
         }
         spair = (size_t)r * H + h;
     }
+    // feat: the inputs are feature vectors already (no SiLU here)
     if (tid < D) {
-        fq[tid] = silu(load_as_f32<InT>(q + vb + tid));
-        fk[tid] = silu(load_as_f32<InT>(k + vb + tid));
+        const float xq = load_as_f32<InT>(q + vb + tid), xk = load_as_f32<InT>(k + vb + tid);
+        fq[tid] = feat ? xq : silu(xq);
+        fk[tid] = feat ? xk : silu(xk);
     }
-    if (tid < DC) fv[tid] = silu(load_as_f32<InT>(v + vb + c0 + tid));
+    if (tid < DC) {
+        const float xv = load_as_f32<InT>(v + vb + c0 + tid);
+        fv[tid] = feat ? xv : silu(xv);
+    }
     __syncthreads();
     float den_part = 0.f;
     if (NORM && tid < D) {

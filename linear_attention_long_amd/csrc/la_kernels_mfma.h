@@ -188,6 +188,18 @@ __device__ __forceinline__ void silu8(const uint4& w, float (&f)[8]) {
     f[7] = silu(bf16_hi_to_f32(w.w));
 }
 
+// Eight bf16 values as fp32 (no feature map: the inputs are features already).
+__device__ __forceinline__ void unpack8(const uint4& w, float (&f)[8]) {
+    f[0] = bf16_lo_to_f32(w.x);
+    f[1] = bf16_hi_to_f32(w.x);
+    f[2] = bf16_lo_to_f32(w.y);
+    f[3] = bf16_hi_to_f32(w.y);
+    f[4] = bf16_lo_to_f32(w.z);
+    f[5] = bf16_hi_to_f32(w.z);
+    f[6] = bf16_lo_to_f32(w.w);
+    f[7] = bf16_hi_to_f32(w.w);
+}
+
 __device__ __forceinline__ void store_split8(const float (&f)[8], uint16_t* dh, uint16_t* dl) {
     uint4 hi, lo;
     split2(f[0], f[1], hi.x, lo.x);
@@ -212,8 +224,9 @@ __device__ __forceinline__ void store_split8_a8(const float (&f)[8], uint16_t* d
 }
 
 // phi(k) and phi(v) of the block into LDS (hi/lo); with NORM, column sums of
-// phi(k) over the wave's rows into zpart[wave][col..col+7].
-template <bool NORM, int NJ>
+// phi(k) over the wave's rows into zpart[wave][col..col+7].  FEAT: k and v
+// are feature vectors already, exact in bf16: stored as they are, no low part.
+template <bool NORM, int NJ, bool FEAT = false>
 __device__ __forceinline__ void stage_kv(const uint4 (&rk)[NJ], const uint4 (&rv)[NJ],
                                          uint16_t* kh, uint16_t* kl, uint16_t* vh, uint16_t* vl,
                                          float* zpart, int tid) {
@@ -225,14 +238,22 @@ __device__ __forceinline__ void stage_kv(const uint4 (&rk)[NJ], const uint4 (&rv
     for (int j = 0; j < NJ; ++j) {
         const int r = (tid >> 4) + 16 * j;
         float f[8];
-        silu8(rk[j], f);
-        store_split8(f, kh + r * KS + col, kl + r * KS + col);
+        if constexpr (FEAT) {
+            *(uint4*)(kh + r * KS + col) = rk[j];
+            *(uint4*)(vh + r * KS + col) = rv[j];
+            if (NORM) unpack8(rk[j], f);
+        } else {
+            silu8(rk[j], f);
+            store_split8(f, kh + r * KS + col, kl + r * KS + col);
+        }
         if (NORM) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) zs[e] += f[e];
         }
-        silu8(rv[j], f);
-        store_split8(f, vh + r * KS + col, vl + r * KS + col);
+        if constexpr (!FEAT) {
+            silu8(rv[j], f);
+            store_split8(f, vh + r * KS + col, vl + r * KS + col);
+        }
     }
     if (NORM) {
 #pragma unroll
@@ -270,7 +291,7 @@ __device__ __forceinline__ bf16x8_t row_operand(const uint16_t* tile, int stride
 // nks*32 rows of the staged block (rows past the data are zero).
 // S[dkt][dvt]: C-layout tile, lane (g, c) holds dv = 32*wave + 16*dvt + c,
 // dk = 16*dkt + 4*g + i.
-template <int NKS>
+template <int NKS, bool FEAT = false>
 __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t* kh,
                                              const uint16_t* kl, const uint16_t* vh,
                                              const uint16_t* vl, int nks, int wave, int g, int c) {
@@ -282,17 +303,24 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
             for (int dvt = 0; dvt < 2; ++dvt) {
                 const int c0 = 32 * wave + 16 * dvt;
                 Vh[dvt] = tr_operand(vh, KS, 32 * ks, c0, g, c);
-                Vl[dvt] = tr_operand(vl, KS, 32 * ks, c0, g, c);
+                if constexpr (!FEAT) Vl[dvt] = tr_operand(vl, KS, 32 * ks, c0, g, c);
             }
 #pragma unroll
             for (int dkt = 0; dkt < 8; ++dkt) {
                 const bf16x8_t Kh = tr_operand(kh, KS, 32 * ks, 16 * dkt, g, c);
-                const bf16x8_t Kl = tr_operand(kl, KS, 32 * ks, 16 * dkt, g, c);
+                if constexpr (FEAT) {
+                    // bf16-exact features: one product is exact
 #pragma unroll
-                for (int dvt = 0; dvt < 2; ++dvt) {
-                    S[dkt][dvt] = mfma16x16x32(Kh, Vh[dvt], S[dkt][dvt]);
-                    S[dkt][dvt] = mfma16x16x32(Kh, Vl[dvt], S[dkt][dvt]);
-                    S[dkt][dvt] = mfma16x16x32(Kl, Vh[dvt], S[dkt][dvt]);
+                    for (int dvt = 0; dvt < 2; ++dvt)
+                        S[dkt][dvt] = mfma16x16x32(Kh, Vh[dvt], S[dkt][dvt]);
+                } else {
+                    const bf16x8_t Kl = tr_operand(kl, KS, 32 * ks, 16 * dkt, g, c);
+#pragma unroll
+                    for (int dvt = 0; dvt < 2; ++dvt) {
+                        S[dkt][dvt] = mfma16x16x32(Kh, Vh[dvt], S[dkt][dvt]);
+                        S[dkt][dvt] = mfma16x16x32(Kh, Vl[dvt], S[dkt][dvt]);
+                        S[dkt][dvt] = mfma16x16x32(Kl, Vh[dvt], S[dkt][dvt]);
+                    }
                 }
             }
         }
@@ -307,7 +335,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[8][2], const uint16_t*
 // the workgroup stages block n+1 (SiLU + split, vector ALU) into one buffer
 // while the state update of block n (matrix cores) reads the other, with
 // one barrier per step; raw k, v are loaded two blocks ahead.
-template <bool NORM>
+template <bool NORM, bool FEAT = false>
 __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, ItemMap map,
                                                        int H, float* __restrict__ buf,
@@ -336,7 +364,7 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     // block 0 staged, block 1 in registers
     load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, it.len), rs, tid);
     load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, it.len), rs, tid);
-    stage_kv<NORM, L::NJ>(rk, rv, sm.kh[0], sm.kl[0], sm.vh[0], sm.vl[0], sm.zpart[0], tid);
+    stage_kv<NORM, L::NJ, FEAT>(rk, rv, sm.kh[0], sm.kl[0], sm.vh[0], sm.vl[0], sm.zpart[0], tid);
     kb += (size_t)TB * rs;
     vb += (size_t)TB * rs;
     load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, it.len - TB), rs, tid);
@@ -357,8 +385,8 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
         const int n2 = it.len - (ti + 2) * TB;
         load_tile_buf<L::NJ>(nk, tile_rsrc(kb, rs, n2), rs, tid);
         load_tile_buf<L::NJ>(nv, tile_rsrc(vb, rs, n2), rs, tid);
-        state_update<1>(S, sm.kh[CUR], sm.kl[CUR], sm.vh[CUR], sm.vl[CUR], 1, wave, g, c);
-        stage_kv<NORM, L::NJ>(rk, rv, sm.kh[CUR ^ 1], sm.kl[CUR ^ 1], sm.vh[CUR ^ 1],
+        state_update<1, FEAT>(S, sm.kh[CUR], sm.kl[CUR], sm.vh[CUR], sm.vl[CUR], 1, wave, g, c);
+        stage_kv<NORM, L::NJ, FEAT>(rk, rv, sm.kh[CUR ^ 1], sm.kl[CUR ^ 1], sm.vh[CUR ^ 1],
                               sm.vl[CUR ^ 1], sm.zpart[CUR ^ 1], tid);
 #pragma unroll
         for (int j = 0; j < L::NJ; ++j) {
@@ -511,15 +539,21 @@ __device__ __forceinline__ void gather_finish(SmemMain<TB>& sm, const GateArgs<u
 }
 
 // phi(q) of the block into the Q tile (hi/lo); with NORM zq[row] = phi(q_row) . z.
-template <bool NORM, int NJ, typename SM>
+template <bool NORM, int NJ, typename SM, bool FEAT = false>
 __device__ __forceinline__ void stage_q(SM& sm, const uint4 (&rq)[NJ], int tid) {
     const int col = (tid & 15) * 8;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int r = (tid >> 4) + 16 * j;
         float f[8];
-        silu8(rq[j], f);
-        store_split8_a8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
+        if constexpr (FEAT) {
+            *(uint2*)(sm.qh + r * QS + col) = make_uint2(rq[j].x, rq[j].y);
+            *(uint2*)(sm.qh + r * QS + col + 4) = make_uint2(rq[j].z, rq[j].w);
+            if (NORM) unpack8(rq[j], f);
+        } else {
+            silu8(rq[j], f);
+            store_split8_a8(f, sm.qh + r * QS + col, sm.ql + r * QS + col);
+        }
         if (NORM) {
             float part = 0.f;
 #pragma unroll
@@ -539,7 +573,7 @@ __device__ __forceinline__ void stage_q(SM& sm, const uint4 (&rq)[NJ], int tid) 
 // given).  Unfused: Y goes to y[t][h*D + j].  Fused: the
 // gated output goes there instead; the heads of the chunk exchange each
 // block's per-token sums of y^2 (tag = block number + 1).  k16 must be 16.
-template <bool NORM, bool FUSE, typename OutT, typename InT, int TB>
+template <bool NORM, bool FUSE, typename OutT, typename InT, int TB, bool FEAT>
 __device__ __forceinline__ void process_item(
     SmemMain<TB>& sm, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const Item& it, int item, int H, int h,
@@ -603,7 +637,7 @@ __device__ __forceinline__ void process_item(
     load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, nv0), rs, tid);
     __syncthreads();  // z (normalised mode) is set
     // the Q tile of block n is staged at the end of block n-1 (here, block 0)
-    stage_q<NORM, L::NJ>(sm, rq, tid);
+    stage_q<NORM, L::NJ, SmemMain<TB>, FEAT>(sm, rq, tid);
 
     for (int ti = 0; ti < ntiles; ++ti) {
         const int64_t tt0 = it.t0 + (int64_t)ti * TB;
@@ -615,7 +649,7 @@ __device__ __forceinline__ void process_item(
         if constexpr (FUSE) {
             if (ti > 0) publish_ssq<TB>(sm, ga, H, h, (uint32_t)ti);
         }
-        stage_kv<NORM, L::NJ>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+        stage_kv<NORM, L::NJ, FEAT>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
         if (ti + 1 < ntiles) {
             const int nv1 = min(TB, it.len - (ti + 1) * TB);
             qb += (size_t)TB * rs;
@@ -641,13 +675,15 @@ __device__ __forceinline__ void process_item(
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     const bf16x8_t ah = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, 16);
-                    const bf16x8_t al = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
                     // run-time column steps: no merged K reads (they conflict at KS)
                     const bf16x8_t bh = row_operand(sm.kh, KS, 16 * kt + c, 2 * k16 * s, g, k16);
-                    const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 2 * k16 * s, g, k16);
                     a0 = mfma16x16x32(ah, bh, a0);
-                    a1 = mfma16x16x32(ah, bl, a1);
-                    a2 = mfma16x16x32(al, bh, a2);
+                    if constexpr (!FEAT) {
+                        const bf16x8_t al = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
+                        const bf16x8_t bl = row_operand(sm.kl, KS, 16 * kt + c, 2 * k16 * s, g, k16);
+                        a1 = mfma16x16x32(ah, bl, a1);
+                        a2 = mfma16x16x32(al, bh, a2);
+                    }
                 }
                 f32x4_t acc = a0 + (a1 + a2);
                 // acc[i]: query 16qt + 4g + i, key 16kt + c; keep key <= query
@@ -704,7 +740,7 @@ __device__ __forceinline__ void process_item(
                 for (int dvt = 0; dvt < 2; ++dvt) {
                     const int c0 = 32 * wave + 16 * dvt;
                     Ah[dvt] = tr_operand(sm.vh, KS, 32 * ks, c0, g, c);
-                    Al[dvt] = tr_operand(sm.vl, KS, 32 * ks, c0, g, c);
+                    if constexpr (!FEAT) Al[dvt] = tr_operand(sm.vl, KS, 32 * ks, c0, g, c);
                 }
 #pragma unroll
                 for (int qt = 0; qt < L::NQT; ++qt) {
@@ -715,7 +751,8 @@ __device__ __forceinline__ void process_item(
                         for (int dvt = 0; dvt < 2; ++dvt) {
                             acc[dvt][qt] = mfma16x16x32(Ah[dvt], bh, acc[dvt][qt]);
                             acc[dvt][qt] = mfma16x16x32(Ah[dvt], bl, acc[dvt][qt]);
-                            acc[dvt][qt] = mfma16x16x32(Al[dvt], bh, acc[dvt][qt]);
+                            if constexpr (!FEAT)
+                                acc[dvt][qt] = mfma16x16x32(Al[dvt], bh, acc[dvt][qt]);
                         }
                     }
                 }
@@ -740,12 +777,20 @@ __device__ __forceinline__ void process_item(
             for (int qt = 0; qt < L::NQT; ++qt) {
                 if (qt < nqt) {
                     const bf16x8_t Bh = row_operand(sm.qh, QS, 16 * qt + c, 32 * s, g, 16);
-                    const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
+                    if constexpr (FEAT) {
 #pragma unroll
-                    for (int dvt = 0; dvt < 2; ++dvt) {
-                        acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bh, acc[dvt][qt]);
-                        acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bl, acc[dvt][qt]);
-                        acc[dvt][qt] = mfma16x16x32(Al[dvt], Bh, acc[dvt][qt]);
+                        for (int dvt = 0; dvt < 2; ++dvt) {
+                            acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bh, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(Al[dvt], Bh, acc[dvt][qt]);
+                        }
+                    } else {
+                        const bf16x8_t Bl = row_operand(sm.ql, QS, 16 * qt + c, 32 * s, g, 16);
+#pragma unroll
+                        for (int dvt = 0; dvt < 2; ++dvt) {
+                            acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bh, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(Ah[dvt], Bl, acc[dvt][qt]);
+                            acc[dvt][qt] = mfma16x16x32(Al[dvt], Bh, acc[dvt][qt]);
+                        }
                     }
                 }
             }
@@ -789,7 +834,7 @@ __device__ __forceinline__ void process_item(
         // the state update first: its LDS reads then precede the writes
         // below, which the compiler cannot prove disjoint from them
         __builtin_amdgcn_s_setprio(1);
-        state_update<L::NKS>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
+        state_update<L::NKS, FEAT>(S, sm.kh, sm.kl, sm.vh, sm.vl, nks, wave, g, c);
         __builtin_amdgcn_s_setprio(0);
         if constexpr (FUSE) {
             // (for the first block nprev = 0: every store is dropped)
@@ -801,7 +846,7 @@ __device__ __forceinline__ void process_item(
             xb += (size_t)TB * rs;
         }
         // rq holds block ti+1 (stale past the last block: staged, never read)
-        stage_q<NORM, L::NJ>(sm, rq, tid);
+        stage_q<NORM, L::NJ, SmemMain<TB>, FEAT>(sm, rq, tid);
     }
     if constexpr (FUSE) {
         __syncthreads();
@@ -835,7 +880,7 @@ __device__ __forceinline__ void process_item(
 }
 
 // Unfused main pass: one workgroup per (chunk = blockIdx.x, head = blockIdx.y).
-template <bool NORM, typename OutT, int TB>
+template <bool NORM, typename OutT, int TB, bool FEAT = false>
 __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
@@ -845,7 +890,7 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
     Item it;
     if (!decode_item(map, blockIdx.x, it)) return;
     GateArgs<uint16_t> ga{};
-    process_item<NORM, false, OutT, uint16_t, TB>(sm, q, k, v, it, blockIdx.x, H, blockIdx.y,
+    process_item<NORM, false, OutT, uint16_t, TB, FEAT>(sm, q, k, v, it, blockIdx.x, H, blockIdx.y,
                                                    prefix, prefix_stride, state_in, z_in, y,
                                                    state_out, z_out, k16, ga);
 }
@@ -854,7 +899,7 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_main(
 // blockIdx.x % H).  Launched cooperatively: every workgroup is resident, so
 // the H heads of a chunk -- a team -- run together and their per-token sums
 // of y^2 meet in the exchange buffer.  Every wait is bounded.
-template <bool NORM, typename OutT, int TB>
+template <bool NORM, typename OutT, int TB, bool FEAT = false>
 __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_fused(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
@@ -866,7 +911,7 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_fused(
     Item it;
     if (!decode_item(map, item, it)) return;  // the whole team returns together
     GateArgs<uint16_t> ga{x, w, eps, xbuf, item, spin_limit};
-    process_item<NORM, true, OutT, uint16_t, TB>(sm, q, k, v, it, item, H, h, prefix,
+    process_item<NORM, true, OutT, uint16_t, TB, FEAT>(sm, q, k, v, it, item, H, h, prefix,
                                                   prefix_stride, state_in, z_in, out, state_out,
                                                   z_out, k16, ga);
 }

@@ -52,6 +52,26 @@ def test_default_options(lib):
     o = lib.la_default_options()
     assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (0, 0, 0, 0, 0)
     assert abs(o.rms_eps - 1e-6) < 1e-12
+    assert o.featurized == 0
+
+
+def test_featurized_inputs_supported_set(lib):
+    """Inputs given as features: the bf16 d = 128 prefill with 32-token blocks;
+    anything else is refused on the host before any device work."""
+    bad = ctypes.c_size_t(-1).value
+    bf, f32 = _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32
+    ok = _lib.options(featurized=True)
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(ok)) != bad
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, f32, f32, ctypes.byref(ok)) == bad
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 64, bf, f32, ctypes.byref(ok)) == bad
+    b64 = _lib.options(featurized=True, block_size=64)
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(b64)) == bad
+    odd = _lib.options()
+    odd.featurized = 2
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(odd)) == bad
+    r = _lib.Plan()
+    assert lib.la_prefill_plan(0, 1, 4096, 4096, 8, 64, bf, f32, 1, ctypes.byref(ok),
+                               ctypes.byref(r)) == _lib.LA_ERR_UNSUPPORTED
 
 
 def test_status_strings(lib):

@@ -1,0 +1,109 @@
+"""GPU parity of the features-given mode (q, k, v arrive as phi(.) already,
+e.g. from a projection whose epilogue applies SiLU) against the oracle's
+same mode, through the C ABI.
+
+The inputs are arbitrary bf16 feature vectors (the mode does not care how they
+were made): N(0, 1) / sqrt(d), and |N(0, 1)| / sqrt(d) for the normalised mode
+so that its denominators stay away from zero.  Tolerance: the bf16 bar,
+max|err| / rms(ref) <= 1e-2; with bf16-exact features the products are exact
+and the measured error is far below it (reported per case).
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_long_amd import api
+from oracle import oracle as O
+from tests._util import banner, np64, randn, rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+DEV = "cuda"
+D = 128
+
+
+def feats(shape, seed, positive=False):
+    x = randn(shape, seed, scale=D ** -0.5)
+    return (x.abs() if positive else x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("T,chunk,gated,odt", [(1000, 0, True, torch.float32),
+                                                (4101, 1024, True, torch.bfloat16),
+                                                (333, 0, False, torch.float32),
+                                                (1, 0, False, torch.float32),
+                                                (2048, 512, False, torch.float32)])
+def test_prefill_features_given(T, chunk, gated, odt):
+    banner("featurized prefill T=%d chunk=%d gated=%s out=%s" % (T, chunk, gated, odt))
+    H = 4
+    q, k, v = (feats((T, H, D), 300 + i) for i in range(3))
+    x = randn((T, H * D), 303).to(torch.bfloat16) if gated else None
+    S0 = randn((H, D, D), 304, scale=0.05)
+    out, S, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), None if x is None else x.to(DEV),
+                               state_in=S0.to(DEV), chunk_tokens=chunk, out_dtype=odt,
+                               featurized=True)
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(np64(q), np64(k), np64(v), None if x is None else np64(x),
+                             state_in=np64(S0)[None], gated=gated, featurized=True)
+    got = np64(out).reshape(T, H * D)
+    e_out = rel_err(got, ref)
+    e_S = rel_err(np64(S).reshape(H, D, D), Sref[0])
+    print("  out %.2e state %.2e" % (e_out, e_S))
+    if odt == torch.bfloat16:
+        # plus the output's own rounding to bf16, element by element
+        rms = np.sqrt(np.mean(ref * ref))
+        assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + TOL * rms).all()
+    else:
+        assert e_out <= TOL
+    assert e_S <= TOL
+
+
+def test_prefill_normalised_features_given():
+    banner("featurized prefill normalised T=1500")
+    T, H = 1500, 2
+    q, k, v = (feats((T, H, D), 310 + i, positive=True) for i in range(3))
+    out, S, z = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), normalized=True,
+                               chunk_tokens=512, featurized=True)
+    torch.cuda.synchronize()
+    ref, Sref, zref = O.forward(np64(q), np64(k), np64(v), normalized=True, featurized=True)
+    e = rel_err(np64(out).reshape(T, H * D), ref)
+    ez = rel_err(np64(z).reshape(H, D), zref[0])
+    print("  out %.2e z %.2e" % (e, ez))
+    assert e <= TOL and ez <= TOL
+
+
+def test_varlen_features_given():
+    banner("featurized varlen lengths 0,300,1,0,699,64 gated")
+    H = 8
+    lens = [0, 300, 1, 0, 699, 64]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q, k, v = (feats((T, H, D), 320 + i) for i in range(3))
+    x = randn((T, H * D), 323).to(torch.bfloat16)
+    out, S, _ = api.la_prefill_varlen(q.to(DEV), k.to(DEV), v.to(DEV), torch.tensor(cu, device=DEV),
+                                      max(lens), x.to(DEV), featurized=True)
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(np64(q), np64(k), np64(v), np64(x), cu_seqlens=cu, gated=True,
+                             featurized=True)
+    e, eS = rel_err(np64(out), ref), rel_err(np64(S), Sref)
+    print("  out %.2e state %.2e" % (e, eS))
+    assert e <= TOL and eS <= TOL
+
+
+@pytest.mark.parametrize("normalized", [False, True])
+def test_decode_features_given(normalized):
+    banner("featurized decode normalised=%s" % normalized)
+    N, H, steps = 4, 8, 20
+    S = randn((N, H, D, D), 330, scale=0.01).to(DEV)
+    z = (randn((N, H, D), 331).abs() + 1.0).to(DEV) if normalized else None
+    Sr = np64(S)
+    zr = None if z is None else np64(z)
+    for t in range(steps):
+        q, k, v = (feats((N, H, D), 340 + 3 * t + i, positive=normalized) for i in range(3))
+        y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S, z, normalized=normalized,
+                               featurized=True)
+        torch.cuda.synchronize()
+        yr, Sr, zr = O.decode_step(np64(q), np64(k), np64(v), Sr, zr, normalized=normalized,
+                                   featurized=True)
+        assert rel_err(np64(y).reshape(N, H, D), yr) <= 1e-5, t
+    assert rel_err(np64(S), Sr) <= 1e-5
