@@ -107,3 +107,33 @@ def test_decode_features_given(normalized):
                                    featurized=True)
         assert rel_err(np64(y).reshape(N, H, D), yr) <= 1e-5, t
     assert rel_err(np64(S), Sr) <= 1e-5
+
+
+def test_prefill_1m_features_given_sampled():
+    """The 1M-token workload in the launch configuration bench.py times for this
+    mode, its q, k, v values taken as features; sampled outputs (chunk and block
+    boundaries, whole 256-token blocks, seeded random tokens) and the final state."""
+    from linear_attention_long_amd import inputs
+    from tests.test_gpu_zlarge import chunk_tokens, sample_tokens
+
+    w = inputs.WORKLOADS["prefill_1m"]
+    banner("prefill_1m workload, features given (sampled)")
+    q, k, v, x = inputs.prefill_inputs(w, device="cuda")
+    out, S, _ = api.la_prefill(q, k, v, x, featurized=True)
+    torch.cuda.synchronize()
+    C, dev = chunk_tokens(False, 1, w.T, w.T, w.H, w.d)
+    idx = sample_tokens([0], [w.T], C, 4096, 17, every64=dev)
+    blocks = np.concatenate([np.arange(256 * b, 256 * (b + 1)) for b in (0, 63, 64, 2048, 4095)])
+    idx = np.union1d(idx, blocks).astype(np.int64)
+    got = np64(out[0, torch.from_numpy(idx).cuda()])
+    S_got = np64(S)
+    del out, S
+    qc, kc, vc = (t[0].float().cpu() for t in (q, k, v))
+    xs = x[0, torch.from_numpy(idx).cuda()].float().cpu()
+    del q, k, v, x
+    torch.cuda.empty_cache()
+    y, S_ref, _ = O.prefill_sampled_f32(qc, kc, vc, idx, featurized=True, nthreads=w.H)
+    ref = O.gate(y.reshape(len(idx), w.H * w.d), xs, None, 0, 1e-6)
+    e, eS = rel_err(got, ref), rel_err(S_got[0], S_ref[0])
+    print("  %d sampled tokens: out %.2e, state %.2e" % (len(idx), e, eS))
+    assert e <= TOL and eS <= TOL
