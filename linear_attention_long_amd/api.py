@@ -196,7 +196,8 @@ def la_schedule_step(remaining, max_batched_tokens=32768):
 
 def la_serve_step(q, k, v, state_pool, decode_slots, prefill_cu, prefill_slots, max_chunk,
                   x=None, w=None, z_pool=None, *, normalized=False, norm_group=0, rms_eps=1e-6,
-                  out_dtype=torch.float32, out=None, decode_stream=None, prefill_stream=None):
+                  out_dtype=torch.float32, out=None, decode_stream=None, prefill_stream=None,
+                  featurized=False):
     """One serving step (la_serve_step): rows [0, len(decode_slots)) of the
     packed q, k, v (and x) are decode tokens, the rest prefill chunks at
     prefill_cu (int32 on the GPU, relative offsets); decode_slots and
@@ -207,7 +208,7 @@ def la_serve_step(q, k, v, state_pool, decode_slots, prefill_cu, prefill_slots, 
     nd = decode_slots.numel() if decode_slots is not None else 0
     npf = prefill_slots.numel() if prefill_slots is not None else 0
     ptok = rows - nd
-    opt = _lib.options(0, normalized, x is not None, norm_group, rms_eps, 0)
+    opt = _lib.options(0, normalized, x is not None, norm_group, rms_eps, 0, featurized)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     if out is None:
         out = torch.empty((rows, H * d), dtype=out_dtype, device=q.device)
