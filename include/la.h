@@ -128,7 +128,8 @@ typedef struct {
 la_options_t la_default_options(void);
 
 /* Prefill of a batch of Bt equal-length sequences.
- *   q, k, v     [Bt, T, H, d]  in_dtype, pre-activation (SiLU applied inside)
+ *   q, k, v     [Bt, T, H, d]  in_dtype, pre-activation (SiLU applied inside), or
+ *                              features when opt->featurized = 1
  *   x_gate      [Bt, T, H*d]   in_dtype gate pre-activation; required iff gated
  *   rms_weight  [H*d] fp32 RMSNorm weight, or NULL for unit weight
  *   state_in    [Bt, H, d, d] fp32 initial state (key feature i, value
@@ -176,6 +177,7 @@ la_status_t la_prefill_varlen(const void* q, const void* k, const void* v,
  * updates the state and reads its output from it; [Deploy] 6: decode is a
  * call of its own).
  *   q, k, v     [N, H, d] in_dtype, one pre-activation token per sequence
+ *               (features when opt->featurized = 1)
  *   x_gate      [N, H*d] | NULL (required iff gated);  rms_weight [H*d] | NULL
  *   state       [N, H, d, d] fp32, updated IN PLACE (S <- S + phi(k) phi(v)^T)
  *   z           [N, H, d] fp32, updated in place; required iff normalized
