@@ -137,3 +137,33 @@ def test_prefill_1m_features_given_sampled():
     e, eS = rel_err(got, ref), rel_err(S_got[0], S_ref[0])
     print("  %d sampled tokens: out %.2e, state %.2e" % (len(idx), e, eS))
     assert e <= TOL and eS <= TOL
+
+
+def test_serve_step_features_given():
+    """One serving step (two decode tokens, two prompt chunks continuing from
+    pool rows) with the inputs given as features."""
+    banner("featurized serve step: 2 decode tokens + chunks of 100 and 37")
+    rows, H = 6, 4
+    dslots, pslots, lens = [1, 4], [0, 3], [100, 37]
+    nd, total = len(dslots), len(dslots) + sum(lens)
+    q, k, v = (feats((total, H, D), 350 + i) for i in range(3))
+    x = randn((total, H * D), 353).to(torch.bfloat16)
+    pool0 = randn((rows, H, D, D), 354, scale=0.05)
+    pool = pool0.to(DEV)
+    cu = torch.tensor([0, lens[0], lens[0] + lens[1]], dtype=torch.int32, device=DEV)
+    out = api.la_serve_step(q.to(DEV), k.to(DEV), v.to(DEV), pool,
+                            torch.tensor(dslots, dtype=torch.int32, device=DEV), cu,
+                            torch.tensor(pslots, dtype=torch.int32, device=DEV), max(lens),
+                            x.to(DEV), featurized=True)
+    torch.cuda.synchronize()
+    out = np64(out)
+    spans = [(n, n + 1, r) for n, r in enumerate(dslots)]
+    a = nd
+    for L, r in zip(lens, pslots):
+        spans.append((a, a + L, r))
+        a += L
+    for a, b, r in spans:
+        ref, Sref, _ = O.forward(np64(q[a:b]), np64(k[a:b]), np64(v[a:b]), np64(x[a:b]),
+                                 state_in=np64(pool0[r:r + 1]), gated=True, featurized=True)
+        assert rel_err(out[a:b], ref) <= TOL, (a, b)
+        assert rel_err(np64(pool[r]), Sref[0]) <= 1e-4, r

@@ -96,6 +96,28 @@ def test_prefill_writes_exactly_its_outputs(T, chunk, gated, odt):
     so.check("state_out")
 
 
+@pytest.mark.parametrize("T,chunk,gated,odt", [(1000, 256, True, torch.float32),
+                                                 (4101, 1024, False, torch.bfloat16)])
+def test_prefill_features_given_writes_exactly_its_outputs(T, chunk, gated, odt):
+    lib = _lib.load()
+    Bt, H, d = 2, 4, 128
+    s = 1.0 / np.sqrt(d)
+    q, k, v = (rnd((Bt, T, H, d), 50 + i, s) for i in range(3))
+    x = rnd((Bt, T, H * d), 53) if gated else None
+    out = Fenced((Bt, T, H * d), odt)
+    so = Fenced((Bt, H, d, d), torch.float32)
+    opt = _lib.options(gated=gated, chunk_tokens=chunk, featurized=True)
+    in_dt, out_dt = _lib.LA_DTYPE_BF16, (_lib.LA_DTYPE_BF16 if odt == torch.bfloat16
+                                         else _lib.LA_DTYPE_F32)
+    w = ws(lib.la_prefill_workspace_bytes(Bt, T, H, d, in_dt, out_dt, ctypes.byref(opt)))
+    st = lib.la_prefill(ptr(q), ptr(k), ptr(v), ptr(x), None, None, None, ptr(out.t), ptr(so.t),
+                        None, Bt, T, H, d, in_dt, out_dt, ctypes.byref(opt), ptr(w),
+                        0 if w is None else w.numel(), stream())
+    _lib.check(st, "la_prefill")
+    out.check("out")
+    so.check("state_out")
+
+
 def test_prefill_varlen_normalised_writes_exactly_its_outputs():
     lib = _lib.load()
     H, d = 2, 128
