@@ -107,10 +107,10 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               SiLU is applied inside ([Arch] 2.1).  1: q, k, v are feature
  *               vectors already -- SiLU applied where they were produced,
  *               e.g. in the epilogue of the projection GEMM -- and are used
- *               as given.  Supported by the decode step and by the bf16
- *               d = 128 prefill with block 32; other prefill configurations
- *               return LA_ERR_UNSUPPORTED.  The gate's sigmoid(x) is the same
- *               in both modes.                                               */
+ *               as given.  Supported by the decode step and by every prefill
+ *               configuration except bf16 d = 128 with block 64, which
+ *               returns LA_ERR_UNSUPPORTED.  The gate's sigmoid(x) is the
+ *               same in both modes.                                          */
 typedef struct {
     int32_t block_size;
     int32_t normalized;

@@ -312,11 +312,11 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
                                  : (o.feat ? mf::k_chunk_state<false, true> : mf::k_chunk_state<false, false>);
             ck<<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
         } else if (d == 128) {
-            if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
-            else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+            if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
+            else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
         } else {
-            if (norm) vk::k_valu_state<64, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
-            else vk::k_valu_state<64, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride);
+            if (norm) vk::k_valu_state<64, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
+            else vk::k_valu_state<64, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
         }
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
@@ -383,7 +383,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     mf::k_prefill_main<NN, YT, TBV><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
 #define LA_MF_MAIN_F(NN, YT) \
     mf::k_prefill_main<NN, YT, 32, true><<<grid, mf::NT, 0, st>>>(qb, kb, vb, map, H, buf, p.stride, state_in, z_in, (YT*)ydst, so, NN ? zo : nullptr, 16)
-        if (o.feat) {  // (the plan admits block 32 only)
+        if (o.feat) {  // (the checks admit block 32 only on this path)
             if (y_is_f32) { if (norm) LA_MF_MAIN_F(true, float); else LA_MF_MAIN_F(false, float); }
             else { if (norm) LA_MF_MAIN_F(true, uint16_t); else LA_MF_MAIN_F(false, uint16_t); }
         } else if (p.block == 32) {
@@ -399,7 +399,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
 #define LA_VALU_MAIN(DD, YT, NN)                                                                \
     vk::k_valu_main<DD, InT, YT, NN><<<grid, vk::NT, 0, st>>>(                                  \
         (const InT*)q, (const InT*)k, (const InT*)v, map, H, p.block, buf, p.stride, state_in,  \
-        z_in, (YT*)ydst, state_out, z_out)
+        z_in, (YT*)ydst, state_out, z_out, o.feat ? 1 : 0)
         if (d == 128) {
             if (y_is_f32) { if (norm) LA_VALU_MAIN(128, float, true); else LA_VALU_MAIN(128, float, false); }
             else { if (norm) LA_VALU_MAIN(128, uint16_t, true); else LA_VALU_MAIN(128, uint16_t, false); }
@@ -441,10 +441,11 @@ la_status_t launch_prefill(const Plan& p, const Opts& o, la_dtype_t in_dtype, la
 }
 
 // Checks shared by both prefill entry points.
-// Inputs given as features are taken by the bf16 d = 128 matrix-core prefill
-// with 32-token blocks only (the library default there).
+// Inputs given as features: every prefill configuration except the bf16
+// d = 128 matrix-core pass with 64-token blocks (its kernels have no such
+// variant).
 bool feat_unsupported(const Opts& o, la_dtype_t in_dtype, int d) {
-    return o.feat && !(in_dtype == LA_DTYPE_BF16 && d == 128 && (o.block == 0 || o.block == 32));
+    return o.feat && in_dtype == LA_DTYPE_BF16 && d == 128 && o.block == 64;
 }
 
 la_status_t check_prefill_common(const void* q, const void* k, const void* v, const void* x_gate,

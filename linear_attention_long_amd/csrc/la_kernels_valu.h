@@ -37,14 +37,17 @@ struct SmemState {
 };
 
 // phi of rows [0, nvalid) of a 32-row sub-tile of one head into LDS (fp32);
-// rows past nvalid are zero.
+// rows past nvalid are zero.  feat: the inputs are features already (no SiLU).
 template <int D, typename InT>
 __device__ __forceinline__ void load_sub(float* dst, const InT* __restrict__ src, int64_t t0,
-                                         int nvalid, int H, int h, int tid) {
+                                         int nvalid, int H, int h, int tid, int feat) {
     for (int e = tid; e < SUB * D; e += NT) {
         const int r = e / D, col = e % D;
         float x = 0.f;
-        if (r < nvalid) x = silu(load_as_f32<InT>(src + ((size_t)(t0 + r) * H + h) * D + col));
+        if (r < nvalid) {
+            x = load_as_f32<InT>(src + ((size_t)(t0 + r) * H + h) * D + col);
+            if (!feat) x = silu(x);
+        }
         dst[e] = x;
     }
 }
@@ -52,7 +55,8 @@ __device__ __forceinline__ void load_sub(float* dst, const InT* __restrict__ src
 template <int D, typename InT, bool NORM>
 __global__ __launch_bounds__(NT, 1) void k_valu_state(const InT* __restrict__ k,
                                                       const InT* __restrict__ v, ItemMap map, int H,
-                                                      float* __restrict__ buf, int64_t buf_stride) {
+                                                      float* __restrict__ buf, int64_t buf_stride,
+                                                      int feat) {
     constexpr int PER = D * D / NT;
     __shared__ SmemState<D> sm;
     const int tid = threadIdx.x, h = blockIdx.y;
@@ -68,8 +72,8 @@ __global__ __launch_bounds__(NT, 1) void k_valu_state(const InT* __restrict__ k,
     for (int r0 = 0; r0 < it.len; r0 += SUB) {
         const int n = min(SUB, it.len - r0);
         __syncthreads();
-        load_sub<D, InT>(sm.fk, k, it.t0 + r0, n, H, h, tid);
-        load_sub<D, InT>(sm.fv, v, it.t0 + r0, n, H, h, tid);
+        load_sub<D, InT>(sm.fk, k, it.t0 + r0, n, H, h, tid, feat);
+        load_sub<D, InT>(sm.fv, v, it.t0 + r0, n, H, h, tid, feat);
         __syncthreads();
 #pragma unroll 2
         for (int r = 0; r < SUB; ++r) {
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, ItemMap map,
     int H, int B, const float* __restrict__ prefix, int64_t prefix_stride,
     const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ y,
-    float* state_out, float* z_out) {
+    float* state_out, float* z_out, int feat) {
     constexpr int CPT = D / 8;          // output columns per thread
     constexpr int PER = D * D / NT;     // state elements per thread
     constexpr int DKS = NT / D;
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
             const int64_t tq = it.t0 + b0 + i * SUB;
             const int nq = min(SUB, blen - i * SUB);
             __syncthreads();
-            load_sub<D, InT>(sm.fq, q, tq, nq, H, h, tid);
+            load_sub<D, InT>(sm.fq, q, tq, nq, H, h, tid, feat);
             __syncthreads();
             float acc[CPT];
 #pragma unroll
@@ -143,8 +147,8 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
                 const int64_t tk = it.t0 + b0 + jj * SUB;
                 const int nk = min(SUB, blen - jj * SUB);
                 __syncthreads();
-                load_sub<D, InT>(sm.fk, k, tk, nk, H, h, tid);
-                load_sub<D, InT>(sm.fv, v, tk, nk, H, h, tid);
+                load_sub<D, InT>(sm.fk, k, tk, nk, H, h, tid, feat);
+                load_sub<D, InT>(sm.fv, v, tk, nk, H, h, tid, feat);
                 __syncthreads();
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -174,8 +178,8 @@ __global__ __launch_bounds__(NT, 1) void k_valu_main(
             const int64_t tk = it.t0 + b0 + jj * SUB;
             const int nk = min(SUB, blen - jj * SUB);
             __syncthreads();
-            load_sub<D, InT>(sm.fk, k, tk, nk, H, h, tid);
-            load_sub<D, InT>(sm.fv, v, tk, nk, H, h, tid);
+            load_sub<D, InT>(sm.fk, k, tk, nk, H, h, tid, feat);
+            load_sub<D, InT>(sm.fv, v, tk, nk, H, h, tid, feat);
             __syncthreads();
             float a[PER];
 #pragma unroll

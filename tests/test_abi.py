@@ -56,21 +56,22 @@ def test_default_options(lib):
 
 
 def test_featurized_inputs_supported_set(lib):
-    """Inputs given as features: the bf16 d = 128 prefill with 32-token blocks;
-    anything else is refused on the host before any device work."""
+    """Inputs given as features: every prefill configuration but the bf16
+    d = 128 matrix-core pass with 64-token blocks, which is refused on the host
+    before any device work."""
     bad = ctypes.c_size_t(-1).value
     bf, f32 = _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32
     ok = _lib.options(featurized=True)
     assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(ok)) != bad
-    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, f32, f32, ctypes.byref(ok)) == bad
-    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 64, bf, f32, ctypes.byref(ok)) == bad
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, f32, f32, ctypes.byref(ok)) != bad
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 64, bf, f32, ctypes.byref(ok)) != bad
     b64 = _lib.options(featurized=True, block_size=64)
     assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(b64)) == bad
     odd = _lib.options()
     odd.featurized = 2
     assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, bf, f32, ctypes.byref(odd)) == bad
     r = _lib.Plan()
-    assert lib.la_prefill_plan(0, 1, 4096, 4096, 8, 64, bf, f32, 1, ctypes.byref(ok),
+    assert lib.la_prefill_plan(0, 1, 4096, 4096, 8, 128, bf, f32, 1, ctypes.byref(b64),
                                ctypes.byref(r)) == _lib.LA_ERR_UNSUPPORTED
 
 

@@ -167,3 +167,20 @@ def test_serve_step_features_given():
                                  state_in=np64(pool0[r:r + 1]), gated=True, featurized=True)
         assert rel_err(out[a:b], ref) <= TOL, (a, b)
         assert rel_err(np64(pool[r]), Sref[0]) <= 1e-4, r
+
+
+@pytest.mark.parametrize("dtype,d,block", [(torch.float32, 64, 64), (torch.float32, 128, 32),
+                                           (torch.bfloat16, 128, 128), (torch.bfloat16, 64, 0)])
+def test_vector_path_features_given(dtype, d, block):
+    """The fp32 vector path (fp32 inputs, d = 64, blocks of 128 or 256) in the same mode."""
+    banner("featurized vector path dtype=%s d=%d block=%d" % (dtype, d, block))
+    T, H = 777, 2
+    q, k, v = (randn((T, H, d), 360 + i, scale=d ** -0.5).to(dtype) for i in range(3))
+    out, S, _ = api.la_prefill(q.to(DEV), k.to(DEV), v.to(DEV), block_size=block,
+                               chunk_tokens=256, featurized=True)
+    torch.cuda.synchronize()
+    ref, Sref, _ = O.forward(np64(q), np64(k), np64(v), featurized=True)
+    tol = 1e-5 if dtype == torch.float32 else TOL
+    e, eS = rel_err(np64(out).reshape(T, H * d), ref), rel_err(np64(S).reshape(H, d, d), Sref[0])
+    print("  out %.2e state %.2e" % (e, eS))
+    assert e <= tol and eS <= tol
