@@ -13,11 +13,15 @@ What it computes follows the pages (page title, then section):
 * "MiniMax-Text-01 405B MoE模型架构与训练策略解析", section 2.1: SiLU on Q, K
   and V; output RMSNorm(Y) * sigmoid(X).
 
-Every function here has pins in ``tests/test_oracle_pins.py`` that do not go
-through the oracle's own formula (brute-force masked quadratic form, closed
+Every function here has pins that do not go through the oracle's own formula:
+``tests/test_oracle_pins.py`` (brute-force masked quadratic form, closed
 forms for constant inputs, T = 1, the non-causal last row, state chaining,
 decode = prefill, varlen = per sequence, block-size invariance, gate
-invariants).  Nothing here is "parity unpinned".
+invariants), ``tests/test_oracle_featurized_pins.py`` (inputs given as
+features) and ``tests/test_oracle_sampled_f32_pins.py`` (the float-input
+sampled form: bit-for-bit equal to the fp64 recurrence and equal to the
+masked quadratic form across sequence boundaries, empty sequences, duplicate
+samples and carried states).  Nothing here is "parity unpinned".
 """
 from __future__ import annotations
 
