@@ -54,6 +54,21 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             self.arr[i] = ev.value
         self.n = n
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def close(self) -> None:
+        """Destroy the events (before the runtime is torn down at exit)."""
+        for i in range(self.n):
+            if self.arr[i]:
+                self.hip.hipEventDestroy(ctypes.c_void_p(self.arr[i]))
+                self.arr[i] = None
+        self.n = 0
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
     def ptr(self, offset: int = 0) -> ctypes.c_void_p:
         return ctypes.c_void_p(ctypes.addressof(self.arr) + offset * ctypes.sizeof(ctypes.c_void_p))
@@ -88,10 +103,12 @@ def inputs_digest(torch, tensors, span=4 << 20):
     return res
 
 
-def bench_prefill(args, torch, lib, _lib, inputs, featurized=False):
+def bench_prefill(args, torch, lib, _lib, inputs, featurized=False, keep_rows=0):
     """The prefill step.  With ``featurized`` the same q, k, v values are
     passed as feature vectors already (the library's features-given mode: the
-    feature map applied where they were produced), so the call skips SiLU."""
+    feature map applied where they were produced), so the call skips SiLU.
+    ``keep_rows``: a host copy of the output's first rows (of the last timed
+    step) is returned for the parity leg."""
     w = inputs.WORKLOADS[args.workload]
     T, H, d = w.T, w.H, w.d
     log("generating %s inputs on the GPU (%s)" % (w.name, w.note))
@@ -138,6 +155,7 @@ def bench_prefill(args, torch, lib, _lib, inputs, featurized=False):
             base = 2 * nk * i
             tot += ev.elapsed_ms(base + 2 * j, base + 2 * j + 1)
         per_kernel[name] = tot / K
+    ev.close()
     log("%s: %.3f ms/step; kernels (ms): %s" %
         (tag, ms_step, ", ".join("%s %.3f" % kv for kv in per_kernel.items())))
     th = T * H
@@ -148,6 +166,8 @@ def bench_prefill(args, torch, lib, _lib, inputs, featurized=False):
         "tokens_per_s": T / (ms_step * 1e-3), "per_kernel_ms": per_kernel, "token_heads": th,
         "inputs_sha256": digest,
     }
+    if keep_rows:
+        res["out_head"] = out[0, :keep_rows].cpu()
     del q, k, v, x, out, ws
     torch.cuda.empty_cache()
     return res
@@ -214,9 +234,63 @@ def bench_decode(args, torch, lib, _lib, inputs):
         }
         log("decode %s: kernel %.1f us/step median of %d (%.0f GB/s), loop %.1f us/step" %
             (key, kern * 1e3, len(per_step), res[key]["GBps"], loop * 1e3))
+    ev.close()
     del toks, S, z
     torch.cuda.empty_cache()
+    res["cold"] = bench_decode_cold(args, torch, lib, _lib, inputs)
     return res
+
+
+def bench_decode_cold(args, torch, lib, _lib, inputs, pools=4):
+    """The decode step with its state out of the Infinity Cache: step s
+    works on state pool s % pools (each the workload's 64 x 64 x 128 x 128
+    fp32 state, 256 MiB), so between two visits to a pool the other pools
+    stream 768 MiB through the 256 MB cache.  Plain mode, per-step kernel
+    times from HIP events."""
+    w = inputs.WORKLOADS["decode_64x64"]
+    N, H, d, steps = w.N, w.H, w.d, args.decode_steps
+    S0, _ = inputs.decode_state(w, device="cuda")
+    Ss = [S0.clone() for _ in range(pools)]
+    del S0
+    toks = [inputs.decode_token(w, s, device="cuda") for s in range(min(steps, 64))]
+    out = torch.empty((N, H * d), dtype=torch.float32, device="cuda")
+    opt = _lib.options(block_size=64)
+    stream = torch.cuda.current_stream().cuda_stream
+    per_step = []
+    with HipEvents(2 * steps) as ev:
+        def call(s, timed):
+            qs, ks, vs = toks[s % len(toks)]
+            opt.timing_events = ev.ptr(2 * s) if timed else None
+            opt.n_timing = 1 if timed else 0
+            st = lib.la_decode_step(qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), None, None,
+                                    Ss[s % pools].data_ptr(), None, out.data_ptr(), N, H, d,
+                                    _lib.LA_DTYPE_BF16, _lib.LA_DTYPE_F32, ctypes.byref(opt),
+                                    None, 0, ctypes.c_void_p(stream))
+            _lib.check(st, "la_decode_step")
+
+        for s in range(2 * pools):
+            call(s, False)
+        torch.cuda.synchronize()
+        for _trial in range(3):
+            for s in range(steps):
+                call(s, True)
+            torch.cuda.synchronize()
+            per_step += [ev.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)]
+    per_step.sort()
+    kern = per_step[len(per_step) // 2]
+    nbytes = 2 * N * H * d * d * 4 + 3 * N * H * d * 2 + N * H * d * 4
+    gbs = nbytes / (kern * 1e-3) / 1e9
+    log("decode cold (%d rotating state pools, %d MiB): kernel %.1f us/step (%.0f GB/s)"
+        % (pools, pools * N * H * d * d * 4 >> 20, kern * 1e3, gbs))
+    del Ss, toks, out
+    torch.cuda.empty_cache()
+    return {"pools": pools, "state_bytes_total": pools * N * H * d * d * 4,
+            "kernel_us": kern * 1e3, "steps": 3 * steps, "bytes_per_step": nbytes, "GBps": gbs,
+            "hbm_frac": gbs / HBM_PEAK_GBS,
+            "note": "step s updates state pool s %% %d in place: each pool is the decode "
+                    "workload's 256 MiB state, so consecutive visits to a pool are 768 MiB of "
+                    "other state traffic apart and the 256 MB Infinity Cache cannot hold it"
+                    % pools}
 
 
 def bench_other_prefill(args, torch, api, inputs):
@@ -392,8 +466,12 @@ def bench_serving(args, torch, api, inputs, reps=50):
 
 
 # (workload, timed calls, precision option: 0 single bf16 operands, 1 split)
-SOFTMAX_WORKLOADS = (("softmax_32k", 20, 0), ("softmax_varlen_512k", 5, 0), ("softmax_1m", 2, 0),
-                     ("softmax_32k", 10, 1), ("softmax_varlen_512k", 3, 1))
+# (workload, timed calls, precision): 1 = split operands (the library's
+# default, within 1e-2 of the output's rms), 0 = single bf16 operands
+SOFTMAX_WORKLOADS = (("softmax_32k", 10, 1), ("softmax_varlen_512k", 3, 1), ("softmax_1m", 1, 1),
+                     ("softmax_32k", 20, 0), ("softmax_varlen_512k", 5, 0))
+SINGLE_NOTE = ("single bf16 operands: about 1e-3 of the values' scale, which on long rows exceeds "
+               "the 1e-2-of-output-rms bound for bf16 inputs (not the library default)")
 
 
 def softmax_flops(cu):
@@ -411,7 +489,7 @@ def bench_softmax(args, torch, lib, _lib, inputs):
     for name, reps, prec in SOFTMAX_WORKLOADS:
         if name == "softmax_1m" and args.no_softmax_1m:
             continue
-        key = name + ("_split" if prec else "")
+        key = name + ("" if prec else "_single")
         w = inputs.WORKLOADS[name]
         q, k, v, cu = inputs.softmax_inputs(w, device="cuda")
         cud = cu.cuda()
@@ -452,10 +530,12 @@ def bench_softmax(args, torch, lib, _lib, inputs):
         for j, kn in enumerate(names):
             per[kn] = sum(ev.elapsed_ms(2 * nk * i + 2 * j, 2 * nk * i + 2 * j + 1)
                           for i in range(1, reps + 1)) / reps
+        ev.close()
         att = per["attention"]
         res[key] = {"tokens": T, "sequences": nseq, "max_seqlen": maxlen, "H": H, "Hkv": Hkv,
                     "d": d, "rotary_dim": w.extra["rotary_dim"], "rope_base": w.extra["rope_base"],
-                    "precision": "split bf16 hi+lo operands" if prec else "single bf16 operands",
+                    "precision": ("split bf16 hi+lo operands (default; within 1e-2 of the "
+                                  "output's rms)") if prec else SINGLE_NOTE,
                     "ms_per_call": ms, "per_kernel_ms": per, "algorithmic_flops": flops,
                     "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
                     "call_TFLOPs": flops / (ms * 1e-3) / 1e12,
@@ -465,6 +545,93 @@ def bench_softmax(args, torch, lib, _lib, inputs):
                                 100 * res[key]["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS))
         del q, k, v, cud, out, ws
         torch.cuda.empty_cache()
+    return res
+
+
+def bench_projection(args, torch, lib, _lib, inputs):
+    """The layer's input projection (include/la_proj.h): the GEMM kernel on
+    proj_32k (HIP events around each launch; algorithmic flops 2 T K 4F), and
+    the layer's input side end to end on 32K and 1M tokens: the projection
+    with SiLU in its epilogue followed by the path in its features-given mode,
+    against the raw projection followed by the path's own SiLU."""
+    from linear_attention_long_amd import api
+
+    res = {}
+    w = inputs.WORKLOADS["proj_32k"]
+    h, wt = inputs.projection_inputs(w, device="cuda")
+    T, K = h.shape
+    H, d = w.H, w.d
+    F = H * d
+    outs = [torch.empty((T, F), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    reps = 20
+    stream = torch.cuda.current_stream().cuda_stream
+    opt = _lib.proj_options(True)
+    with HipEvents(2 * (reps + 1)) as ev:
+        def call(i):
+            opt.timing_events = ev.ptr(2 * i)
+            opt.n_timing = 1
+            st = lib.la_qkvx_projection(h.data_ptr(), wt.data_ptr(), outs[0].data_ptr(),
+                                        outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(),
+                                        T, K, F, _lib.LA_DTYPE_BF16, ctypes.byref(opt),
+                                        ctypes.c_void_p(stream))
+            _lib.check(st, "la_qkvx_projection")
+
+        call(0)
+        torch.cuda.synchronize()
+        for i in range(1, reps + 1):
+            call(i)
+        torch.cuda.synchronize()
+        times = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(1, reps + 1))
+    ms = times[len(times) // 2]
+    flops = 2.0 * T * K * 4 * F
+    tfs = flops / (ms * 1e-3) / 1e12
+    res["kernel"] = {"workload": w.name, "T": T, "K": K, "F": F, "out": "bf16 q, k, v (SiLU), gate",
+                     "kernel_ms": ms, "kernel_ms_mean": sum(times) / len(times),
+                     "algorithmic_flops": flops, "TFLOPs": tfs,
+                     "mfma_bf16_peak_frac": tfs / MFMA_BF16_PEAK_TFS, "reps": reps}
+    log("projection %s: %.3f ms, %.0f TFLOP/s = %.1f%% of the bf16 peak"
+        % (w.name, ms, tfs, 100 * tfs / MFMA_BF16_PEAK_TFS))
+    del outs
+    layer = {}
+    for name, nrep in (("proj_32k", 10), ("proj_1m", 3)):
+        wl = inputs.WORKLOADS[name]
+        if name != w.name:
+            del h, wt
+            torch.cuda.empty_cache()
+            h, wt = inputs.projection_inputs(wl, device="cuda")
+        T = h.shape[0]
+        o4 = [torch.empty((T, F), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+
+        def side(feat):
+            q, k, v, xg = api.la_qkvx_projection(h, wt, F, featurize=feat, out=o4)
+            return api.la_prefill(q.view(1, T, H, d), k.view(1, T, H, d), v.view(1, T, H, d),
+                                  xg.view(1, T, F), featurized=feat, return_state=False)[0]
+
+        entry = {}
+        for key, feat in (("silu_in_projection", True), ("silu_in_path", False)):
+            side(feat)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(nrep):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                side(feat)
+                b.record()
+                b.synchronize()
+                ts.append(a.elapsed_time(b))
+            ts.sort()
+            entry[key + "_ms"] = ts[len(ts) // 2]
+        entry["tokens"] = T
+        entry["tokens_per_s_silu_in_projection"] = T / (entry["silu_in_projection_ms"] * 1e-3)
+        layer[name] = entry
+        log("layer input side %s: projection + path %.3f ms with SiLU in the projection's "
+            "epilogue, %.3f ms with SiLU in the path" % (name, entry["silu_in_projection_ms"],
+                                                        entry["silu_in_path_ms"]))
+        del o4
+        torch.cuda.empty_cache()
+    res["layer_input_side"] = layer
+    del h, wt
+    torch.cuda.empty_cache()
     return res
 
 
@@ -587,26 +754,43 @@ def measured_softmax_traffic():
     return float(vals["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(args, inputs):
-    """The oracle (plain fp64 C) on the first tokens of the same workload."""
+def cpu_baseline(args, inputs, gpu_head=None):
+    """The oracle (plain fp64 C) on the first tokens of the same workload.
+    With ``gpu_head`` (the benched call's output for those tokens, on the
+    host) it also reports the parity of the benched configuration: causal,
+    so the first tokens' outputs do not depend on the rest."""
+    import numpy as np
     import torch
 
     from oracle import oracle as O
 
     w = inputs.WORKLOADS[args.workload]
     T = args.cpu_tokens
-    q, k, v, x = inputs.prefill_inputs(w, T=T, device="cuda")
-    q, k, v, x = (t.cpu() for t in (q, k, v, x))
+    # the benched call's own inputs, cut to their first T tokens (a shorter
+    # draw on the GPU would not be a prefix of them)
+    q, k, v, x = inputs.prefill_inputs(w, device="cuda")
+    q, k, v, x = (t[:, :T].cpu() for t in (q, k, v, x))
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     threads = min(os.cpu_count() or 1, w.H)
     log("cpu baseline: oracle on %d tokens x %d heads with %d threads" % (T, w.H, threads))
     t0 = time.perf_counter()
-    O.forward(q[0], k[0], v[0], x[0], gated=True, nthreads=threads)
+    ref, _, _ = O.forward(q[0], k[0], v[0], x[0], gated=True, nthreads=threads)
     dt = time.perf_counter() - t0
     log("cpu baseline: %.2f s -> %.0f tokens/s" % (dt, T / dt))
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d tokens of the %s workload, all %d heads, gated; fp64 "
-                      "token-by-token recurrence; %.1f s" % (T, w.name, w.H, dt)}
+    res = {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "first %d tokens of the %s workload, all %d heads, gated; fp64 "
+                     "token-by-token recurrence; %.1f s" % (T, w.name, w.H, dt)}
+    parity = None
+    if gpu_head is not None:
+        got = gpu_head.numpy().astype(np.float64)
+        err = float(np.abs(got - ref).max() / np.sqrt(np.mean(ref * ref)))
+        parity = {"max_abs_err_over_rms": err, "bound": 1e-2, "pass": bool(err <= 1e-2),
+                  "elements": int(ref.size),
+                  "compared": "every output of the first %d tokens (all %d heads) of the benched "
+                              "call against the oracle above" % (T, w.H)}
+        log("parity of the benched call: max|err|/rms %.2e over %d outputs" % (err, ref.size))
+    return res, parity
 
 
 def features_given_summary(feat, main_name):
@@ -649,6 +833,10 @@ def main():
     ap.add_argument("--softmax-only", action="store_true",
                     help="only time the softmax layer's workloads (for profiling its kernels); "
                          "prints their JSON instead of the benchmark line")
+    ap.add_argument("--no-projection", action="store_true",
+                    help="skip the input projection GEMM and the layer input side")
+    ap.add_argument("--projection-only", action="store_true",
+                    help="only time the input projection (prints its JSON)")
     ap.add_argument("--block", type=int, default=0, help="block size (0 = library default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes --steps times "
@@ -675,12 +863,18 @@ def main():
         return
     lib = _lib.load()
     log("device: %s" % torch.cuda.get_device_name(0))
+    if args.projection_only:
+        print(json.dumps({"projection": bench_projection(args, torch, lib, _lib, inputs)}),
+              flush=True)
+        return
     if args.softmax_only:
         print(json.dumps({"softmax_layer": bench_softmax(args, torch, lib, _lib, inputs)}),
               flush=True)
         return
 
-    pre = bench_prefill(args, torch, lib, _lib, inputs)
+    keep = 0 if args.no_cpu_baseline else args.cpu_tokens
+    pre = bench_prefill(args, torch, lib, _lib, inputs, keep_rows=keep)
+    head = pre.pop("out_head", None)
     feat = None if args.no_featurized else bench_prefill(args, torch, lib, _lib, inputs,
                                                          featurized=True)
     dec = None if args.no_decode else bench_decode(args, torch, lib, _lib, inputs)
@@ -696,16 +890,19 @@ def main():
             for key in dec:
                 dec[key]["device_copy_GBps"] = cgbs
                 dec[key]["frac_of_copy"] = dec[key]["GBps"] / cgbs
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, inputs)
+    proj = None if args.no_projection else bench_projection(args, torch, lib, _lib, inputs)
+    cpu, parity = (None, None) if args.no_cpu_baseline else cpu_baseline(args, inputs, head)
+    del head
     soft = None
     if not args.no_softmax:
         soft = bench_softmax(args, torch, lib, _lib, inputs)
-        lead = soft["softmax_32k"]
+        lead = soft["softmax_32k"]   # the default (split-operand) mode
         att_ms = lead["per_kernel_ms"]["attention"]
         soft_traffic = measured_softmax_traffic()
         soft = {
             "workloads": soft,
-            "roofline": {"bound": "mfma", "kernel": "attention (k_sm_attn), softmax_32k",
+            "roofline": {"bound": "mfma",
+                         "kernel": "attention (k_sm_attn), softmax_32k, split operands (default)",
                          "achieved": lead["attention_TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": lead["attention_TFLOPs"] / MFMA_BF16_PEAK_TFS,
                          "traffic": soft_traffic,
@@ -739,6 +936,9 @@ def main():
     B, d = pre["block"], pre["d"]
     flops = th * (2 * (B + 1) * d + 4 * d * d)
     tflops = flops / (pre["ms_per_step"] * 1e-3) / 1e12
+    # the same count at the pages' block of 256 tokens (131,328 per token-head
+    # at d = 128): more intra-block work for the same result
+    tflops256 = th * (2 * 257 * d + 4 * d * d) / (pre["ms_per_step"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": pre["tokens_per_s"],
@@ -765,14 +965,26 @@ def main():
                      "algorithmic_bytes_per_launch": main_bytes,
                      "avg_launch_ms": main_ms},
         "cpu_baseline": cpu,
+        "parity": parity,
         "prefill": {"per_kernel_ms": pre["per_kernel_ms"], "path_min_bytes_GBps": path_gbs,
                     "inputs_sha256": pre["inputs_sha256"],
                     "path_hbm_roofline_frac": path_gbs / HBM_PEAK_GBS,
-                    "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS},
+                    "algorithmic_TFLOPs": tflops, "mfma_bf16_peak_frac": tflops / MFMA_BF16_PEAK_TFS,
+                    "flops_per_token_head": 2 * (B + 1) * d + 4 * d * d,
+                    "algorithmic_TFLOPs_at_block_256": tflops256,
+                    "mfma_bf16_peak_frac_at_block_256": tflops256 / MFMA_BF16_PEAK_TFS},
         "decode": dec,
         "other_prefill": other,
         "serving_step": serve,
         "softmax_layer": soft,
+        "projection": None if proj is None else {
+            "roofline": {"bound": "mfma", "kernel": "input projection GEMM (k_proj), proj_32k",
+                         "achieved": proj["kernel"]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": proj["kernel"]["mfma_bf16_peak_frac"],
+                         "traffic": None,
+                         "algorithmic_flops_per_launch": proj["kernel"]["algorithmic_flops"],
+                         "avg_launch_ms": proj["kernel"]["kernel_ms"]},
+            **proj},
         "features_given_prefill": None if feat is None else features_given_summary(feat, main_name),
     }
     print(json.dumps(line), flush=True)

@@ -60,7 +60,10 @@ typedef enum {
     LA_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, bad size, bad option */
     LA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (e.g. d not in {64,128}) */
     LA_ERR_WORKSPACE_TOO_SMALL = 3,
-    LA_ERR_HIP = 4                 /* a HIP launch failed */
+    LA_ERR_HIP = 4,                /* a HIP launch failed */
+    LA_ERR_WAIT_TIMEOUT = 5        /* la_prefill_wait_status only: a bounded
+                                      device wait of the call gave up; the
+                                      rows it could not finish hold NaN */
 } la_status_t;
 
 typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
@@ -110,7 +113,16 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               as given.  Supported by the decode step and by every prefill
  *               configuration except bf16 d = 128 with block 64, which
  *               returns LA_ERR_UNSUPPORTED.  The gate's sigmoid(x) is the
- *               same in both modes.                                          */
+ *               same in both modes.
+ *   wait_spin_limit
+ *               bound of the fused gate's waits for the other heads' sums
+ *               (retries per wait, each after a short sleep): 0 = library
+ *               default (2^22, seconds); > 0 = that many; -1 = give up at
+ *               once (every wait fails: a deterministic way to test the
+ *               failure path).  A wait that gives up never returns data
+ *               it could not verify: the rows it gates get NaN and the
+ *               call's device status word is set (la_prefill_wait_status).
+ *               Other values: LA_ERR_INVALID_ARGUMENT.                        */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -123,11 +135,17 @@ typedef struct {
     const int32_t* state_slots;
     int32_t state_rows;
     int32_t featurized;
+    int32_t wait_spin_limit;
 } la_options_t;
 
 la_options_t la_default_options(void);
 
-/* Prefill of a batch of Bt equal-length sequences.
+/* Prefill of a batch of Bt equal-length sequences: for each sequence and head
+ * the causal recurrence of [Tut] 3 (state updated with token t before y_t is
+ * read, so the sum runs over i <= t), evaluated in blocks as [Arch] 2.1's
+ * Q (K^T V) across blocks plus the masked quadratic form inside a block, with
+ * SiLU on q, k, v and the RMSNorm * sigmoid gate of [Arch] 2.1; [Deploy] 3's
+ * chunked prefill continues a sequence through state_in / state_out.
  *   q, k, v     [Bt, T, H, d]  in_dtype, pre-activation (SiLU applied inside), or
  *                              features when opt->featurized = 1
  *   x_gate      [Bt, T, H*d]   in_dtype gate pre-activation; required iff gated
@@ -153,7 +171,11 @@ la_status_t la_prefill(const void* q, const void* k, const void* v,
                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Prefill of a packed batch of variable-length sequences; the state starts
- * from state_in[s] (or zero) at each sequence start cu_seqlens[s].
+ * from state_in[s] (or zero) at each sequence start cu_seqlens[s].  Per
+ * sequence it computes exactly what la_prefill computes ([Tut] 3 recurrence,
+ * [Arch] 2.1 feature map, blocked product and gate); the packing of several
+ * requests into one call is [Deploy] 3's batching of prefill work under a
+ * token budget.
  *   q, k, v     [total_T, H, d] in_dtype, sequences back to back
  *   x_gate      [total_T, H*d] | NULL;  rms_weight [H*d] | NULL
  *   cu_seqlens  DEVICE int32 [num_seqs + 1]: 0 = c_0 <= c_1 <= ... = total_T.
@@ -236,6 +258,10 @@ typedef struct {
                                  at once -- so chunk_tokens is an upper bound */
     int32_t n_kernels;        /* kernels launched, <= 8 */
     int32_t kernels[8];       /* la_kernel_t values, launch order */
+    int64_t status_offset;    /* byte offset in the call's workspace of its
+                                 device status word (set when a bounded wait
+                                 gave up; see la_prefill_wait_status), or -1
+                                 when the plan has no such wait */
 } la_plan_t;
 
 /* Fills *plan for a la_prefill (varlen = 0: num_seqs = Bt, total_T = Bt*T,
@@ -252,6 +278,18 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T,
                             la_dtype_t in_dtype, la_dtype_t out_dtype,
                             int32_t has_state_out, const la_options_t* opt,
                             la_plan_t* plan);
+
+/* Outcome of the bounded waits of a finished prefill call whose plan has a
+ * status word (la_plan_t.status_offset >= 0, i.e. the fused gate, whose heads
+ * wait for each other's per-token sums).  Synchronises hip_stream, then reads
+ * the word from `workspace` (the call's workspace, not reused since):
+ * LA_OK when every wait succeeded, LA_ERR_WAIT_TIMEOUT when one gave up (the
+ * rows it gated hold NaN), LA_ERR_HIP when the read fails.  status_offset < 0
+ * returns LA_OK at once; a NULL workspace with status_offset >= 0 returns
+ * LA_ERR_INVALID_ARGUMENT.  The word is cleared by the next call that uses
+ * the workspace. */
+la_status_t la_prefill_wait_status(const void* workspace, int64_t status_offset,
+                                   void* hip_stream);
 
 /* ------------------------------------------------------------- serving --
  * Prefill/decode co-scheduling with chunked prefill ([Deploy] section 3:

@@ -68,12 +68,15 @@ extern "C" {
  *               events[2i+1] are recorded around the i-th kernel launched on
  *               hip_stream, i < n_timing.  Kernels in launch order: [plan]
  *               (only when num_seqs > 1), rotate, attention.
- *   precision   0 (default): single bf16 operands for both products (the
- *               usual attention kernel; error against fp64 about 1e-3 of the
- *               values' scale, see "Precision" above).  1: split operands --
- *               q, k and the probabilities each carried as bf16 hi + lo, three
- *               products for the scores and two for P V -- about 1e-4 of the
- *               output's rms at 2.5x the matrix-core work.  Other values:
+ *   precision   1 (default): split operands -- q, k and the probabilities
+ *               each carried as bf16 hi + lo, three products for the scores
+ *               and two for P V -- about 1e-4 of the output's rms, within
+ *               the 1e-2-of-rms bound for bf16 inputs with fp32
+ *               accumulation.  0: single bf16 operands for both products
+ *               (the usual attention kernel, 2.5x fewer matrix-core
+ *               instructions; error against fp64 about 1e-3 of the values'
+ *               scale, which on long rows is more than 1e-2 of the output's
+ *               own rms, see "Precision" above).  Other values:
  *               LA_ERR_INVALID_ARGUMENT.                                    */
 typedef struct {
     int32_t rotary_dim;

@@ -1,5 +1,5 @@
-"""ctypes view of liblinattn.so (the C ABI declared in include/la.h and
-include/la_softmax.h)."""
+"""ctypes view of liblinattn.so (the C ABI declared in include/la.h,
+include/la_softmax.h and include/la_proj.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -13,11 +13,13 @@ LA_ERR_INVALID_ARGUMENT = 1
 LA_ERR_UNSUPPORTED = 2
 LA_ERR_WORKSPACE_TOO_SMALL = 3
 LA_ERR_HIP = 4
+LA_ERR_WAIT_TIMEOUT = 5
 
 LA_DTYPE_F32 = 0
 LA_DTYPE_BF16 = 1
 
-# every extern "C" function declared in include/la.h and include/la_softmax.h
+# every extern "C" function declared in include/la.h, include/la_softmax.h and
+# include/la_proj.h
 EXPORTS = (
     "la_default_options",
     "la_prefill",
@@ -27,6 +29,7 @@ EXPORTS = (
     "la_prefill_varlen_workspace_bytes",
     "la_decode_workspace_bytes",
     "la_prefill_plan",
+    "la_prefill_wait_status",
     "la_schedule_step",
     "la_serve_step",
     "la_serve_step_workspace_bytes",
@@ -34,6 +37,8 @@ EXPORTS = (
     "la_softmax_default_options",
     "la_softmax_attention_varlen",
     "la_softmax_workspace_bytes",
+    "la_proj_default_options",
+    "la_qkvx_projection",
 )
 
 
@@ -50,6 +55,7 @@ class Options(ctypes.Structure):
         ("state_slots", ctypes.c_void_p),
         ("state_rows", ctypes.c_int32),
         ("featurized", ctypes.c_int32),
+        ("wait_spin_limit", ctypes.c_int32),
     ]
 
 
@@ -77,6 +83,14 @@ class SoftmaxOptions(ctypes.Structure):
     ]
 
 
+class ProjOptions(ctypes.Structure):
+    _fields_ = [
+        ("featurize", ctypes.c_int32),
+        ("timing_events", ctypes.c_void_p),
+        ("n_timing", ctypes.c_int32),
+    ]
+
+
 class Plan(ctypes.Structure):
     _fields_ = [
         ("main_workgroups", ctypes.c_int64),
@@ -86,6 +100,7 @@ class Plan(ctypes.Structure):
         ("chunk_on_device", ctypes.c_int32),
         ("n_kernels", ctypes.c_int32),
         ("kernels", ctypes.c_int32 * 8),
+        ("status_offset", ctypes.c_int64),
     ]
 
     def kernel_names(self):
@@ -157,6 +172,8 @@ def load() -> ctypes.CDLL:
         lib.la_prefill_plan.restype = ctypes.c_int
         lib.la_prefill_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                                         ctypes.c_int, _i32, _optp, ctypes.POINTER(Plan)]
+        lib.la_prefill_wait_status.restype = ctypes.c_int
+        lib.la_prefill_wait_status.argtypes = [_vp, ctypes.c_int64, _vp]
         lib.la_schedule_step.restype = ctypes.c_int
         lib.la_schedule_step.argtypes = [ctypes.POINTER(Request), _i32, _i32,
                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32),
@@ -179,6 +196,11 @@ def load() -> ctypes.CDLL:
         lib.la_softmax_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                    ctypes.c_int, ctypes.c_int,
                                                    ctypes.POINTER(SoftmaxOptions)]
+        lib.la_proj_default_options.restype = ProjOptions
+        lib.la_proj_default_options.argtypes = []
+        lib.la_qkvx_projection.restype = ctypes.c_int
+        lib.la_qkvx_projection.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                           ctypes.c_int, ctypes.POINTER(ProjOptions), _vp]
         _lib = lib
         return lib
 
@@ -191,7 +213,7 @@ def status_string(status: int) -> str:
 
 
 def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
-            chunk_tokens=0, featurized=False) -> Options:
+            chunk_tokens=0, featurized=False, wait_spin_limit=0) -> Options:
     o = load().la_default_options()
     o.block_size = int(block_size)
     o.normalized = int(bool(normalized))
@@ -200,15 +222,22 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     o.rms_eps = float(rms_eps)
     o.chunk_tokens = int(chunk_tokens)
     o.featurized = int(bool(featurized))
+    o.wait_spin_limit = int(wait_spin_limit)
     return o
 
 
-def softmax_options(rotary_dim=-1, rope_base=10000.0, scale=0.0, precision=0) -> SoftmaxOptions:
+def softmax_options(rotary_dim=-1, rope_base=10000.0, scale=0.0, precision=1) -> SoftmaxOptions:
     o = load().la_softmax_default_options()
     o.rotary_dim = int(rotary_dim)
     o.rope_base = float(rope_base)
     o.scale = float(scale)
     o.precision = int(precision)
+    return o
+
+
+def proj_options(featurize=True) -> ProjOptions:
+    o = load().la_proj_default_options()
+    o.featurize = int(bool(featurize))
     return o
 
 

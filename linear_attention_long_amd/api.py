@@ -36,17 +36,33 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor | None:
+def _workspace(nbytes: int, device, given=None) -> torch.Tensor | None:
     if nbytes == ctypes.c_size_t(-1).value:
         return None
     if nbytes == 0:
         return None
+    if given is not None:
+        if given.dtype != torch.uint8 or given.numel() < nbytes:
+            raise ValueError("workspace must be a uint8 tensor of at least %d bytes" % nbytes)
+        return given
     return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def _keep_for(stream, *tensors):
+    """Buffers allocated here on the current stream but used by kernels on
+    ``stream``: tell the caching allocator, so that it does not hand their
+    memory to another allocation before that stream's work is done."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=False,
                block_size=0, norm_group=0, rms_eps=1e-6, chunk_tokens=0,
-               out_dtype=torch.float32, return_state=True, featurized=False, stream=None):
+               out_dtype=torch.float32, return_state=True, featurized=False, stream=None,
+               workspace=None, wait_spin_limit=0):
     """Prefill of Bt equal-length sequences.
 
     q, k, v: [Bt, T, H, d] (or [T, H, d]) pre-activation, float32 or bfloat16.
@@ -54,7 +70,10 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
     w: RMSNorm weight [H*d] float32 or None.  state_in [Bt, H, d, d], z_in
     [Bt, H, d] float32 or None.  Returns (out [Bt, T, H*d], state_out, z_out).
     ``featurized``: q, k, v are feature vectors already (SiLU applied where
-    they were produced); bfloat16 with d = 128 and block 32 only.
+    they were produced).  ``workspace``: a uint8 device tensor to use as the
+    call's workspace (else one is allocated); pass one to read the call's
+    wait status afterwards (:func:`la_prefill_wait_status`).
+    ``wait_spin_limit``: bound of the fused gate's waits (0 = default).
     """
     lib = _lib.load()
     squeeze = q.dim() == 3
@@ -71,7 +90,7 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
         raise ValueError("q, k, v must have the same shape and dtype")
     gated = x is not None
     opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens,
-                       featurized)
+                       featurized, wait_spin_limit)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
     out = torch.empty((Bt, T, H * d), dtype=out_dtype, device=dev)
@@ -79,12 +98,13 @@ def la_prefill(q, k, v, x=None, w=None, state_in=None, z_in=None, *, normalized=
     z_out = (torch.empty((Bt, H, d), dtype=torch.float32, device=dev)
              if (return_state and normalized) else None)
     nbytes = lib.la_prefill_workspace_bytes(Bt, T, H, d, in_dt, out_dt, ctypes.byref(opt))
-    ws = _workspace(nbytes, dev)
+    ws = _workspace(nbytes, dev, workspace)
     st = lib.la_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(state_in), _ptr(z_in),
                         _ptr(out), _ptr(state_out), _ptr(z_out), Bt, T, H, d, in_dt, out_dt,
                         ctypes.byref(opt), _ptr(ws), 0 if ws is None else ws.numel(),
                         _stream(stream))
     _lib.check(st, "la_prefill")
+    _keep_for(stream, out, state_out, z_out, ws)
     if squeeze:
         out = out[0]
         state_out = None if state_out is None else state_out[0]
@@ -108,7 +128,8 @@ def _slots(opt, state_slots, pool):
 def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=None, z_in=None,
                       *, normalized=False, block_size=0, norm_group=0, rms_eps=1e-6,
                       chunk_tokens=0, out_dtype=torch.float32, return_state=True,
-                      state_slots=None, out=None, featurized=False, stream=None):
+                      state_slots=None, out=None, featurized=False, stream=None,
+                      workspace=None, wait_spin_limit=0):
     """Prefill of a packed batch.  q, k, v: [total_T, H, d]; cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
     Returns (out [total_T, H*d], state_out [num_seqs, H, d, d], z_out).
@@ -122,7 +143,7 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
         raise TypeError("cu_seqlens must be int32")
     gated = x is not None
     opt = _lib.options(block_size, normalized, gated, norm_group, rms_eps, chunk_tokens,
-                       featurized)
+                       featurized, wait_spin_limit)
     _slots(opt, state_slots, state_in)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     dev = q.device
@@ -137,14 +158,28 @@ def la_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, x=None, w=None, state_in=
                  if (return_state and normalized) else None)
     nbytes = lib.la_prefill_varlen_workspace_bytes(total_T, num_seqs, int(max_seqlen), H, d,
                                                    in_dt, out_dt, ctypes.byref(opt))
-    ws = _workspace(nbytes, dev)
+    ws = _workspace(nbytes, dev, workspace)
     st = lib.la_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(w), _ptr(cu_seqlens),
                                num_seqs, total_T, int(max_seqlen), _ptr(state_in), _ptr(z_in),
                                _ptr(out), _ptr(state_out), _ptr(z_out), H, d, in_dt, out_dt,
                                ctypes.byref(opt), _ptr(ws), 0 if ws is None else ws.numel(),
                                _stream(stream))
     _lib.check(st, "la_prefill_varlen")
+    _keep_for(stream, out, state_out, z_out, ws)
     return out, state_out, z_out
+
+
+def la_prefill_wait_status(workspace, status_offset, stream=None) -> int:
+    """Status of the bounded waits of a finished prefill call
+    (la_prefill_wait_status): synchronises ``stream`` and reads the word at
+    ``status_offset`` (la_plan_t.status_offset of the call's plan) of the
+    call's ``workspace``.  Returns LA_OK (0) or LA_ERR_WAIT_TIMEOUT (5)."""
+    lib = _lib.load()
+    st = lib.la_prefill_wait_status(_ptr(workspace), int(status_offset), _stream(stream))
+    if st not in (_lib.LA_OK, _lib.LA_ERR_WAIT_TIMEOUT):
+        _lib.check(st, "la_prefill_wait_status")
+    return st
+
 
 
 def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, norm_group=0,
@@ -171,6 +206,7 @@ def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, 
                             _ptr(workspace), 0 if workspace is None else workspace.numel(),
                             _stream(stream))
     _lib.check(st, "la_decode_step")
+    _keep_for(stream, out, workspace)
     return out
 
 
@@ -242,15 +278,16 @@ serve_step = la_serve_step
 
 
 def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-1,
-                                rope_base=10000.0, scale=0.0, precision=0,
+                                rope_base=10000.0, scale=0.0, precision=1,
                                 out_dtype=torch.bfloat16, return_lse=False, out=None,
                                 stream=None):
     """Causal softmax attention with rotary embedding over a packed batch
     (the hybrid model's softmax layer).  q: [total_T, H, d] bfloat16; k, v:
     [total_T, H_kv, d] bfloat16 (H_kv divides H); cu_seqlens: int32
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
-    rotary_dim -1 = d/2; scale 0 = 1/sqrt(d); precision 0 = single bf16
-    operands, 1 = split (hi + lo) operands.  Returns (out [total_T, H, d],
+    rotary_dim -1 = d/2; scale 0 = 1/sqrt(d); precision 1 (default) = split
+    (hi + lo) operands, within 1e-2 of the output's rms; 0 = single bf16
+    operands (faster, looser).  Returns (out [total_T, H, d],
     lse [total_T, H] float32 or None)."""
     lib = _lib.load()
     total_T, H, d = q.shape
@@ -276,4 +313,29 @@ def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-
                                          _ptr(out), _ptr(lse), ctypes.byref(opt), _ptr(ws),
                                          0 if ws is None else ws.numel(), _stream(stream))
     _lib.check(st, "la_softmax_attention_varlen")
+    _keep_for(stream, out, lse, ws)
     return out, lse
+
+
+def la_qkvx_projection(hidden, weight, F, *, gate=True, featurize=True, out_dtype=torch.bfloat16,
+                       out=None, stream=None):
+    """The layer's input projection (include/la_proj.h): hidden [T, K] bf16,
+    weight [nblk * F, K] bf16 with rows [W_q; W_k; W_v; W_g] (nblk = 4 with
+    ``gate``, else 3).  Returns (q, k, v, x_gate), each [T, F] ``out_dtype``
+    (x_gate None without ``gate``); q, k, v carry SiLU when ``featurize``.
+    ``out``: four (or three) preallocated outputs to write instead."""
+    lib = _lib.load()
+    T, K = hidden.shape
+    nblk = 4 if gate else 3
+    if weight.shape != (nblk * F, K):
+        raise ValueError("weight must be [%d * F, K]" % nblk)
+    if out is None:
+        out = [torch.empty((T, F), dtype=out_dtype, device=hidden.device) for _ in range(nblk)]
+    outs = list(out) + [None] * (4 - len(out))
+    opt = _lib.proj_options(featurize)
+    st = lib.la_qkvx_projection(_ptr(hidden), _ptr(weight), _ptr(outs[0]), _ptr(outs[1]),
+                                _ptr(outs[2]), _ptr(outs[3]), T, K, F, _dtype(out_dtype),
+                                ctypes.byref(opt), _stream(stream))
+    _lib.check(st, "la_qkvx_projection")
+    _keep_for(stream, *outs)
+    return tuple(outs)

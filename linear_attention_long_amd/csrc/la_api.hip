@@ -36,6 +36,7 @@ constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
 constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
 constexpr int kSpinLimit = 1 << 22;     // bounded waits of the fused gate (~seconds)
+constexpr size_t kStatusBytes = 256;    // the call's device status word, padded
 #ifndef LA_DECODE_SPLIT
 #define LA_DECODE_SPLIT 4
 #endif
@@ -65,6 +66,7 @@ struct Opts {
     const int32_t* slots;  // state row per sequence (device), or nullptr
     int rows;              // rows of the state arrays when slots is given
     bool feat;             // q, k, v are feature vectors already (no SiLU inside)
+    int spin;              // retries per bounded wait of the fused gate (< 0: none)
 };
 
 // Records the caller's timing events around each launched kernel.
@@ -86,7 +88,7 @@ struct Timer {
 struct Plan {
     bool fuse_ok;      // gated bf16 d=128 block 32 with H <= 8: gate fused into the main pass
     int64_t xbuf_words;  // exchange buffer of the fused gate (64-bit words)
-    size_t off_xbuf;
+    size_t off_xbuf;     // fused: [status word (256 B) | exchange buffer], cleared together
     int block;         // resolved block size
     bool mfma;         // bf16, d = 128, block 32 or 64: matrix-core kernels
     bool chunked;      // some sequence spans more than one chunk
@@ -135,6 +137,8 @@ la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
     if (x.state_slots && (x.state_rows < 1 || !aligned(x.state_slots, 4))) return LA_ERR_INVALID_ARGUMENT;
     if (x.featurized != 0 && x.featurized != 1) return LA_ERR_INVALID_ARGUMENT;
     o.feat = x.featurized == 1;
+    if (x.wait_spin_limit < -1) return LA_ERR_INVALID_ARGUMENT;
+    o.spin = x.wait_spin_limit == 0 ? kSpinLimit : x.wait_spin_limit;
     return LA_OK;
 }
 
@@ -243,7 +247,7 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
     if (o.gated && out_dtype != LA_DTYPE_F32 && !p.fuse_ok)
         off += align256((size_t)total_T * H * d * sizeof(float));
     p.off_xbuf = off;
-    off += align256((size_t)p.xbuf_words * sizeof(uint64_t));
+    if (p.fuse_ok) off += kStatusBytes + align256((size_t)p.xbuf_words * sizeof(uint64_t));
     p.total = off;
     return p;
 }
@@ -326,7 +330,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         k_chunk_scan<<<dim3((unsigned)nblk, (unsigned)H, (unsigned)nseq), 256, 0, st>>>(
             buf, p.stride, map, H, d, E, state_in, norm ? z_in : nullptr, state_out,
             norm ? z_out : nullptr, p.fuse_ok ? (uint64_t*)(ws + p.off_xbuf) : nullptr,
-            p.fuse_ok ? p.xbuf_words : 0);
+            p.fuse_ok ? p.xbuf_words + (int64_t)(kStatusBytes / 8) : 0);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
     }
@@ -336,11 +340,12 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     if (p.fuse_ok) {
         const bool f32o = std::is_same<OutT, float>::value;
         const void* kern = fused_kernel(norm, f32o, o.feat);
-        uint64_t* xbuf = (uint64_t*)(ws + p.off_xbuf);
-        const int64_t nw = p.xbuf_words;
+        uint32_t* status = (uint32_t*)(ws + p.off_xbuf);
+        uint64_t* xbuf = (uint64_t*)(ws + p.off_xbuf + kStatusBytes);
+        const int64_t nw = p.xbuf_words + (int64_t)(kStatusBytes / 8);
         if (!p.chunked) {  // (a chunked call's scan cleared it)
             tm.before();
-            k_zero_u64<<<(unsigned)((nw + 255) / 256), 256, 0, st>>>(xbuf, nw);
+            k_zero_u64<<<(unsigned)((nw + 255) / 256), 256, 0, st>>>((uint64_t*)status, nw);
             if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
             tm.after();
         }
@@ -348,7 +353,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         const uint16_t* kb = (const uint16_t*)k;
         const uint16_t* vb = (const uint16_t*)v;
         const uint16_t* xb = (const uint16_t*)x;
-        int k16 = 16, spin = kSpinLimit, Hh = H;
+        int k16 = 16, spin = o.spin, Hh = H;
         float eps = o.eps;
         float* so = state_out;  // written after each sequence's last chunk
         float* zo = norm ? z_out : nullptr;
@@ -358,7 +363,7 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         void* args[] = {(void*)&qb, (void*)&kb, (void*)&vb, (void*)&map, (void*)&Hh,
                         (void*)&bufc, (void*)&stride, (void*)&state_in, (void*)&z_in,
                         (void*)&outp, (void*)&so, (void*)&zo, (void*)&k16, (void*)&xb,
-                        (void*)&w, (void*)&eps, (void*)&xbuf, (void*)&spin};
+                        (void*)&w, (void*)&eps, (void*)&xbuf, (void*)&spin, (void*)&status};
         tm.before();
         const hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)(p.items * H)),
                                                         dim3(mf::NT), args, 0, st);
@@ -504,6 +509,7 @@ la_options_t la_default_options(void) {
     o.state_slots = nullptr;
     o.state_rows = 0;
     o.featurized = 0;
+    o.wait_spin_limit = 0;
     return o;
 }
 
@@ -516,6 +522,7 @@ const char* la_status_string(la_status_t s) {
         case LA_ERR_UNSUPPORTED: return "unsupported configuration";
         case LA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case LA_ERR_HIP: return "HIP launch failed";
+        case LA_ERR_WAIT_TIMEOUT: return "a bounded device wait gave up (its rows hold NaN)";
     }
     return "unknown status";
 }
@@ -591,8 +598,23 @@ la_status_t la_prefill_plan(int32_t varlen, int32_t num_seqs, int32_t total_T, i
         }
     }
     r.n_kernels = n;
+    r.status_offset = (total_T > 0 && p.fuse_ok) ? (int64_t)p.off_xbuf : -1;
     *plan = r;
     return LA_OK;
+}
+
+la_status_t la_prefill_wait_status(const void* workspace, int64_t status_offset, void* hip_stream) {
+    if (status_offset < 0) return LA_OK;
+    if (!workspace) return LA_ERR_INVALID_ARGUMENT;
+    hipStream_t st = (hipStream_t)hip_stream;
+    uint32_t word = 0;
+    if (hipMemcpyAsync(&word, (const char*)workspace + status_offset, sizeof word,
+                       hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess) {
+        (void)hipGetLastError();
+        return LA_ERR_HIP;
+    }
+    return word ? LA_ERR_WAIT_TIMEOUT : LA_OK;
 }
 
 la_status_t la_prefill(const void* q, const void* k, const void* v, const void* x_gate,

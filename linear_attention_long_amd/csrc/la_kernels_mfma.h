@@ -421,7 +421,8 @@ struct GateArgs {
     float eps;
     uint64_t* xbuf;          // [teams][NSLOT][H][TB] (tag << 32 | sum of squares), zeroed per call
     int team;
-    int spin_limit;
+    int spin_limit;          // retries per wait; < 0: every wait gives up at once
+    uint32_t* status;        // set to 1 when a wait gives up (zeroed per call)
 };
 constexpr int NSLOT = 4;     // exchange slots per team (2 suffice: see publish order)
 constexpr int FUSE_HMAX = 8; // heads per token the fused gate handles (more: separate gate)
@@ -515,15 +516,21 @@ __device__ __forceinline__ void gather_issue(const GateArgs<uint16_t>& ga, int H
     }
 }
 
+// A wait that gives up (spin_limit retries, or at once when spin_limit < 0)
+// never gates with a word it could not verify: the token's sum becomes NaN,
+// so its gated outputs are NaN, and the call's status word is set.  (A word
+// with the current tag is always this block's: an older block in the same
+// slot carries a tag NSLOT * n smaller.)
 template <int TB>
 __device__ __forceinline__ void gather_finish(SmemMain<TB>& sm, const GateArgs<uint16_t>& ga,
                                               int H, uint32_t tag, int lane, uint64_t (&word)[4]) {
     const uint64_t* slot = ga.xbuf + ((size_t)ga.team * NSLOT + (tag % NSLOT)) * H * TB;
-    for (int n = 0; n < ga.spin_limit; ++n) {
-        bool ready = true;
+    bool ready = false;
+    for (int n = 0;; ++n) {
+        ready = ga.spin_limit >= 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) ready = ready && (word[j] >> 32) == (uint64_t)tag;
-        if (ready) break;
+        if (ready || n >= ga.spin_limit) break;
         __builtin_amdgcn_s_sleep(1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -534,6 +541,10 @@ __device__ __forceinline__ void gather_finish(SmemMain<TB>& sm, const GateArgs<u
     }
     float ss = (__uint_as_float((uint32_t)word[0]) + __uint_as_float((uint32_t)word[1])) +
                (__uint_as_float((uint32_t)word[2]) + __uint_as_float((uint32_t)word[3]));
+    if (!ready) {
+        ss = __builtin_nanf("");
+        __hip_atomic_store(ga.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     ss += __shfl_xor(ss, 32, 64);
     if (lane < TB) sm.ssum[lane] = ss;
 }
@@ -905,12 +916,12 @@ __global__ __launch_bounds__(NT, Tile<TB>::WG_PER_CU) void k_prefill_fused(
     ItemMap map, int H, const float* __restrict__ prefix, int64_t prefix_stride,
     const float* __restrict__ state_in, const float* __restrict__ z_in, OutT* __restrict__ out,
     float* state_out, float* z_out, int k16, const uint16_t* __restrict__ x,
-    const float* __restrict__ w, float eps, uint64_t* xbuf, int spin_limit) {
+    const float* __restrict__ w, float eps, uint64_t* xbuf, int spin_limit, uint32_t* status) {
     __shared__ SmemMain<TB> sm;
     const int item = blockIdx.x / H, h = blockIdx.x - item * H;
     Item it;
     if (!decode_item(map, item, it)) return;  // the whole team returns together
-    GateArgs<uint16_t> ga{x, w, eps, xbuf, item, spin_limit};
+    GateArgs<uint16_t> ga{x, w, eps, xbuf, item, spin_limit, status};
     process_item<NORM, true, OutT, uint16_t, TB, FEAT>(sm, q, k, v, it, item, H, h, prefix,
                                                   prefix_stride, state_in, z_in, out, state_out,
                                                   z_out, k16, ga);

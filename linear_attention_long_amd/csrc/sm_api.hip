@@ -163,7 +163,7 @@ la_softmax_options_t la_softmax_default_options(void) {
     o.scale = 0.f;
     o.timing_events = nullptr;
     o.n_timing = 0;
-    o.precision = 0;
+    o.precision = 1;
     return o;
 }
 

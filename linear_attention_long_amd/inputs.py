@@ -18,6 +18,10 @@ Recipe (every workload):
   * variable lengths: numpy ``PCG64`` seeded with ``seed``, lengths
     ``round(exp(U(ln 1024, ln 131072)))`` drawn until their sum reaches the
     target; the last one is clipped to the remainder.
+  * projection workloads (kind "proj"): the layer input hidden [T, K] ~
+    N(0,1) (index 0) and the weight [4F, K] ~ N(0, 1/K) (index 1), rows
+    [W_q; W_k; W_v; W_g], both bf16, so the projections have unit spread.
+    The pages give no hidden width; K = 6144 (the bench's reading).
   * softmax-layer workloads (kind "softmax"): q [T, H, d], k and v
     [T, Hkv, d], N(0,1) in bf16 (unit-spread scores after the 1/sqrt(d)
     scale), index order q=0, k=1, v=2; packed lengths as above, drawn with
@@ -91,6 +95,16 @@ WORKLOADS = {
                                 state_std=0.01, gen_device="cuda",
                                 note="serving step, 64 decode tokens + a 32704-token prompt "
                                      "chunk, H=8 d=128, gated, state pool N(0,0.01)"),
+    # the layer's input projection for one GPU's 8 heads (F = 1024 features
+    # each of q, k, v and the gate) from a 6144-wide layer input
+    "proj_32k": Workload("proj_32k", "proj", 1011, H=8, d=128, dtype="bf16", T=32768,
+                         gen_device="cuda", extra={"K": 6144},
+                         note="input projection, bf16 hidden [32768, 6144] x weight "
+                              "[4096, 6144] -> q, k, v (SiLU) and gate pre-activation"),
+    "proj_1m": Workload("proj_1m", "proj", 1012, H=8, d=128, dtype="bf16", T=1048576,
+                        gen_device="cuda", extra={"K": 6144},
+                        note="input projection of the 1M-token sequence, hidden "
+                             "[1048576, 6144] x weight [4096, 6144]"),
     # the softmax attention layer of the hybrid model on the same shapes:
     # one GPU's 8 heads, rotary embedding on half of d = 128, the
     # long-context base 1e7, Hkv = H
@@ -238,3 +252,14 @@ def softmax_inputs(w: Workload, device: str | None = None, Hkv: int | None = Non
     k = normal((total, Hkv, w.d), w.seed, 1, w.scale, dt, dev)
     v = normal((total, Hkv, w.d), w.seed, 2, w.scale, dt, dev)
     return q, k, v, cu
+
+
+def projection_inputs(w: Workload, T: int | None = None, device=None):
+    """hidden [T, K] ~ N(0,1) and weight [4F, K] ~ N(0, 1/K), both bf16."""
+    T = w.T if T is None else T
+    K = w.extra["K"]
+    F = w.H * w.d
+    dev = w.gen_device if device is None else device
+    hidden = normal((T, K), w.seed, 0, 1.0, torch.bfloat16, dev)
+    weight = normal((4 * F, K), w.seed, 1, 1.0 / math.sqrt(K), torch.bfloat16, dev)
+    return hidden, weight

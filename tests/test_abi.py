@@ -14,7 +14,7 @@ import pytest
 from linear_attention_long_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", "la.h"), os.path.join(ROOT, "include", "la_softmax.h")]
+HEADERS = [os.path.join(ROOT, "include", n) for n in ("la.h", "la_softmax.h", "la_proj.h")]
 
 F32, BF16 = _lib.LA_DTYPE_F32, _lib.LA_DTYPE_BF16
 INVALID, UNSUPPORTED, WS_SMALL = (_lib.LA_ERR_INVALID_ARGUMENT, _lib.LA_ERR_UNSUPPORTED,
@@ -52,7 +52,7 @@ def test_default_options(lib):
     o = lib.la_default_options()
     assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (0, 0, 0, 0, 0)
     assert abs(o.rms_eps - 1e-6) < 1e-12
-    assert o.featurized == 0
+    assert o.featurized == 0 and o.wait_spin_limit == 0
 
 
 def test_featurized_inputs_supported_set(lib):
@@ -76,8 +76,8 @@ def test_featurized_inputs_supported_set(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
-        assert lib.la_status_string(s)
+    for s in range(6):
+        assert lib.la_status_string(s) and lib.la_status_string(s) != b"unknown status"
     assert lib.la_status_string(99) == b"unknown status"
 
 
@@ -105,8 +105,10 @@ def test_workspace_queries(lib):
     if pg.fused_gate:
         # fused gate (a device that holds every workgroup): chunk states plus
         # the exchange buffer (4 slots x H x 32 tokens of 8 bytes per chunk)
+        # after the call's 256-byte status word
         n = (1 << 20) // pg.chunk_tokens
-        assert nb2 == n * 8 * 128 * 128 * 4 + n * 4 * 8 * 32 * 8
+        assert nb2 == n * 8 * 128 * 128 * 4 + 256 + n * 4 * 8 * 32 * 8
+        assert pg.status_offset == n * 8 * 128 * 128 * 4
     else:
         # separate gate with a bf16 output: an fp32 Y buffer
         assert nb2 == nb + (1 << 20) * 8 * 128 * 4
@@ -147,6 +149,22 @@ def test_prefill_plan(lib):
     assert lib.la_prefill_plan(0, 1, 64, 64, 2, 96, F32, F32, 1, ctypes.byref(o),
                                ctypes.byref(r)) == UNSUPPORTED
     assert lib.la_prefill_plan(0, 1, 64, 64, 2, 64, F32, F32, 1, ctypes.byref(o), None) == INVALID
+
+
+def test_wait_options_and_status_query(lib):
+    """wait_spin_limit takes -1, 0 (default) or a positive bound; the status
+    query of a plan without a bounded wait returns at once, and a status word
+    with no workspace is an invalid argument (neither touches the device)."""
+    for lim in (-1, 0, 1, 1 << 20):
+        assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, BF16, F32,
+                                              ctypes.byref(opt(gated=1, wait_spin_limit=lim))) != SIZE_MAX
+    assert lib.la_prefill_workspace_bytes(1, 4096, 8, 128, BF16, F32,
+                                          ctypes.byref(opt(gated=1, wait_spin_limit=-2))) == SIZE_MAX
+    assert prefill(lib, o=opt(wait_spin_limit=-5)) == INVALID
+    p = _lib.plan(0, 1, 4096, 4096, 8, 128, BF16, F32, opt())   # ungated: no wait
+    assert p.status_offset == -1
+    assert lib.la_prefill_wait_status(None, -1, None) == _lib.LA_OK
+    assert lib.la_prefill_wait_status(None, 0, None) == INVALID
 
 
 def prefill(lib, q=A[0], k=A[1], v=A[2], x=None, w=None, si=None, zi=None, out=A[3], so=None,
@@ -227,10 +245,11 @@ def test_decode_rejects_bad_arguments(lib):
 def test_softmax_default_options(lib):
     o = lib.la_softmax_default_options()
     assert (o.rotary_dim, o.rope_base, o.scale, o.n_timing) == (-1, 10000.0, 0.0, 0)
+    assert o.precision == 1  # split operands: the mode within 1e-2 of the output's rms
 
 
 def test_softmax_workspace_bytes(lib):
-    o = _lib.softmax_options()
+    o = _lib.softmax_options(precision=0)
     # one sequence: rotated q and k only (bf16), each rounded up to 256 bytes
     assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
                                           ctypes.byref(o)) == 1000 * 4 * 256 + 1000 * 2 * 256
@@ -290,3 +309,29 @@ def test_softmax_rejects_bad_arguments(lib):
     assert call(wsb=need - 1) == WS_SMALL
     # an empty batch is accepted with no pointers and launches nothing
     assert call(q=None, k=None, v=None, cu=None, out=None, total=0, maxlen=0, ws=None, wsb=0) == 0
+
+
+def test_projection_rejects_bad_arguments(lib):
+    """la_qkvx_projection's host checks (no call reaches the device)."""
+    def call(h=A[0], w=A[1], q=A[2], k=A[3], v=A[4], xg=A[5], T=300, K=6144, F=1024, odt=BF16,
+             o=None):
+        o = o or _lib.proj_options()
+        return lib.la_qkvx_projection(h, w, q, k, v, xg, T, K, F, odt, ctypes.byref(o), None)
+
+    o = lib.la_proj_default_options()
+    assert o.featurize == 1 and o.n_timing == 0
+    assert call(T=0) == _lib.LA_OK                       # nothing to do
+    assert call(h=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(K=100) == UNSUPPORTED                    # not a multiple of 64
+    assert call(F=1000) == UNSUPPORTED                   # not a multiple of 256
+    assert call(K=0) == INVALID
+    assert call(F=1 << 21) == INVALID
+    assert call(odt=7) == INVALID
+    assert call(q=ctypes.c_void_p(0x10000008)) == INVALID  # misaligned
+    assert call(q=A[0]) == INVALID                       # output overlaps the input
+    assert call(k=A[2]) == INVALID                       # outputs overlap each other
+    bad = _lib.proj_options()
+    bad.featurize = 2
+    assert call(o=bad) == INVALID

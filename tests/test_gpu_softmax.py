@@ -57,6 +57,7 @@ def packed(lengths, H, Hkv, seed, d=128, qstd=1.0):
 
 def run(q, k, v, cu, max_seqlen=None, **kw):
     max_seqlen = int((cu[1:] - cu[:-1]).max()) if max_seqlen is None else max_seqlen
+    kw.setdefault("precision", 0)  # the single-operand mode unless a test asks otherwise
     out, lse = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV),
                                                max_seqlen, return_lse=True, **kw)
     torch.cuda.synchronize()
@@ -147,7 +148,7 @@ def test_max_seqlen_above_the_longest_and_repeat_is_identical():
 def test_empty_batch_is_a_no_op():
     q = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device=DEV)
     cu = torch.zeros(3, dtype=torch.int32, device=DEV)
-    out, lse = api.la_softmax_attention_varlen(q, q, q, cu, 0, return_lse=True)
+    out, lse = api.la_softmax_attention_varlen(q, q, q, cu, 0, return_lse=True, precision=0)
     torch.cuda.synchronize()
     assert out.shape == (0, 2, 128) and lse.shape == (0, 2)
 
@@ -202,7 +203,7 @@ def test_workload_sampled(name):
     maxlen = int((cu[1:] - cu[:-1]).max())
     out, lse = api.la_softmax_attention_varlen(q, k, v, cu.to(DEV), maxlen, rotary_dim=rot,
                                                rope_base=base, out_dtype=torch.float32,
-                                               return_lse=True)
+                                               return_lse=True, precision=0)
     torch.cuda.synchronize()
     rows, heads = sample_pairs(cu.numpy(), w.H, 48, 5)
     got = out[torch.from_numpy(rows).to(DEV), torch.from_numpy(heads).to(DEV)].double().cpu().numpy()
@@ -322,7 +323,29 @@ def test_many_heads_grouped_and_without_lse():
     ref, lref = SO.attention(q, k, v, cu, rope_base=1e7)
     check(got, ref, v, lse, lref)
     out2, none = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 512,
-                                                 out_dtype=torch.float32, rope_base=1e7)
+                                                 out_dtype=torch.float32, rope_base=1e7,
+                                                 precision=0)
     torch.cuda.synchronize()
     assert none is None
     np.testing.assert_array_equal(out2.double().cpu().numpy(), got)
+
+
+def test_default_mode_meets_the_bf16_bound():
+    """Without a precision argument the layer runs the split mode, held to
+    max|err| <= 1e-2 of the output's own rms (the bound for bf16 inputs with
+    fp32 accumulation), on ragged packed lengths with grouped heads."""
+    from linear_attention_long_amd import _lib
+
+    assert _lib.load().la_softmax_default_options().precision == 1
+    lengths = [1, 127, 129, 700, 0, 2050]
+    q, k, v, cu = packed(lengths, 8, 2, 97)
+    out, lse = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 2050,
+                                               out_dtype=torch.float32, return_lse=True,
+                                               rope_base=1e7)
+    torch.cuda.synchronize()
+    ref, lref = SO.attention(q, k, v, cu, rope_base=1e7)
+    got = out.double().cpu().numpy()
+    err = float(np.abs(got - ref).max() / np.sqrt(np.mean(ref ** 2)))
+    print("default (split) mode: max|err|/rms(ref) %.2e" % err)
+    assert err <= 1e-2
+    assert float(np.abs(lse.double().cpu().numpy() - lref).max()) <= 1e-4
