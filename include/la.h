@@ -170,6 +170,28 @@ la_status_t la_prefill(const void* q, const void* k, const void* v,
                        const la_options_t* opt,
                        void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* la_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and result, without a workspace.  Its scratch space is a
+ * fixed array of LA_NOALLOC_SCRATCH_BYTES bytes per GPU that the library
+ * holds until the process ends (its address is looked up on the first call
+ * on a device); the call allocates nothing.  Calls whose plan needs more
+ * (la_prefill_workspace_bytes of the same arguments) return
+ * LA_ERR_WORKSPACE_TOO_SMALL with no side effects; 64 MiB holds, e.g., the
+ * gated prefill of one 4,194,304-token sequence with 8 heads of d = 128.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams, or from different threads without
+ * ordering) race and must not be issued; calls ordered on one stream are
+ * safe.  What must start at zero is cleared by each call's own kernels.   */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+la_status_t la_prefill_noalloc(const void* q, const void* k, const void* v,
+                               const void* x_gate, const float* rms_weight,
+                               const float* state_in, const float* z_in,
+                               void* out, float* state_out, float* z_out,
+                               int32_t Bt, int32_t T, int32_t H, int32_t d,
+                               la_dtype_t in_dtype, la_dtype_t out_dtype,
+                               const la_options_t* opt, void* hip_stream);
+
 /* Prefill of a packed batch of variable-length sequences; the state starts
  * from state_in[s] (or zero) at each sequence start cu_seqlens[s].  Per
  * sequence it computes exactly what la_prefill computes ([Tut] 3 recurrence,

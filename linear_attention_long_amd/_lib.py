@@ -15,6 +15,8 @@ LA_ERR_WORKSPACE_TOO_SMALL = 3
 LA_ERR_HIP = 4
 LA_ERR_WAIT_TIMEOUT = 5
 
+LA_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/la.h
+
 LA_DTYPE_F32 = 0
 LA_DTYPE_BF16 = 1
 
@@ -23,6 +25,7 @@ LA_DTYPE_BF16 = 1
 EXPORTS = (
     "la_default_options",
     "la_prefill",
+    "la_prefill_noalloc",
     "la_prefill_varlen",
     "la_decode_step",
     "la_prefill_workspace_bytes",
@@ -154,6 +157,10 @@ def load() -> ctypes.CDLL:
         lib.la_prefill.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _fp,
                                    _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
                                    _optp, _vp, _sz, _vp]
+        lib.la_prefill_noalloc.restype = ctypes.c_int
+        lib.la_prefill_noalloc.argtypes = [_vp, _vp, _vp, _vp, _fp, _fp, _fp, _vp, _fp, _fp,
+                                           _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
+                                           _optp, _vp]
         lib.la_prefill_varlen.restype = ctypes.c_int
         lib.la_prefill_varlen.argtypes = [_vp, _vp, _vp, _vp, _fp, _vp, _i32, _i32, _i32,
                                           _fp, _fp, _vp, _fp, _fp, _i32, _i32, ctypes.c_int,

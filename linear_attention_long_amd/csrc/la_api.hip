@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "la_kernels_aux.h"
@@ -17,6 +18,13 @@
 #include "la_kernels_valu.h"
 
 using namespace la;
+
+// ---- scratch of the entry point that allocates nothing (la_prefill_noalloc) ----
+// One array per GPU, for the life of the process.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is ever
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -492,6 +500,27 @@ la_status_t check_workspace(const Plan& p, void* ws, size_t ws_bytes) {
     return LA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device; nullptr on failure.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -639,6 +668,34 @@ la_status_t la_prefill(const void* q, const void* k, const void* v, const void* 
     if (s != LA_OK) return s;
     return launch_prefill(p, o, in_dtype, out_dtype, q, k, v, x_gate, rms_weight, nullptr, Bt, T,
                           total_T, state_in, z_in, out, state_out, z_out, H, d, (char*)workspace,
+                          (hipStream_t)hip_stream);
+}
+
+la_status_t la_prefill_noalloc(const void* q, const void* k, const void* v, const void* x_gate,
+                               const float* rms_weight, const float* state_in, const float* z_in,
+                               void* out, float* state_out, float* z_out, int32_t Bt, int32_t T,
+                               int32_t H, int32_t d, la_dtype_t in_dtype, la_dtype_t out_dtype,
+                               const la_options_t* opt, void* hip_stream) {
+    if (!dtype_arg_ok(in_dtype) || !dtype_arg_ok(out_dtype)) return LA_ERR_INVALID_ARGUMENT;
+    la_status_t s = check_shape(H, d, in_dtype, out_dtype);
+    if (s != LA_OK) return s;
+    if (Bt < 1 || T < 0 || (int64_t)Bt * T > INT32_MAX) return LA_ERR_INVALID_ARGUMENT;
+    Opts o;
+    s = parse_options(opt, H, d, o);
+    if (s != LA_OK) return s;
+    const int64_t total_T = (int64_t)Bt * T;
+    s = check_prefill_common(q, k, v, x_gate, rms_weight, state_in, z_in, out, state_out, z_out, Bt,
+                             total_T, H, d, in_dtype, out_dtype, o);
+    if (s != LA_OK) return s;
+    const Plan p = make_plan(false, Bt, total_T, T, H, d, in_dtype, out_dtype, o);
+    if (p.total > (size_t)LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (p.total > 0) {
+        ws = scratch_for_current_device();
+        if (!ws) return LA_ERR_HIP;
+    }
+    return launch_prefill(p, o, in_dtype, out_dtype, q, k, v, x_gate, rms_weight, nullptr, Bt, T,
+                          total_T, state_in, z_in, out, state_out, z_out, H, d, (char*)ws,
                           (hipStream_t)hip_stream);
 }
 
