@@ -30,10 +30,14 @@ inline bool dtype_arg_ok(const la_dtype_t& t) {
 #ifndef LA_SM_WAVES
 #define LA_SM_WAVES 8
 #endif
-// Waves per attention workgroup: single-operand mode LA_SM_WAVES (32 queries
-// each), split mode 4 (its registers allow one workgroup of 4 waves per CU).
+#ifndef LA_SM_WAVES_SPLIT
+#define LA_SM_WAVES_SPLIT 8
+#endif
+// Waves per attention workgroup (32 queries each): single-operand mode
+// LA_SM_WAVES, split mode LA_SM_WAVES_SPLIT; one workgroup per CU either way,
+// two waves per SIMD with 8.
 constexpr int kWavesPlain = LA_SM_WAVES;
-constexpr int kWavesSplit = 4;
+constexpr int kWavesSplit = LA_SM_WAVES_SPLIT;
 inline int tile_queries(bool split) { return 32 * (split ? kWavesSplit : kWavesPlain); }
 
 struct SmOpts {
@@ -243,7 +247,10 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     {
         const int64_t want = ((int64_t)total_T + 15) / 16;
         const int grid = (int)(want < 16384 ? want : 16384);
-        const float qscale = o.scale * 1.4426950408889634f;  // scores in log2 units
+        // scores in log2 units: q carries scale * log2(e), except with split
+        // operands, where the attention kernel scales the fp32 scores (q then
+        // stays exact in bf16 outside the rotated dimensions)
+        const float qscale = o.split ? 1.0f : o.scale * 1.4426950408889634f;
         tm.before();
         sm::k_sm_rope<<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, cu_seqlens,
                                                 num_seqs, total_T, H, H_kv, o.rot,
@@ -254,17 +261,28 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     const unsigned grid = (unsigned)(p.emax * H);
     tm.before();
     if (grid > 0) {
-#define SM_ATTN(OT, SP, W)                                                                     \
-    sm::k_sm_attn<OT, SP, W><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
-                                                          cu_seqlens, table, count, H, H_kv,   \
-                                                          (OT*)out, lse)
+        const float qs = o.scale * 1.4426950408889634f;
+        const int nrk = (o.rot + 31) / 32;  // 32-dimension steps holding rotated dimensions
+#define SM_ATTN(OT, SP, W, NRK)                                                                     \
+    sm::k_sm_attn<OT, SP, W, NRK><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
+                                                               cu_seqlens, table, count, H, H_kv,   \
+                                                               (OT*)out, lse, qs)
+#define SM_ATTN_SPLIT(OT)                                        \
+    switch (nrk) {                                               \
+        case 0: SM_ATTN(OT, true, kWavesSplit, 0); break;        \
+        case 1: SM_ATTN(OT, true, kWavesSplit, 1); break;        \
+        case 2: SM_ATTN(OT, true, kWavesSplit, 2); break;        \
+        case 3: SM_ATTN(OT, true, kWavesSplit, 3); break;        \
+        default: SM_ATTN(OT, true, kWavesSplit, 4); break;       \
+    }
         if (out_dtype == LA_DTYPE_BF16) {
-            if (o.split) SM_ATTN(uint16_t, true, kWavesSplit);
-            else SM_ATTN(uint16_t, false, kWavesPlain);
+            if (o.split) SM_ATTN_SPLIT(uint16_t)
+            else SM_ATTN(uint16_t, false, kWavesPlain, 4);
         } else {
-            if (o.split) SM_ATTN(float, true, kWavesSplit);
-            else SM_ATTN(float, false, kWavesPlain);
+            if (o.split) SM_ATTN_SPLIT(float)
+            else SM_ATTN(float, false, kWavesPlain, 4);
         }
+#undef SM_ATTN_SPLIT
 #undef SM_ATTN
     }
     tm.after();

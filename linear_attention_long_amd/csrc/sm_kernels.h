@@ -312,11 +312,14 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
 //   or null.  table/ecount: the plan (null for a single sequence, whose
 //   tiles then run last tile first).
 // SPLIT: qrl, krl hold the bf16 remainders (x - bf16(x)) of the rotated q and
-// k; the scores take three products (hi.hi + lo.hi + hi.lo) and the
-// probabilities are split into bf16 hi + lo for two products with V, which
-// keeps ~16 significant bits in both contractions (one workgroup per CU:
-// the remainders need the registers and LDS of the second).
-template <typename OutT, bool SPLIT, int W>
+// k, and q is NOT pre-scaled: the scores are multiplied by qs (scale * log2 e)
+// in fp32.  Dimensions past the rotated ones are then exact in bf16 on both
+// sides (the inputs are bf16), so the 32-dimension steps kk >= NRK (NRK =
+// ceil(rot / 32)) take one product and the rotated steps three
+// (hi.hi + lo.hi + hi.lo); the probabilities are split into bf16 hi + lo for
+// two products with V (V is exact).  Both contractions keep ~16 significant
+// bits.  Without SPLIT, q carries the scale and NRK is unused.
+template <typename OutT, bool SPLIT, int W, int NRK = 4>
 __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
                                                    const uint16_t* __restrict__ qrl,
@@ -326,7 +329,8 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                                                    const int2* __restrict__ table,
                                                    const int32_t* __restrict__ ecount, int H,
                                                    int Hkv, OutT* __restrict__ out,
-                                                   float* __restrict__ lse) {
+                                                   float* __restrict__ lse, float qs) {
+    static_assert(NRK >= 0 && NRK <= 4, "rotated 32-dimension steps");
     constexpr int BN = SPLIT ? kBlockSplit : kBlockPlain;  // keys per K/V block
     constexpr int NKT = BN / 16;  // 16-key score tiles per block
     constexpr int NKS = BN / 32;  // 32-key steps of the P V product
@@ -365,7 +369,8 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
 
     // Q^T operands: lane (g, c) holds query wq0 + 16 qt + c, dimensions
     // {32 kk + 4g + i, 32 kk + 16 + 4g + i}.
-    bf16x8_t Qf[2][4], Ql[SPLIT ? 2 : 1][4];
+    constexpr int NQL = (SPLIT && NRK > 0) ? NRK : 1;  // steps with a q remainder
+    bf16x8_t Qf[2][4], Ql[2][NQL];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
         const int row = wq0 + 16 * qt + c;
@@ -379,12 +384,14 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             }
             Qf[qt][kk] = as_bf16x8(lo, hi);
             if constexpr (SPLIT) {
-                i16x4_t lo2 = {0, 0, 0, 0}, hi2 = {0, 0, 0, 0};
-                if (row < L) {
-                    lo2 = *(const i16x4_t*)(qrl + off + 32 * kk);
-                    hi2 = *(const i16x4_t*)(qrl + off + 32 * kk + 16);
+                if (kk < NRK) {
+                    i16x4_t lo2 = {0, 0, 0, 0}, hi2 = {0, 0, 0, 0};
+                    if (row < L) {
+                        lo2 = *(const i16x4_t*)(qrl + off + 32 * kk);
+                        hi2 = *(const i16x4_t*)(qrl + off + 32 * kk + 16);
+                    }
+                    Ql[qt][kk < NQL ? kk : 0] = as_bf16x8(lo2, hi2);
                 }
-                Ql[qt][kk] = as_bf16x8(lo2, hi2);
             }
         }
     }
@@ -479,16 +486,24 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                     for (int qt = 0; qt < 2; ++qt)
                         Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk],
                                                   kk == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Sc[kt][qt]);
-                    if constexpr (SPLIT) {  // + k_lo . q_hi + k_hi . q_lo
-                        const bf16x8_t Al = k_operand(sm.kl[buf], 16 * kt + c, 32 * kk, g);
+                    if constexpr (SPLIT) {  // rotated steps: + k_lo . q_hi + k_hi . q_lo
+                        if (kk < NRK) {
+                            const bf16x8_t Al = k_operand(sm.kl[buf], 16 * kt + c, 32 * kk, g);
 #pragma unroll
-                        for (int qt = 0; qt < 2; ++qt) {
-                            Sc[kt][qt] = mfma16x16x32(Al, Qf[qt][kk], Sc[kt][qt]);
-                            Sc[kt][qt] = mfma16x16x32(A, Ql[qt][kk], Sc[kt][qt]);
+                            for (int qt = 0; qt < 2; ++qt) {
+                                Sc[kt][qt] = mfma16x16x32(Al, Qf[qt][kk], Sc[kt][qt]);
+                                Sc[kt][qt] = mfma16x16x32(A, Ql[qt][kk < NQL ? kk : 0], Sc[kt][qt]);
+                            }
                         }
                     }
                 }
             __builtin_amdgcn_s_setprio(0);
+            if constexpr (SPLIT) {  // scores in log2 units
+#pragma unroll
+                for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                    for (int qt = 0; qt < 2; ++qt) Sc[kt][qt] *= qs;
+            }
             if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
