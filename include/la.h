@@ -122,7 +122,20 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               failure path).  A wait that gives up never returns data
  *               it could not verify: the rows it gates get NaN and the
  *               call's device status word is set (la_prefill_wait_status).
- *               Other values: LA_ERR_INVALID_ARGUMENT.                        */
+ *               Other values: LA_ERR_INVALID_ARGUMENT.
+ *   state_access
+ *               la_decode_step's access to the state: 0 = auto (streaming
+ *               when the call touches at least 64 MiB of state, a quarter of
+ *               MI355X's 256 MB Infinity Cache -- between two visits to one
+ *               layer's state a serving step streams every other layer's
+ *               state and weights, so a state that large is not cache-
+ *               resident); 1 = streaming: non-temporal loads and stores, one
+ *               workgroup streaming each (sequence, head)'s block
+ *               contiguously; 2 = cache-resident: plain accesses, the block
+ *               split over four workgroups (faster when the state really is
+ *               in the cache, e.g. the same small batch stepped back to
+ *               back).  Results are identical.  Other values:
+ *               LA_ERR_INVALID_ARGUMENT.                                    */
 typedef struct {
     int32_t block_size;
     int32_t normalized;
@@ -136,6 +149,7 @@ typedef struct {
     int32_t state_rows;
     int32_t featurized;
     int32_t wait_spin_limit;
+    int32_t state_access;
 } la_options_t;
 
 la_options_t la_default_options(void);

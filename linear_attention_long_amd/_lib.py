@@ -59,6 +59,7 @@ class Options(ctypes.Structure):
         ("state_rows", ctypes.c_int32),
         ("featurized", ctypes.c_int32),
         ("wait_spin_limit", ctypes.c_int32),
+        ("state_access", ctypes.c_int32),
     ]
 
 
@@ -220,7 +221,7 @@ def status_string(status: int) -> str:
 
 
 def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1e-6,
-            chunk_tokens=0, featurized=False, wait_spin_limit=0) -> Options:
+            chunk_tokens=0, featurized=False, wait_spin_limit=0, state_access=0) -> Options:
     o = load().la_default_options()
     o.block_size = int(block_size)
     o.normalized = int(bool(normalized))
@@ -230,6 +231,7 @@ def options(block_size=0, normalized=False, gated=False, norm_group=0, rms_eps=1
     o.chunk_tokens = int(chunk_tokens)
     o.featurized = int(bool(featurized))
     o.wait_spin_limit = int(wait_spin_limit)
+    o.state_access = int(state_access)
     return o
 
 

@@ -184,16 +184,18 @@ def la_prefill_wait_status(workspace, status_offset, stream=None) -> int:
 
 def la_decode_step(q, k, v, state, z=None, x=None, w=None, *, normalized=False, norm_group=0,
                    rms_eps=1e-6, out_dtype=torch.float32, out=None, workspace=None,
-                   state_slots=None, featurized=False, stream=None):
+                   state_slots=None, featurized=False, stream=None, state_access=0):
     """One decode token per sequence.  q, k, v: [N, H, d]; state [N, H, d, d]
     float32 and z [N, H, d] (normalised mode) are updated in place (with
     ``state_slots``, int32 [N] on the GPU: pools [rows, H, d, d] / [rows, H, d]
     indexed by slot).  Returns out [N, H*d].  ``out``/``workspace`` may be
-    passed to reuse buffers."""
+    passed to reuse buffers.  ``state_access``: 0 auto, 1 streaming
+    (non-temporal), 2 cache-resident (include/la.h); results are identical."""
     lib = _lib.load()
     N, H, d = q.shape
     gated = x is not None
-    opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0, featurized)
+    opt = _lib.options(64, normalized, gated, norm_group, rms_eps, 0, featurized,
+                       state_access=state_access)
     _slots(opt, state_slots, state)
     in_dt, out_dt = _dtype(q.dtype), _dtype(out_dtype)
     if out is None:

@@ -49,6 +49,7 @@ constexpr size_t kStatusBytes = 256;    // the call's device status word, padded
 #define LA_DECODE_SPLIT 4
 #endif
 constexpr int kDecodeSplit = LA_DECODE_SPLIT;  // decode workgroups per (sequence, head), plain mode
+constexpr int64_t kStreamStateBytes = (int64_t)64 << 20;  // decode: stream states at least this large
 
 // Workgroups of `kernel` (256 threads) the current device keeps resident at
 // once, or 0 when cooperative launch is unavailable.
@@ -75,6 +76,7 @@ struct Opts {
     int rows;              // rows of the state arrays when slots is given
     bool feat;             // q, k, v are feature vectors already (no SiLU inside)
     int spin;              // retries per bounded wait of the fused gate (< 0: none)
+    int state_access;      // decode: 0 auto, 1 streaming (non-temporal), 2 cache-resident
 };
 
 // Records the caller's timing events around each launched kernel.
@@ -147,6 +149,8 @@ la_status_t parse_options(const la_options_t* opt, int H, int d, Opts& o) {
     o.feat = x.featurized == 1;
     if (x.wait_spin_limit < -1) return LA_ERR_INVALID_ARGUMENT;
     o.spin = x.wait_spin_limit == 0 ? kSpinLimit : x.wait_spin_limit;
+    if (x.state_access < 0 || x.state_access > 2) return LA_ERR_INVALID_ARGUMENT;
+    o.state_access = x.state_access;
     return LA_OK;
 }
 
@@ -539,6 +543,7 @@ la_options_t la_default_options(void) {
     o.state_rows = 0;
     o.featurized = 0;
     o.wait_spin_limit = 0;
+    o.state_access = 0;
     return o;
 }
 
@@ -782,14 +787,27 @@ static la_status_t decode_step_impl(bool launch, const void* q, const void* k, c
     Timer tm(o, st);
     void* ydst = o.gated ? (need ? workspace : out) : out;
     const bool yf32 = o.gated || out_dtype == LA_DTYPE_F32;
-    // plain mode, d = 128: kDecodeSplit workgroups per (sequence, head), each
-    // owning 128 / kDecodeSplit state columns
+    // The state's access mode: streaming (non-temporal hints, one workgroup
+    // per (sequence, head) streaming its block contiguously) unless the state
+    // the call touches is small enough to stay cache-resident between calls
+    // (auto: under a quarter of the 256 MB Infinity Cache; a serving step
+    // streams every layer's state and weights between two visits to one
+    // layer), or the caller says it is.  Cache-resident, plain mode, d = 128:
+    // kDecodeSplit workgroups per (sequence, head), each owning 128 /
+    // kDecodeSplit state columns.
+    const int64_t touched = (int64_t)N * H * d * d * 4;
+    const bool stream = o.state_access == 1 || (o.state_access == 0 && touched >= kStreamStateBytes);
     const unsigned grid = (unsigned)((int64_t)N * H);
 #define LA_DEC(DD, IT, OT, NN)                                                                     \
     do {                                                                                           \
-        constexpr int SP = (!(NN) && (DD) == 128) ? kDecodeSplit : 1;                              \
-        k_decode<DD, IT, OT, NN, SP><<<grid * SP, 256, 0, st>>>((const IT*)q, (const IT*)k,         \
-            (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H, o.feat ? 1 : 0);               \
+        if (stream) {                                                                              \
+            k_decode<DD, IT, OT, NN, 1, true><<<grid, 256, 0, st>>>((const IT*)q, (const IT*)k,     \
+                (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H, o.feat ? 1 : 0);           \
+        } else {                                                                                   \
+            constexpr int SP = (!(NN) && (DD) == 128) ? kDecodeSplit : 1;                          \
+            k_decode<DD, IT, OT, NN, SP><<<grid * SP, 256, 0, st>>>((const IT*)q, (const IT*)k,     \
+                (const IT*)v, state, z, (OT*)ydst, o.slots, o.rows, H, o.feat ? 1 : 0);           \
+        }                                                                                          \
     } while (0)
 #define LA_DEC_OUT(DD, IT)                                                                  \
     do {                                                                                    \

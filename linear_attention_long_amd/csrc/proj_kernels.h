@@ -158,15 +158,23 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     fragments(0, 0, A0, B0);
+    // (sched_barrier keeps each group of fragment reads ahead of the
+    // products that do not depend on it; left alone, the scheduler sinks the
+    // reads next to their consumers, past the loop's back edge)
     for (int kt = 0; kt < nk; ++kt) {
         const int b = kt & 1;
         fragments(b, 1, A1, B1);
+        __builtin_amdgcn_sched_barrier(0);
         products(A0, B0);
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
         gload(kt + 2, b);
         fragments(b ^ 1, 0, A0, B0);
+        __builtin_amdgcn_sched_barrier(0);
         products(A1, B1);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // epilogue: acc[i][jj][e] = P[token m0 + 64 wm + 16 jj + c][feature n0 + 128 wn + 16 i + 4 g + e]

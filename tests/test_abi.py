@@ -52,7 +52,7 @@ def test_default_options(lib):
     o = lib.la_default_options()
     assert (o.block_size, o.normalized, o.gated, o.norm_group, o.chunk_tokens) == (0, 0, 0, 0, 0)
     assert abs(o.rms_eps - 1e-6) < 1e-12
-    assert o.featurized == 0 and o.wait_spin_limit == 0
+    assert o.featurized == 0 and o.wait_spin_limit == 0 and o.state_access == 0
 
 
 def test_featurized_inputs_supported_set(lib):

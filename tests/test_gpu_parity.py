@@ -364,10 +364,11 @@ def test_varlen_matches_oracle(dtype, d, chunk):
 
 # ------------------------------------------------------------------- decode --
 
+@pytest.mark.parametrize("access", [0, 1, 2])   # auto (here cache-resident), streaming, cache-resident
 @pytest.mark.parametrize("normalized", [False, True])
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
-def test_decode_steps(normalized, dtype, d):
-    banner("decode normalized=%s dtype=%s d=%d" % (normalized, dtype, d))
+def test_decode_steps(normalized, dtype, d, access):
+    banner("decode normalized=%s dtype=%s d=%d access=%d" % (normalized, dtype, d, access))
     N, H, steps = 3, 4, 12
     S0 = randn((N, H, d, d), 80, 0.01)
     z0 = randn((N, H, d), 81, 0.01).abs() + 1.0 if normalized else None
@@ -378,7 +379,8 @@ def test_decode_steps(normalized, dtype, d):
     for t in range(steps):
         q, k, v = (randn((N, H, d), 100 * t + i, 1.0, shift if i < 2 else 0.0, dtype=dtype)
                    for i in range(3))
-        y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S_dev, z_dev, normalized=normalized)
+        y = api.la_decode_step(q.to(DEV), k.to(DEV), v.to(DEV), S_dev, z_dev, normalized=normalized,
+                               state_access=access)
         yr, S_ref, z_new = O.decode_step(q, k, v, S_ref, z_ref, normalized)
         if normalized:
             z_ref = z_new
@@ -500,3 +502,28 @@ def test_state_alias_in_place():
         torch.cuda.synchronize()
         assert rel_err(np64(out), ref) <= TOL_BF16
         assert rel_err(np64(S), Sref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("normalized", [False, True])
+def test_decode_access_modes_agree(normalized):
+    """Streaming (non-temporal, one workgroup per sequence-head) and
+    cache-resident (plain, four workgroups) state access: the state update is
+    elementwise and identical, so S (and z) agree bit for bit; y only
+    reassociates its sum over rows."""
+    banner("decode access modes, normalized=%s" % normalized)
+    N, H, d = 5, 6, 128
+    S0 = randn((N, H, d, d), 90, 0.01).to(DEV)
+    z0 = (randn((N, H, d), 91, 0.01).abs() + 1.0).to(DEV) if normalized else None
+    shift = 1.0 if normalized else 0.0
+    Ss = {a: S0.clone() for a in (1, 2)}
+    zs = {a: None if z0 is None else z0.clone() for a in (1, 2)}
+    for t in range(6):
+        q, k, v = (randn((N, H, d), 300 * t + i, 1.0, shift if i < 2 else 0.0,
+                         dtype=torch.bfloat16).to(DEV) for i in range(3))
+        ys = {a: api.la_decode_step(q, k, v, Ss[a], zs[a], normalized=normalized, state_access=a)
+              for a in (1, 2)}
+        torch.cuda.synchronize()
+        assert torch.equal(Ss[1], Ss[2])
+        if normalized:
+            assert torch.equal(zs[1], zs[2])
+        assert rel_err(np64(ys[1]), np64(ys[2])) <= 1e-5

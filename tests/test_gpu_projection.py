@@ -123,3 +123,26 @@ def test_projection_then_path(featurize):
     e, es = rel_err(out.double().cpu().numpy(), ref), rel_err(S.double().cpu().numpy(), Sref[0])
     print("projection then path (featurize=%s): out %.2e state %.2e" % (featurize, e, es))
     assert e <= 1e-2 and es <= 1e-2
+
+
+def test_projection_1m_workload_sampled():
+    """The bench's 1M-token projection (hidden [1048576, 6144] drawn on the GPU
+    as the bench draws it): sampled rows, including the first and last tokens
+    and tile edges, of all four outputs."""
+    from linear_attention_long_amd import inputs
+
+    w = inputs.WORKLOADS["proj_1m"]
+    banner("projection 1M sampled")
+    h, wt = inputs.projection_inputs(w, device=DEV)
+    T, F = h.shape[0], w.H * w.d
+    got = api.la_qkvx_projection(h, wt, F)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, T // 2, T - 257, T - 256, T - 1],
+                                     r.integers(0, T, 120)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    ref = P.project(h[ri].cpu(), wt.cpu(), F)
+    for a, b in zip(got, ref):
+        check_bf16(a[ri].double().cpu().numpy(), b)
+    del h, got
+    torch.cuda.empty_cache()
