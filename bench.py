@@ -700,64 +700,69 @@ def calibrate_copy(args, torch):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "main_gated_prefill_1m_traffic.md")
+SOFTMAX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_attention_32k_traffic.md")
+PROJECTION_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "projection_gemm_32k_traffic.md")
 SOURCES = os.path.join(ROOT, "linear_attention_long_amd", "csrc")
 
 
-def source_digest() -> str:
-    """sha256 over the linear-attention kernels' HIP sources (names and
-    contents of csrc/la_*)."""
+def _digest(names) -> str:
+    """sha256 over the names and contents of the given csrc/ files, in order."""
     import hashlib
 
     h = hashlib.sha256()
-    for name in sorted(os.listdir(SOURCES)):
-        if name.startswith("la_") and name.endswith((".h", ".hip")):
-            h.update(name.encode())
-            h.update(open(os.path.join(SOURCES, name), "rb").read())
-    return h.hexdigest()
-
-
-def measured_traffic():
-    """HBM bytes per launch of the fused main pass from the committed counter
-    summary, or None when the sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    vals = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and line.strip().startswith(("source_sha256", "hbm_bytes_per_launch")):
-            key, val = line.strip().strip("`").split(":", 1)
-            vals[key.strip()] = val.strip().strip("`")
-    if vals.get("source_sha256") != source_digest() or "hbm_bytes_per_launch" not in vals:
-        return None
-    return float(vals["hbm_bytes_per_launch"])
-
-
-SOFTMAX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "softmax_attention_32k_traffic.md")
-
-
-def softmax_source_digest() -> str:
-    """sha256 over the sources the softmax kernels are built from."""
-    import hashlib
-
-    h = hashlib.sha256()
-    for name in ("la_device.h", "sm_api.hip", "sm_kernels.h"):
+    for name in names:
         h.update(name.encode())
         h.update(open(os.path.join(SOURCES, name), "rb").read())
     return h.hexdigest()
 
 
-def measured_softmax_traffic():
-    """HBM bytes per launch of the softmax attention kernel (32K workload) from
-    the committed counter summary, or None when its sources changed."""
-    if not os.path.exists(SOFTMAX_TRAFFIC_FILE):
+def source_digest() -> str:
+    """sha256 over the linear-attention kernels' HIP sources (names and
+    contents of csrc/la_*, sorted)."""
+    return _digest(sorted(n for n in os.listdir(SOURCES)
+                          if n.startswith("la_") and n.endswith((".h", ".hip"))))
+
+
+def softmax_source_digest() -> str:
+    """sha256 over the sources the softmax kernels are built from."""
+    return _digest(("la_device.h", "sm_api.hip", "sm_kernels.h"))
+
+
+def projection_source_digest() -> str:
+    """sha256 over the sources the projection GEMM is built from."""
+    return _digest(("la_device.h", "proj_api.hip", "proj_kernels.h"))
+
+
+def committed_traffic(path, digest):
+    """HBM bytes per launch from a committed counter summary (its
+    `hbm_bytes_per_launch` line), or None when the file is missing or its
+    `source_sha256` line no longer matches `digest` (the kernel changed since
+    the counters were taken)."""
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(SOFTMAX_TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and line.strip().startswith(("source_sha256", "hbm_bytes_per_launch")):
             key, val = line.strip().strip("`").split(":", 1)
             vals[key.strip()] = val.strip().strip("`")
-    if vals.get("source_sha256") != softmax_source_digest() or "hbm_bytes_per_launch" not in vals:
+    if vals.get("source_sha256") != digest or "hbm_bytes_per_launch" not in vals:
         return None
     return float(vals["hbm_bytes_per_launch"])
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused main pass (1M-token prefill)."""
+    return committed_traffic(TRAFFIC_FILE, source_digest())
+
+
+def measured_softmax_traffic():
+    """HBM bytes per launch of the softmax attention kernel (32K, split operands)."""
+    return committed_traffic(SOFTMAX_TRAFFIC_FILE, softmax_source_digest())
+
+
+def measured_projection_traffic():
+    """HBM bytes per launch of the projection GEMM (proj_32k)."""
+    return committed_traffic(PROJECTION_TRAFFIC_FILE, projection_source_digest())
 
 
 def cpu_baseline(args, inputs, gpu_head=None):
@@ -987,7 +992,7 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "input projection GEMM (k_proj), proj_32k",
                          "achieved": proj["kernel"]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": proj["kernel"]["mfma_bf16_peak_frac"],
-                         "traffic": None,
+                         "traffic": measured_projection_traffic(),
                          "algorithmic_flops_per_launch": proj["kernel"]["algorithmic_flops"],
                          "avg_launch_ms": proj["kernel"]["kernel_ms"]},
             **proj},
