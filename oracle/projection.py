@@ -1,5 +1,5 @@
-"""CPU oracle of the input projection of a lightning-attention layer --
-TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the input and output projections of a lightning-attention
+layer -- TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module.  It shares nothing with the HIP library.
@@ -19,8 +19,21 @@ projection is one product with four column blocks:
 With ``featurize=False`` the first three blocks are returned unactivated
 (pre-activations for a path that applies SiLU itself).  Everything is fp64:
 numpy's matmul on the exactly widened inputs, SiLU(x) = x / (1 + exp(-x)).
-The pins (``tests/test_oracle_projection_pins.py``) check it against a
-pure-Python triple loop, closed forms for selection and constant weights,
+The output projection maps the gated attention output back to the hidden
+width: page "MiniMax-01系列大模型：超长上下文与多模态能力深度解析与部署指南",
+FAQ Q5 (fine-tuning), names the attention layer's four projection matrices
+Q, K, V and O.  For one GPU's heads (its F = H * d columns of the gated
+output) the product with the matching columns of W_o is that GPU's partial
+sum of the layer output:
+
+    out = y @ W_o^T,   y: [T, F] gated output,  W_o: [N, F]  (row n = hidden feature n)
+
+and the partial sums of the GPUs holding the other heads add up to the
+whole product (the identity ``test_out_projection_column_split_sums_to_the_whole``
+pins).
+
+The pins (``tests/test_oracle_projection_pins.py``) check both against
+pure-Python triple loops, closed forms for selection and constant weights,
 and the composition with the pinned path oracle.
 """
 from __future__ import annotations
@@ -58,3 +71,16 @@ def project(hidden, weight, F, featurize=True, rows=None):
     if featurize:
         blocks = [silu(b) for b in blocks[:3]] + [blocks[3]]
     return tuple(np.ascontiguousarray(b) for b in blocks)
+
+
+def out_project(y, weight, rows=None):
+    """y [T, F] (the gated attention output), weight [N, F] (any float dtype,
+    widened exactly).  Returns y @ weight^T, [T, N] fp64 (or [len(rows), N]
+    for the listed token rows)."""
+    a = _f64(y)
+    if rows is not None:
+        a = a[np.asarray(rows, dtype=np.int64)]
+    W = _f64(weight)
+    if W.ndim != 2 or a.ndim != 2 or W.shape[1] != a.shape[1]:
+        raise ValueError("weight must be [N, F] with F = y's width")
+    return np.ascontiguousarray(a @ W.T)

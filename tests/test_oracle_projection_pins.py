@@ -106,3 +106,76 @@ def test_rejects_mismatched_weight():
         P.project(np.zeros((2, 8)), np.zeros((12, 8)), 4)
     with pytest.raises(ValueError):
         P.project(np.zeros((2, 8)), np.zeros((16, 9)), 4)
+
+
+# ---- the output projection (page "MiniMax-01系列大模型：超长上下文与多模态能力深度解析与部署指南",
+# FAQ Q5: the attention layer's Q, K, V and O projection matrices) ----
+
+
+def test_out_projection_against_a_python_triple_loop():
+    """Every output of a small case against sums written out in pure Python."""
+    rng = np.random.default_rng(11)
+    T, F, N = 3, 5, 4
+    y = rng.standard_normal((T, F))
+    W = rng.standard_normal((N, F))
+    got = P.out_project(y, W)
+    assert got.shape == (T, N)
+    for t in range(T):
+        for n in range(N):
+            s = 0.0
+            for f in range(F):
+                s += float(y[t, f]) * float(W[n, f])
+            assert abs(got[t, n] - s) <= 1e-13 * max(1.0, abs(s))
+
+
+def test_out_projection_selection_and_constants():
+    """Unit-vector weight rows select (and scale) input features exactly;
+    constant inputs times constant rows give F * c * w."""
+    rng = np.random.default_rng(12)
+    T, F = 6, 8
+    y = rng.standard_normal((T, F))
+    perm = [3, 0, 7, 7, 1]
+    W = np.zeros((len(perm), F))
+    for n, f in enumerate(perm):
+        W[n, f] = 2.0 if n % 2 else 1.0
+    got = P.out_project(y, W)
+    for n, f in enumerate(perm):
+        assert np.array_equal(got[:, n], y[:, f] * (2.0 if n % 2 else 1.0))
+    c = P.out_project(np.full((2, F), 0.5), np.full((3, F), -0.25))
+    assert np.array_equal(c, np.full((2, 3), F * 0.5 * -0.25))
+
+
+def test_out_projection_column_split_sums_to_the_whole():
+    """The heads of a layer split over devices: each holds some columns of y
+    and the matching columns of W_o; the per-device partial products add up
+    to the product over all heads."""
+    rng = np.random.default_rng(13)
+    T, F, N = 9, 12, 7
+    y = rng.standard_normal((T, F))
+    W = rng.standard_normal((N, F))
+    whole = P.out_project(y, W)
+    parts = sum(P.out_project(y[:, a:b], W[:, a:b]) for a, b in ((0, 4), (4, 9), (9, 12)))
+    assert np.abs(whole - parts).max() <= 1e-12 * np.abs(whole).max()
+
+
+def test_out_projection_linearity_rows_and_bf16():
+    """Linear in y; sampled rows equal the full rows; bf16 widens exactly."""
+    g = torch.Generator().manual_seed(14)
+    T, F, N = 20, 64, 24
+    y1 = torch.randn((T, F), generator=g).to(torch.bfloat16)
+    y2 = torch.randn((T, F), generator=g).to(torch.bfloat16)
+    W = torch.randn((N, F), generator=g).to(torch.bfloat16)
+    a = P.out_project(y1, W)
+    b = P.out_project(y2, W)
+    ab = P.out_project(3.0 * y1.double().numpy() + y2.double().numpy(), W)
+    assert np.abs(ab - (3.0 * a + b)).max() <= 1e-12 * np.abs(ab).max()
+    rows = [0, 19, 5, 5]
+    assert np.array_equal(P.out_project(y1, W, rows=rows), a[rows])
+    assert np.array_equal(a, y1.double().numpy() @ W.double().numpy().T)
+
+
+def test_out_projection_rejects_mismatched_weight():
+    with pytest.raises(ValueError):
+        P.out_project(np.zeros((2, 8)), np.zeros((3, 9)))
+    with pytest.raises(ValueError):
+        P.out_project(np.zeros(8), np.zeros((3, 8)))
