@@ -555,11 +555,13 @@ def bench_softmax(args, torch, lib, _lib, inputs):
 
 
 def bench_projection(args, torch, lib, _lib, inputs):
-    """The layer's input projection (include/la_proj.h): the GEMM kernel on
-    proj_32k (HIP events around each launch; algorithmic flops 2 T K 4F), and
-    the layer's input side end to end on 32K and 1M tokens: the projection
-    with SiLU in its epilogue followed by the path in its features-given mode,
-    against the raw projection followed by the path's own SiLU."""
+    """The layer's projections (include/la_proj.h): the input GEMM kernel on
+    proj_32k (HIP events around each launch; algorithmic flops 2 T K 4F) and
+    the output GEMM on the same layer's output side (2 T F K); the layer's
+    input side end to end on 32K and 1M tokens (the projection with SiLU in
+    its epilogue followed by the path in its features-given mode, against the
+    raw projection followed by the path's own SiLU), and the whole layer with
+    the output projection after the path."""
     from linear_attention_long_amd import api
 
     res = {}
@@ -598,6 +600,38 @@ def bench_projection(args, torch, lib, _lib, inputs):
     log("projection %s: %.3f ms, %.0f TFLOP/s = %.1f%% of the bf16 peak"
         % (w.name, ms, tfs, 100 * tfs / MFMA_BF16_PEAK_TFS))
     del outs
+
+    # the output projection: y [T, F] bf16 times W_o [K, F]^T -> [T, K] bf16
+    yo, wo = inputs.out_projection_inputs(w, device="cuda")
+    zo = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    oopt = _lib.proj_options(False)
+    with HipEvents(2 * (reps + 1)) as ev:
+        def ocall(i):
+            oopt.timing_events = ev.ptr(2 * i)
+            oopt.n_timing = 1
+            st = lib.la_out_projection(yo.data_ptr(), wo.data_ptr(), zo.data_ptr(), T, F, K,
+                                       _lib.LA_DTYPE_BF16, ctypes.byref(oopt),
+                                       ctypes.c_void_p(stream))
+            _lib.check(st, "la_out_projection")
+
+        ocall(0)
+        torch.cuda.synchronize()
+        for i in range(1, reps + 1):
+            ocall(i)
+        torch.cuda.synchronize()
+        otimes = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(1, reps + 1))
+    oms = otimes[len(otimes) // 2]
+    oflops = 2.0 * T * F * K
+    otfs = oflops / (oms * 1e-3) / 1e12
+    res["out_kernel"] = {"workload": w.name + " output side", "T": T, "K_in": F, "N": K,
+                         "out": "bf16 partial sum of the layer output (this device's heads)",
+                         "kernel_ms": oms, "kernel_ms_mean": sum(otimes) / len(otimes),
+                         "algorithmic_flops": oflops, "TFLOPs": otfs,
+                         "mfma_bf16_peak_frac": otfs / MFMA_BF16_PEAK_TFS, "reps": reps}
+    log("output projection %s: %.3f ms, %.0f TFLOP/s = %.1f%% of the bf16 peak"
+        % (w.name, oms, otfs, 100 * otfs / MFMA_BF16_PEAK_TFS))
+    del yo, zo
+
     layer = {}
     for name, nrep in (("proj_32k", 10), ("proj_1m", 3)):
         wl = inputs.WORKLOADS[name]
@@ -613,15 +647,25 @@ def bench_projection(args, torch, lib, _lib, inputs):
             return api.la_prefill(q.view(1, T, H, d), k.view(1, T, H, d), v.view(1, T, H, d),
                                   xg.view(1, T, F), featurized=feat, return_state=False)[0]
 
+        z = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+
+        def whole():
+            q, k, v, xg = api.la_qkvx_projection(h, wt, F, featurize=True, out=o4)
+            y = api.la_prefill(q.view(1, T, H, d), k.view(1, T, H, d), v.view(1, T, H, d),
+                               xg.view(1, T, F), featurized=True, out_dtype=torch.bfloat16,
+                               return_state=False)[0]
+            return api.la_out_projection(y.view(T, F), wo, out=z)
+
         entry = {}
-        for key, feat in (("silu_in_projection", True), ("silu_in_path", False)):
-            side(feat)
+        for key, fn in (("silu_in_projection", lambda: side(True)),
+                        ("silu_in_path", lambda: side(False)), ("whole_layer", whole)):
+            fn()
             torch.cuda.synchronize()
             ts = []
             for _ in range(nrep):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                side(feat)
+                fn()
                 b.record()
                 b.synchronize()
                 ts.append(a.elapsed_time(b))
@@ -629,14 +673,19 @@ def bench_projection(args, torch, lib, _lib, inputs):
             entry[key + "_ms"] = ts[len(ts) // 2]
         entry["tokens"] = T
         entry["tokens_per_s_silu_in_projection"] = T / (entry["silu_in_projection_ms"] * 1e-3)
+        entry["tokens_per_s_whole_layer"] = T / (entry["whole_layer_ms"] * 1e-3)
+        entry["whole_layer_note"] = ("input projection (SiLU in the epilogue), the path (features "
+                                     "given, gated, bf16 out), output projection; whole calls "
+                                     "through the binding")
         layer[name] = entry
         log("layer input side %s: projection + path %.3f ms with SiLU in the projection's "
-            "epilogue, %.3f ms with SiLU in the path" % (name, entry["silu_in_projection_ms"],
-                                                        entry["silu_in_path_ms"]))
-        del o4
+            "epilogue, %.3f ms with SiLU in the path; whole layer with the output projection "
+            "%.3f ms" % (name, entry["silu_in_projection_ms"], entry["silu_in_path_ms"],
+                         entry["whole_layer_ms"]))
+        del o4, z
         torch.cuda.empty_cache()
     res["layer_input_side"] = layer
-    del h, wt
+    del h, wt, wo
     torch.cuda.empty_cache()
     return res
 
@@ -995,6 +1044,14 @@ def main():
                          "traffic": measured_projection_traffic(),
                          "algorithmic_flops_per_launch": proj["kernel"]["algorithmic_flops"],
                          "avg_launch_ms": proj["kernel"]["kernel_ms"]},
+            "out_roofline": {"bound": "mfma",
+                             "kernel": "output projection GEMM (k_proj, one output block), "
+                                       "proj_32k output side",
+                             "achieved": proj["out_kernel"]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
+                             "unit": "TFLOP/s", "frac": proj["out_kernel"]["mfma_bf16_peak_frac"],
+                             "traffic": None,
+                             "algorithmic_flops_per_launch": proj["out_kernel"]["algorithmic_flops"],
+                             "avg_launch_ms": proj["out_kernel"]["kernel_ms"]},
             **proj},
         "features_given_prefill": None if feat is None else features_given_summary(feat, main_name),
     }

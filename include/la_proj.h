@@ -1,6 +1,6 @@
 /*
- * la_proj.h -- C ABI of liblinattn's input projection of a lightning-attention
- * layer (AMD Instinct MI355X, gfx950).
+ * la_proj.h -- C ABI of liblinattn's input and output projections of a
+ * lightning-attention layer (AMD Instinct MI355X, gfx950).
  *
  * Method source: page "MiniMax-Text-01 405B MoE模型架构与训练策略解析",
  * section 2.1: the layer computes Q, K, V = SiLU of projections of its input
@@ -60,12 +60,39 @@ la_proj_options_t la_proj_default_options(void);
  *   LA_DTYPE_BF16 or LA_DTYPE_F32.
  * Outputs must not overlap each other or the inputs.  Errors: NULL or
  * misaligned pointers, overlaps, bad sizes or options ->
- * LA_ERR_INVALID_ARGUMENT; K or F off their multiples ->
+ * LA_ERR_INVALID_ARGUMENT; K or F off their multiples, or more than 2^28
+ * output tiles of 256 x 256 (ceil(T/256) * nblk * F / 256) ->
  * LA_ERR_UNSUPPORTED. */
 la_status_t la_qkvx_projection(const void* hidden, const void* weight,
                                void* q, void* k, void* v, void* x_gate,
                                int32_t T, int32_t K, int32_t F, la_dtype_t out_dtype,
                                const la_proj_options_t* opt, void* hip_stream);
+
+/* The output projection, the same bf16 matrix-core GEMM on the other side of
+ * the path.  Page "MiniMax-01系列大模型：超长上下文与多模态能力深度解析与部署指南",
+ * FAQ Q5 (fine-tuning), names the attention layer's projection matrices Q, K,
+ * V and O; this call is the O side for one GPU's H heads:
+ *
+ *     out = y @ weight^T
+ *
+ *   y        [T, K] bf16, the gated attention output of this GPU's heads
+ *            (la_prefill's output in bf16, K = H * d)
+ *   weight   [N, K] bf16, row n holds hidden feature n: the columns of W_o
+ *            that belong to these heads
+ *   out      [T, N] out_dtype (LA_DTYPE_BF16 or LA_DTYPE_F32): this GPU's
+ *            partial sum of the layer output (the products of the GPUs that
+ *            hold the other heads add up to the whole; that reduction is not
+ *            part of this call)
+ *   T >= 0 (T = 0: nothing to do), K a multiple of 64 in [64, 2^20], N a
+ *   multiple of 256 in [256, 2^20].  opt may be NULL; only its timing fields
+ *   are used (there is no feature map on this side).
+ * out must not overlap y or weight.  Errors as for la_qkvx_projection: NULL or
+ * misaligned pointers, overlaps, bad sizes -> LA_ERR_INVALID_ARGUMENT; K or N
+ * off their multiples, or more than 2^28 output tiles (ceil(T/256) * N / 256)
+ * -> LA_ERR_UNSUPPORTED; all checks before any HIP call. */
+la_status_t la_out_projection(const void* y, const void* weight, void* out,
+                              int32_t T, int32_t K, int32_t N, la_dtype_t out_dtype,
+                              const la_proj_options_t* opt, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -42,6 +42,7 @@ EXPORTS = (
     "la_softmax_workspace_bytes",
     "la_proj_default_options",
     "la_qkvx_projection",
+    "la_out_projection",
 )
 
 
@@ -209,6 +210,9 @@ def load() -> ctypes.CDLL:
         lib.la_qkvx_projection.restype = ctypes.c_int
         lib.la_qkvx_projection.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                            ctypes.c_int, ctypes.POINTER(ProjOptions), _vp]
+        lib.la_out_projection.restype = ctypes.c_int
+        lib.la_out_projection.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_int,
+                                          ctypes.POINTER(ProjOptions), _vp]
         _lib = lib
         return lib
 

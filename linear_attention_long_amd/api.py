@@ -341,3 +341,24 @@ def la_qkvx_projection(hidden, weight, F, *, gate=True, featurize=True, out_dtyp
     _lib.check(st, "la_qkvx_projection")
     _keep_for(stream, *outs)
     return tuple(outs)
+
+
+def la_out_projection(y, weight, *, out_dtype=torch.bfloat16, out=None, stream=None):
+    """The layer's output projection (include/la_proj.h): y [T, K] bf16 (the
+    gated attention output of these heads, K = H * d), weight [N, K] bf16
+    (the O projection's columns for these heads, row n = hidden feature n).
+    Returns y @ weight^T, [T, N] ``out_dtype``: this device's partial sum of
+    the layer output.  ``out``: a preallocated [T, N] output to write instead."""
+    lib = _lib.load()
+    T, K = y.shape
+    N, Kw = weight.shape
+    if Kw != K:
+        raise ValueError("weight must be [N, K] with K = y's width")
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype, device=y.device)
+    opt = _lib.proj_options(False)
+    st = lib.la_out_projection(_ptr(y), _ptr(weight), _ptr(out), T, K, N, _dtype(out.dtype),
+                               ctypes.byref(opt), _stream(stream))
+    _lib.check(st, "la_out_projection")
+    _keep_for(stream, out)
+    return out

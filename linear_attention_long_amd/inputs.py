@@ -263,3 +263,17 @@ def projection_inputs(w: Workload, T: int | None = None, device=None):
     hidden = normal((T, K), w.seed, 0, 1.0, torch.bfloat16, dev)
     weight = normal((4 * F, K), w.seed, 1, 1.0 / math.sqrt(K), torch.bfloat16, dev)
     return hidden, weight
+
+
+def out_projection_inputs(w: Workload, T: int | None = None, device=None):
+    """The output projection's operands for the same layer: y [T, F] ~ N(0,1)
+    (a stand-in for the gated attention output, which the RMSNorm leaves at
+    unit scale) and W_o [K, F] ~ N(0, 1/F) (hidden width K = the input
+    projection's), both bf16."""
+    T = w.T if T is None else T
+    K = w.extra["K"]
+    F = w.H * w.d
+    dev = w.gen_device if device is None else device
+    y = normal((T, F), w.seed, 2, 1.0, torch.bfloat16, dev)
+    wo = normal((K, F), w.seed, 3, 1.0 / math.sqrt(F), torch.bfloat16, dev)
+    return y, wo

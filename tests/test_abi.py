@@ -335,3 +335,35 @@ def test_projection_rejects_bad_arguments(lib):
     bad = _lib.proj_options()
     bad.featurize = 2
     assert call(o=bad) == INVALID
+    # more output tiles than the kernel indexes: T = 2^31 - 1 tokens, 4 x 2^20 features
+    far = [ctypes.c_void_p(0x7F0000000000 + (i << 53)) for i in range(4)]
+    assert call(T=(1 << 31) - 1, K=64, F=1 << 20, q=far[0], k=far[1], v=far[2],
+                xg=far[3]) == UNSUPPORTED
+
+
+
+def test_out_projection_rejects_bad_arguments(lib):
+    """la_out_projection's host checks (no call reaches the device)."""
+    def call(y=A[0], w=A[1], out=A[2], T=300, K=1024, N=6144, odt=BF16, o=None):
+        o = o or _lib.proj_options(False)
+        return lib.la_out_projection(y, w, out, T, K, N, odt, ctypes.byref(o), None)
+
+    assert call(T=0) == _lib.LA_OK                       # nothing to do
+    assert call(y=None) == INVALID
+    assert call(w=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(K=100) == UNSUPPORTED                    # not a multiple of 64
+    assert call(N=1000) == UNSUPPORTED                   # not a multiple of 256
+    assert call(K=0) == INVALID
+    assert call(N=1 << 21) == INVALID
+    assert call(odt=7) == INVALID
+    assert call(out=ctypes.c_void_p(0x30000008)) == INVALID  # misaligned
+    assert call(out=A[0]) == INVALID                     # output overlaps the input
+    assert call(out=ctypes.c_void_p(A[1].value + 4096)) == INVALID  # ... or the weight
+    timed = _lib.proj_options(False)
+    timed.n_timing = 1                                   # events asked for, none given
+    assert call(o=timed) == INVALID
+    # more output tiles than the kernel indexes: T = 2^31 - 1 tokens, N = 2^20
+    far = ctypes.c_void_p(0x7F0000000000)
+    assert call(T=(1 << 31) - 1, K=64, N=1 << 20, out=far) == UNSUPPORTED

@@ -146,3 +146,77 @@ def test_projection_1m_workload_sampled():
         check_bf16(a[ri].double().cpu().numpy(), b)
     del h, got
     torch.cuda.empty_cache()
+
+
+# ---- the output projection (la_out_projection): y [T, K] bf16 times W_o [N, K]^T ----
+
+
+def make_out(T, K, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    y = torch.randn((T, K), generator=g).to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=g) / np.sqrt(K)).to(torch.bfloat16)
+    return y, w
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 64, 256), (255, 128, 512), (257, 1024, 6144),
+                                   (1000, 1024, 6144)])
+def test_out_projection_fp32_out(T, K, N):
+    banner("out projection T=%d K=%d N=%d fp32 out" % (T, K, N))
+    y, w = make_out(T, K, N, 50 + T)
+    got = api.la_out_projection(y.to(DEV), w.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_f32(got.double().cpu().numpy(), P.out_project(y, w))
+
+
+@pytest.mark.parametrize("T", [300, 4096])
+def test_out_projection_bf16_out(T):
+    K, N = 1024, 6144
+    banner("out projection T=%d bf16 out" % T)
+    y, w = make_out(T, K, N, 60 + T)
+    got = api.la_out_projection(y.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    check_bf16(got.double().cpu().numpy(), P.out_project(y, w))
+
+
+def test_out_projection_32k_sampled_rows():
+    """The benched shape (T = 32768, K = 1024, N = 6144): sampled rows, and
+    the untouched guard around the output."""
+    T, K, N = 32768, 1024, 6144
+    banner("out projection 32K sampled")
+    y, w = make_out(T, K, N, 71)
+    buf = torch.full((T + 64, N), float("nan"), dtype=torch.float32, device=DEV)
+    got = api.la_out_projection(y.to(DEV), w.to(DEV), out=buf[32:32 + T])
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(buf[:32]).all()) and bool(torch.isnan(buf[32 + T:]).all())
+    r = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 255, 256, 511, T - 257, T - 256, T - 1],
+                                     r.integers(0, T, 200)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    check_f32(got[ri].double().cpu().numpy(), P.out_project(y, w, rows=rows))
+
+
+def test_whole_layer_projections_and_path():
+    """The layer from its input to its output on one device's heads: input
+    projection (SiLU in the epilogue), the path in its features-given mode
+    with the gate and bf16 output, then the output projection -- against the
+    oracles chained the same way (fp64 at every step, the tensors rounded to
+    bf16 where the device stores them in bf16)."""
+    T, K, H, d, N = 1500, 1024, 8, 128, 2048
+    F = H * d
+    banner("whole layer: projection, path, output projection")
+    h, w = make(T, K, F, 81)
+    _, wo = make_out(1, F, N, 82)
+    q, k, v, xg = api.la_qkvx_projection(h.to(DEV), w.to(DEV), F)
+    y, _, _ = api.la_prefill(q.view(T, H, d), k.view(T, H, d), v.view(T, H, d), xg,
+                             chunk_tokens=512, featurized=True, out_dtype=torch.bfloat16,
+                             return_state=False)
+    z = api.la_out_projection(y.view(T, F), wo.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    pq, pk, pv, px = (torch.from_numpy(a).to(torch.bfloat16) for a in P.project(h, w, F))
+    yref, _, _ = O.forward(pq.view(T, H, d), pk.view(T, H, d), pv.view(T, H, d), px,
+                           gated=True, featurized=True)
+    yref16 = torch.from_numpy(yref).to(torch.bfloat16)
+    zref = P.out_project(yref16, wo)
+    e = rel_err(z.double().cpu().numpy(), zref)
+    print("whole layer: output %.2e of rms" % e)
+    assert e <= 1e-2
