@@ -782,21 +782,21 @@ def projection_source_digest() -> str:
     return _digest(("la_device.h", "proj_api.hip", "proj_kernels.h"))
 
 
-def committed_traffic(path, digest):
-    """HBM bytes per launch from a committed counter summary (its
-    `hbm_bytes_per_launch` line), or None when the file is missing or its
-    `source_sha256` line no longer matches `digest` (the kernel changed since
-    the counters were taken)."""
+def committed_traffic(path, digest, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed counter summary (its `key`
+    line), or None when the file is missing or its `source_sha256` line no
+    longer matches `digest` (the kernel changed since the counters were
+    taken)."""
     if not os.path.exists(path):
         return None
     vals = {}
     for line in open(path):
-        if ":" in line and line.strip().startswith(("source_sha256", "hbm_bytes_per_launch")):
-            key, val = line.strip().strip("`").split(":", 1)
-            vals[key.strip()] = val.strip().strip("`")
-    if vals.get("source_sha256") != digest or "hbm_bytes_per_launch" not in vals:
+        if ":" in line and line.strip().startswith(("source_sha256", key)):
+            k, val = line.strip().strip("`").split(":", 1)
+            vals[k.strip()] = val.strip().strip("`")
+    if vals.get("source_sha256") != digest or key not in vals:
         return None
-    return float(vals["hbm_bytes_per_launch"])
+    return float(vals[key])
 
 
 def measured_traffic():
@@ -809,9 +809,11 @@ def measured_softmax_traffic():
     return committed_traffic(SOFTMAX_TRAFFIC_FILE, softmax_source_digest())
 
 
-def measured_projection_traffic():
-    """HBM bytes per launch of the projection GEMM (proj_32k)."""
-    return committed_traffic(PROJECTION_TRAFFIC_FILE, projection_source_digest())
+def measured_projection_traffic(side="in"):
+    """HBM bytes per launch of the projection GEMM at proj_32k, input side
+    ("in") or output side ("out")."""
+    key = "hbm_bytes_per_launch" if side == "in" else "hbm_bytes_per_launch_out"
+    return committed_traffic(PROJECTION_TRAFFIC_FILE, projection_source_digest(), key)
 
 
 def cpu_baseline(args, inputs, gpu_head=None):
@@ -1049,7 +1051,7 @@ def main():
                                        "proj_32k output side",
                              "achieved": proj["out_kernel"]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFS,
                              "unit": "TFLOP/s", "frac": proj["out_kernel"]["mfma_bf16_peak_frac"],
-                             "traffic": None,
+                             "traffic": measured_projection_traffic("out"),
                              "algorithmic_flops_per_launch": proj["out_kernel"]["algorithmic_flops"],
                              "avg_launch_ms": proj["out_kernel"]["kernel_ms"]},
             **proj},
