@@ -31,6 +31,12 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    return t
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -327,12 +333,17 @@ def la_qkvx_projection(hidden, weight, F, *, gate=True, featurize=True, out_dtyp
     (x_gate None without ``gate``); q, k, v carry SiLU when ``featurize``.
     ``out``: four (or three) preallocated outputs to write instead."""
     lib = _lib.load()
+    _bf16(hidden, "hidden")
+    _bf16(weight, "weight")
     T, K = hidden.shape
     nblk = 4 if gate else 3
     if weight.shape != (nblk * F, K):
         raise ValueError("weight must be [%d * F, K]" % nblk)
     if out is None:
         out = [torch.empty((T, F), dtype=out_dtype, device=hidden.device) for _ in range(nblk)]
+    if len(out) != nblk or any(o.shape != (T, F) or o.dtype != out[0].dtype for o in out):
+        raise ValueError("out must be %d tensors [T, F] of one dtype" % nblk)
+    out_dtype = out[0].dtype
     outs = list(out) + [None] * (4 - len(out))
     opt = _lib.proj_options(featurize)
     st = lib.la_qkvx_projection(_ptr(hidden), _ptr(weight), _ptr(outs[0]), _ptr(outs[1]),
@@ -350,12 +361,16 @@ def la_out_projection(y, weight, *, out_dtype=torch.bfloat16, out=None, stream=N
     Returns y @ weight^T, [T, N] ``out_dtype``: this device's partial sum of
     the layer output.  ``out``: a preallocated [T, N] output to write instead."""
     lib = _lib.load()
+    _bf16(y, "y")
+    _bf16(weight, "weight")
     T, K = y.shape
     N, Kw = weight.shape
     if Kw != K:
         raise ValueError("weight must be [N, K] with K = y's width")
     if out is None:
         out = torch.empty((T, N), dtype=out_dtype, device=y.device)
+    if out.shape != (T, N):
+        raise ValueError("out must be [T, N]")
     opt = _lib.proj_options(False)
     st = lib.la_out_projection(_ptr(y), _ptr(weight), _ptr(out), T, K, N, _dtype(out.dtype),
                                ctypes.byref(opt), _stream(stream))

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every function
-include/la.h and include/la_softmax.h declare, and rejects invalid calls on
+include/la.h, include/la_softmax.h and include/la_proj.h declare, and rejects invalid calls on
 the host.
 
 Every call below fails host validation, so none of them reaches a HIP call;
@@ -10,6 +10,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from linear_attention_long_amd import _lib
 
@@ -367,3 +368,20 @@ def test_out_projection_rejects_bad_arguments(lib):
     # more output tiles than the kernel indexes: T = 2^31 - 1 tokens, N = 2^20
     far = ctypes.c_void_p(0x7F0000000000)
     assert call(T=(1 << 31) - 1, K=64, N=1 << 20, out=far) == UNSUPPORTED
+
+def test_projection_bindings_check_operands():
+    """The Python entry points refuse operands the C ABI would misread (a
+    float32 tensor where bf16 bytes are expected) or host tensors, before any
+    call into the library."""
+    from linear_attention_long_amd import api
+
+    with pytest.raises(TypeError):
+        api.la_out_projection(torch.zeros((4, 64)), torch.zeros((256, 64), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        api.la_qkvx_projection(torch.zeros((4, 64), dtype=torch.bfloat16), torch.zeros((1024, 64)), 256)
+    with pytest.raises(ValueError):  # bf16 but on the host
+        api.la_out_projection(torch.zeros((4, 64), dtype=torch.bfloat16),
+                              torch.zeros((256, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):  # width mismatch
+        api.la_out_projection(torch.zeros((4, 64), dtype=torch.bfloat16),
+                              torch.zeros((256, 128), dtype=torch.bfloat16))
