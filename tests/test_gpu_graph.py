@@ -1,6 +1,8 @@
-"""The calls under HIP graph capture (torch.cuda.graph): decode, the fused and
-chunked prefill (cooperative launch), a packed prefill with state slots, a
-serving step and the softmax attention layer are captured once and replayed several times, with eager work
+"""The calls under HIP graph capture (torch.cuda.graph): decode (both state
+access forms), the fused and chunked prefill (cooperative launch), a packed
+prefill with state slots, a serving step, the softmax attention layer and a
+whole layer (both projections around the path) are captured once and
+replayed several times, with eager work
 and synchronisation between replays; every replay must reproduce the eager
 result bit for bit.  (No call records a memset node: buffers that must start
 at zero are cleared by kernels.)"""
@@ -45,14 +47,17 @@ def replay_and_check(g, reset, outs, refs, n=4):
         assert torch.isfinite(outs[0].float().sum() * 0.5).item()
 
 
-def test_graph_decode():
+@pytest.mark.parametrize("access", [0, 1])
+def test_graph_decode(access):
+    """Both state access forms: the default for this small state
+    (cache-resident) and the streaming form."""
     N, H, d = 8, 8, 128
     q, k, v = rnd((N, H, d), 1), rnd((N, H, d), 2), rnd((N, H, d), 3)
     S0 = rnd((N, H, d, d), 4, 0.01, torch.float32)
     S_e = S0.clone()
-    y_e = api.la_decode_step(q, k, v, S_e)
+    y_e = api.la_decode_step(q, k, v, S_e, state_access=access)
     S_g = S0.clone()
-    g, (y_g,) = capture(lambda: (api.la_decode_step(q, k, v, S_g),))
+    g, (y_g,) = capture(lambda: (api.la_decode_step(q, k, v, S_g, state_access=access),))
     replay_and_check(g, lambda: S_g.copy_(S0), [y_g, S_g], [y_e, S_e])
 
 
@@ -117,3 +122,24 @@ def test_graph_softmax_packed(precision):
     o_e, l_e = api.la_softmax_attention_varlen(q, k, v, cu, 2048, **kw)
     g, (o_g, l_g) = capture(lambda: api.la_softmax_attention_varlen(q, k, v, cu, 2048, **kw))
     replay_and_check(g, lambda: (o_g.zero_(), l_g.zero_()), [o_g, l_g], [o_e, l_e])
+
+
+def test_graph_whole_layer():
+    """Input projection, the path (features given, gated, bf16 out) and the
+    output projection captured as one graph."""
+    T, K, H, d, N = 2048, 1024, 8, 128, 2048
+    F = H * d
+    h = rnd((T, K), 11)
+    w = rnd((4 * F, K), 12, K ** -0.5)
+    wo = rnd((N, F), 13, F ** -0.5)
+
+    def layer():
+        q, k, v, xg = api.la_qkvx_projection(h, w, F)
+        y = api.la_prefill(q.view(T, H, d), k.view(T, H, d), v.view(T, H, d), xg,
+                           featurized=True, out_dtype=torch.bfloat16, return_state=False)[0]
+        return (api.la_out_projection(y.view(T, F), wo, out_dtype=torch.float32),)
+
+    (z_e,) = layer()
+    torch.cuda.synchronize()
+    g, (z_g,) = capture(layer)
+    replay_and_check(g, lambda: z_g.zero_(), [z_g], [z_e])
