@@ -194,3 +194,26 @@ def test_fp32_prefill_writes_exactly_its_outputs():
     _lib.check(st, "la_prefill")
     out.check("out")
     so.check("state_out")
+
+
+@pytest.mark.parametrize("T,odt,gate", [(1, torch.bfloat16, True), (257, torch.float32, True),
+                                        (300, torch.bfloat16, False)])
+def test_input_projection_writes_exactly_its_outputs(T, odt, gate):
+    K, F = 320, 512
+    h = rnd((T, K), 40)
+    nblk = 4 if gate else 3
+    w = rnd((nblk * F, K), 41, K ** -0.5)
+    outs = [Fenced((T, F), odt) for _ in range(nblk)]
+    api.la_qkvx_projection(h, w, F, gate=gate, out=[o.t for o in outs])
+    for name, o in zip("qkvx", outs):
+        o.check(name)
+
+
+@pytest.mark.parametrize("T,odt", [(1, torch.float32), (255, torch.bfloat16), (513, torch.float32)])
+def test_output_projection_writes_exactly_its_output(T, odt):
+    K, N = 192, 768
+    y = rnd((T, K), 42)
+    w = rnd((N, K), 43, K ** -0.5)
+    out = Fenced((T, N), odt)
+    api.la_out_projection(y, w, out=out.t)
+    out.check("out")
