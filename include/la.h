@@ -75,11 +75,16 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               size gives the same result; it changes fp32 rounding order
  *               only.  0 = library default: 32 for bf16 inputs with d = 128
  *               (matrix-core path), 64 otherwise.  The bf16 d=128
- *               matrix-core path implements 32 and 64; the fp32 path
- *               implements 32, 64, 128 and 256.  Other values:
+ *               matrix-core path implements 32 and 64; the vector path
+ *               (any input dtype) implements 32, 64, 128 and 256, as whole
+ *               blocks, and serves bf16 requests for 128 or 256: the
+ *               pages' 256-token blocking exactly, but 20-30x slower than
+ *               the default at d = 128 (the state update moves from the
+ *               matrix cores to the vector ALUs).  Other values:
  *               LA_ERR_UNSUPPORTED.  Partial tail blocks are zero-padded to
- *               the next of 32 or 64 rows (SiLU(0) = 0, so the pad adds
- *               nothing).
+ *               the next of 32 or 64 rows on the matrix-core path, and to
+ *               32-row sub-tiles on the vector path (SiLU(0) = 0, so the pad
+ *               adds nothing).
  *   normalized  0: y = phi(q)^T S.  1: y = phi(q)^T S / phi(q)^T z.
  *   gated       0: out = y.  1: out = RMSNorm(y) * w * sigmoid(x).
  *   norm_group  RMSNorm width in features: 0 = H*d (whole token), or any
