@@ -79,8 +79,8 @@ typedef enum { LA_DTYPE_F32 = 0, LA_DTYPE_BF16 = 1 } la_dtype_t;
  *               (any input dtype) implements 32, 64, 128 and 256, as whole
  *               blocks, and serves bf16 requests for 128 or 256: the
  *               pages' 256-token blocking exactly, but 20-30x slower than
- *               the default at d = 128 (the state update moves from the
- *               matrix cores to the vector ALUs).  Other values:
+ *               the default at d = 128 (every product runs on the vector
+ *               ALUs there).  Other values:
  *               LA_ERR_UNSUPPORTED.  Partial tail blocks are zero-padded to
  *               the next of 32 or 64 rows on the matrix-core path, and to
  *               32-row sub-tiles on the vector path (SiLU(0) = 0, so the pad
