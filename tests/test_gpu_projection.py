@@ -220,3 +220,24 @@ def test_whole_layer_projections_and_path():
     e = rel_err(z.double().cpu().numpy(), zref)
     print("whole layer: output %.2e of rms" % e)
     assert e <= 1e-2
+
+
+def test_out_projection_1m_workload_sampled():
+    """The bench's 1M-token output side (y [1048576, 1024] and W_o [6144,
+    1024] drawn on the GPU as the bench draws them), bf16 output: sampled
+    rows, including the first and last tokens and tile edges."""
+    from linear_attention_long_amd import inputs
+
+    w = inputs.WORKLOADS["proj_1m"]
+    banner("out projection 1M sampled")
+    y, wo = inputs.out_projection_inputs(w, device=DEV)
+    T = y.shape[0]
+    z = api.la_out_projection(y, wo)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, T // 2, T - 257, T - 256, T - 1],
+                                     r.integers(0, T, 120)]))
+    ri = torch.from_numpy(rows).to(DEV)
+    check_bf16(z[ri].double().cpu().numpy(), P.out_project(y[ri].cpu(), wo.cpu()))
+    del y, z
+    torch.cuda.empty_cache()
