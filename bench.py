@@ -471,13 +471,22 @@ def bench_serving(args, torch, api, inputs, reps=50):
     return res
 
 
-# (workload, timed calls, precision option: 0 single bf16 operands, 1 split)
-# (workload, timed calls, precision): 1 = split operands (the library's
-# default, within 1e-2 of the output's rms), 0 = single bf16 operands
+# (workload, timed calls, precision): 1 = split operands in both products
+# (the library's default, within 1e-2 of the output's rms for any bf16
+# input), 2 = fp16 scores with split probabilities, 0 = single bf16 operands
 SOFTMAX_WORKLOADS = (("softmax_32k", 10, 1), ("softmax_varlen_512k", 3, 1), ("softmax_1m", 1, 1),
+                     ("softmax_32k", 10, 2), ("softmax_varlen_512k", 3, 2),
                      ("softmax_32k", 20, 0), ("softmax_varlen_512k", 5, 0))
-SINGLE_NOTE = ("single bf16 operands: about 1e-3 of the values' scale, which on long rows exceeds "
-               "the 1e-2-of-output-rms bound for bf16 inputs (not the library default)")
+SOFTMAX_KEY = {1: "", 2: "_fp16_scores", 0: "_single"}
+SOFTMAX_NOTE = {
+    1: ("split bf16 hi+lo operands in both products (default; within 1e-2 of the output's rms "
+        "for any bf16 input)"),
+    2: ("fp16 scores (q, k times 2^-6 rounded to fp16), split bf16 hi+lo probabilities: about "
+        "2e-3 of the output's rms for unit-spread scores, growing with the spread (not the "
+        "library default)"),
+    0: ("single bf16 operands: about 1e-3 of the values' scale, which on long rows exceeds "
+        "the 1e-2-of-output-rms bound for bf16 inputs (not the library default)"),
+}
 
 
 def softmax_flops(cu):
@@ -495,7 +504,7 @@ def bench_softmax(args, torch, lib, _lib, inputs):
     for name, reps, prec in SOFTMAX_WORKLOADS:
         if name == "softmax_1m" and args.no_softmax_1m:
             continue
-        key = name + ("" if prec else "_single")
+        key = name + SOFTMAX_KEY[prec]
         w = inputs.WORKLOADS[name]
         q, k, v, cu = inputs.softmax_inputs(w, device="cuda")
         cud = cu.cuda()
@@ -540,8 +549,7 @@ def bench_softmax(args, torch, lib, _lib, inputs):
         att = per["attention"]
         res[key] = {"tokens": T, "sequences": nseq, "max_seqlen": maxlen, "H": H, "Hkv": Hkv,
                     "d": d, "rotary_dim": w.extra["rotary_dim"], "rope_base": w.extra["rope_base"],
-                    "precision": ("split bf16 hi+lo operands (default; within 1e-2 of the "
-                                  "output's rms)") if prec else SINGLE_NOTE,
+                    "precision": SOFTMAX_NOTE[prec],
                     "ms_per_call": ms, "per_kernel_ms": per, "algorithmic_flops": flops,
                     "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
                     "call_TFLOPs": flops / (ms * 1e-3) / 1e12,
@@ -805,7 +813,7 @@ def measured_traffic():
 
 
 def measured_softmax_traffic():
-    """HBM bytes per launch of the softmax attention kernel (32K, split operands)."""
+    """HBM bytes per launch of the softmax attention kernel (32K, default mode)."""
     return committed_traffic(SOFTMAX_TRAFFIC_FILE, softmax_source_digest())
 
 

@@ -27,15 +27,21 @@
  * by a fixed permutation of q's and k's features and gives the same scores
  * when both are permuted.)
  *
- * Precision (default mode): the rotated, scaled q and the rotated k are
- * rounded to bf16 once, the scores and the softmax are fp32, the
- * probabilities are rounded to bf16 for the product with V (the same rounded
- * weights give the denominator), accumulation is fp32.  Against fp64 the
- * output error is a few 1e-3 of the values' rms for scores of unit spread
- * (it grows with the spread of the scores); since a row's output shrinks as
- * its keys grow, that is far more than 1e-2 of the output's own rms for long
- * sequences.  The split mode (options.precision = 1) keeps ~16 significant
- * bits in both products and meets 1e-2 of the output's rms.
+ * Precision.  Scores, the softmax and every accumulation are fp32 in all
+ * modes; they differ in how the two products' operands are rounded.
+ * Default, the split mode (options.precision = 1): the rotated q and k and
+ * the probabilities are each carried as bf16 hi + lo (~16 significant bits);
+ * against fp64 the output errs by about 1e-4 of its own rms for any bf16
+ * input, within the 1e-2-of-rms bound for bf16 inputs with fp32
+ * accumulation.  fp16 scores (2): the rotated q and k rounded to fp16 (11
+ * bits), one product per score, the probabilities split as in 1; about 2e-3
+ * of the output's rms for scores of unit spread, growing with the spread
+ * (the score errors scale with the scores: 5e-3 to 7e-3 at spreads of 2 to
+ * 4 on 2K-token rows), so within the bound only where the spread is known
+ * to be small.  Single mode (0): bf16 q, k and probabilities, the usual
+ * attention kernel; a few 1e-3 of the values' rms for scores of unit
+ * spread, growing with the spread, and since a row's output shrinks as its
+ * keys grow, far more than 1e-2 of the output's own rms on long sequences.
  *
  * Conventions as in la.h: device pointers to contiguous row-major data
  * (q, k, v, out 16-byte aligned, lse 4-byte aligned); the caller owns every
@@ -69,15 +75,22 @@ extern "C" {
  *               hip_stream, i < n_timing.  Kernels in launch order: [plan]
  *               (only when num_seqs > 1), rotate, attention.
  *   precision   1 (default): split operands -- q, k and the probabilities
- *               each carried as bf16 hi + lo, three products for the scores
- *               and two for P V -- about 1e-4 of the output's rms, within
- *               the 1e-2-of-rms bound for bf16 inputs with fp32
- *               accumulation.  0: single bf16 operands for both products
- *               (the usual attention kernel, 2.5x fewer matrix-core
- *               instructions; error against fp64 about 1e-3 of the values'
- *               scale, which on long rows is more than 1e-2 of the output's
- *               own rms, see "Precision" above).  Other values:
- *               LA_ERR_INVALID_ARGUMENT.                                    */
+ *               each as bf16 hi + lo, three products per score on the
+ *               rotated dimensions (one elsewhere, where bf16 inputs are
+ *               exact) and two for P V; about 1e-4 of the output's rms for
+ *               any bf16 input.  2: fp16 scores -- the rotated q and k, each
+ *               taken times 2^-6 (exact; the scores are scaled back by
+ *               2^12), rounded to fp16, one product per score; the
+ *               probabilities split as in 1.  0.79x the time of 1; error
+ *               as in "Precision" above.  fp16's normal range then covers
+ *               rotated elements of magnitude 2^-8 to 2^22; smaller ones
+ *               keep an absolute error below 2^-19, and one of 4.19e6 or
+ *               more overflows and makes the outputs of its rows
+ *               non-finite.  0: single bf16 operands for both products
+ *               (the usual attention kernel, the fastest; error against
+ *               fp64 about 1e-3 of the values' scale, on long rows more
+ *               than 1e-2 of the output's own rms, see "Precision" above).
+ *               Other values: LA_ERR_INVALID_ARGUMENT.                      */
 typedef struct {
     int32_t rotary_dim;
     double rope_base;

@@ -38,11 +38,14 @@ inline bool dtype_arg_ok(const la_dtype_t& t) {
 // two waves per SIMD with 8.
 constexpr int kWavesPlain = LA_SM_WAVES;
 constexpr int kWavesSplit = LA_SM_WAVES_SPLIT;
+// fp16 scores: q and k are rounded to fp16 times this power of two
+constexpr float kF16Pre = 0.015625f;  // 2^-6
 inline int tile_queries(bool split) { return 32 * (split ? kWavesSplit : kWavesPlain); }
 
 struct SmOpts {
     int rot;
-    bool split;
+    bool split;    // probabilities split (precision 1 and 2)
+    bool f16s;     // scores from fp16 q and k (precision 2): no q/k remainders
     double base;
     float scale;
     hipEvent_t* events;
@@ -82,8 +85,9 @@ la_status_t sm_parse(const la_softmax_options_t* opt, int d, SmOpts& o) {
     if (x.n_timing < 0 || (x.n_timing > 0 && !x.timing_events)) return LA_ERR_INVALID_ARGUMENT;
     o.events = (hipEvent_t*)x.timing_events;
     o.n_events = x.timing_events ? x.n_timing : 0;
-    if (x.precision != 0 && x.precision != 1) return LA_ERR_INVALID_ARGUMENT;
-    o.split = x.precision == 1;
+    if (x.precision < 0 || x.precision > 2) return LA_ERR_INVALID_ARGUMENT;
+    o.split = x.precision >= 1;
+    o.f16s = x.precision == 2;
     return LA_OK;
 }
 
@@ -102,7 +106,7 @@ la_status_t sm_check(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int3
 }
 
 la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
-                      int32_t H_kv, bool split, SmLayout& p) {
+                      int32_t H_kv, bool split, bool remainders, SmLayout& p) {
     const int BQ = tile_queries(split);
     p.bq = BQ;
     p.ntmax = (max_seqlen + BQ - 1) / BQ;
@@ -117,7 +121,7 @@ la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int
     p.off_kr = o;
     o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
     p.off_qrl = p.off_krl = o;
-    if (split) {  // bf16 remainders of the rotated q and k
+    if (remainders) {  // bf16 remainders of the rotated q and k (precision 1)
         p.off_qrl = o;
         o = a256(o + (size_t)total_T * H * sm::D * 2);
         p.off_krl = o;
@@ -180,7 +184,7 @@ size_t la_softmax_workspace_bytes(int32_t num_seqs, int32_t total_T, int32_t max
     SmOpts o;
     if (sm_parse(opt, d, o) != LA_OK) return (size_t)-1;
     SmLayout p;
-    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, p) != LA_OK) return (size_t)-1;
+    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.split && !o.f16s, p) != LA_OK) return (size_t)-1;
     return p.total;
 }
 
@@ -202,7 +206,7 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         !is_aligned(cu_seqlens, 4) || (lse && !is_aligned(lse, 4)))
         return LA_ERR_INVALID_ARGUMENT;
     SmLayout p;
-    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, p)) != LA_OK) return st;
+    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.split && !o.f16s, p)) != LA_OK) return st;
     const size_t nq = (size_t)total_T * H * d * 2, nkv = (size_t)total_T * H_kv * d * 2;
     const size_t nout = (size_t)total_T * H * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
     const size_t nlse = lse ? (size_t)total_T * H * 4 : 0;
@@ -227,8 +231,9 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     char* ws = (char*)workspace;
     uint16_t* qr = (uint16_t*)(ws + p.off_qr);
     uint16_t* kr = (uint16_t*)(ws + p.off_kr);
-    uint16_t* qrl = o.split ? (uint16_t*)(ws + p.off_qrl) : nullptr;
-    uint16_t* krl = o.split ? (uint16_t*)(ws + p.off_krl) : nullptr;
+    const bool rem = o.split && !o.f16s;
+    uint16_t* qrl = rem ? (uint16_t*)(ws + p.off_qrl) : nullptr;
+    uint16_t* krl = rem ? (uint16_t*)(ws + p.off_krl) : nullptr;
     const int2* table = nullptr;
     const int32_t* count = nullptr;
     if (p.planned) {
@@ -248,39 +253,48 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         const int64_t want = ((int64_t)total_T + 15) / 16;
         const int grid = (int)(want < 16384 ? want : 16384);
         // scores in log2 units: q carries scale * log2(e), except with split
-        // operands, where the attention kernel scales the fp32 scores (q then
-        // stays exact in bf16 outside the rotated dimensions)
-        const float qscale = o.split ? 1.0f : o.scale * 1.4426950408889634f;
+        // probabilities, where the attention kernel scales the fp32 scores (q
+        // then stays exact outside the rotated dimensions).  fp16 q and k are
+        // both taken times 2^-6 (exact), which moves fp16's normal range to
+        // rotated elements in [2^-8, 2^22); the attention kernel multiplies
+        // the scores back by 2^12.
+        const float qscale = o.f16s ? kF16Pre : o.split ? 1.0f : o.scale * 1.4426950408889634f;
+        const float kscale = o.f16s ? kF16Pre : 1.0f;
         tm.before();
         sm::k_sm_rope<<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, cu_seqlens,
                                                 num_seqs, total_T, H, H_kv, o.rot,
-                                                o.rot > 0 ? std::log2(o.base) : 0.0, qscale, qr, kr,
-                                                qrl, krl);
+                                                o.rot > 0 ? std::log2(o.base) : 0.0, qscale, kscale,
+                                                qr, kr,
+                                                qrl, krl, o.f16s ? 1 : 0);
         tm.after();
     }
     const unsigned grid = (unsigned)(p.emax * H);
     tm.before();
     if (grid > 0) {
-        const float qs = o.scale * 1.4426950408889634f;
+        const float qs = o.scale * 1.4426950408889634f * (o.f16s ? 1.0f / (kF16Pre * kF16Pre) : 1.0f);
         const int nrk = (o.rot + 31) / 32;  // 32-dimension steps holding rotated dimensions
-#define SM_ATTN(OT, SP, W, NRK)                                                                     \
-    sm::k_sm_attn<OT, SP, W, NRK><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
+#define SM_ATTN(OT, SP, W, NRK, F16)                                                                \
+    sm::k_sm_attn<OT, SP, W, NRK, F16><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
                                                                cu_seqlens, table, count, H, H_kv,   \
                                                                (OT*)out, lse, qs)
-#define SM_ATTN_SPLIT(OT)                                        \
-    switch (nrk) {                                               \
-        case 0: SM_ATTN(OT, true, kWavesSplit, 0); break;        \
-        case 1: SM_ATTN(OT, true, kWavesSplit, 1); break;        \
-        case 2: SM_ATTN(OT, true, kWavesSplit, 2); break;        \
-        case 3: SM_ATTN(OT, true, kWavesSplit, 3); break;        \
-        default: SM_ATTN(OT, true, kWavesSplit, 4); break;       \
+#define SM_ATTN_SPLIT(OT)                                               \
+    if (o.f16s) {                                                       \
+        SM_ATTN(OT, true, kWavesSplit, 0, true);                        \
+    } else {                                                            \
+        switch (nrk) {                                                  \
+            case 0: SM_ATTN(OT, true, kWavesSplit, 0, false); break;    \
+            case 1: SM_ATTN(OT, true, kWavesSplit, 1, false); break;    \
+            case 2: SM_ATTN(OT, true, kWavesSplit, 2, false); break;    \
+            case 3: SM_ATTN(OT, true, kWavesSplit, 3, false); break;    \
+            default: SM_ATTN(OT, true, kWavesSplit, 4, false); break;   \
+        }                                                               \
     }
         if (out_dtype == LA_DTYPE_BF16) {
-            if (o.split) SM_ATTN_SPLIT(uint16_t)
-            else SM_ATTN(uint16_t, false, kWavesPlain, 4);
+            if (o.split) { SM_ATTN_SPLIT(uint16_t) }
+            else SM_ATTN(uint16_t, false, kWavesPlain, 4, false);
         } else {
-            if (o.split) SM_ATTN_SPLIT(float)
-            else SM_ATTN(float, false, kWavesPlain, 4);
+            if (o.split) { SM_ATTN_SPLIT(float) }
+            else SM_ATTN(float, false, kWavesPlain, 4, false);
         }
 #undef SM_ATTN_SPLIT
 #undef SM_ATTN

@@ -15,9 +15,10 @@
 //  * k_sm_plan (packed batches of more than one sequence): one workgroup
 //    orders the (sequence, query tile) pairs by decreasing tile index, i.e.
 //    by decreasing causal work, so the longest tiles start first;
-//  * k_sm_rope: q and k are rotated once (angles reduced in fp64), q is also
-//    multiplied by scale * log2(e), and both are rounded to bf16 into the
-//    workspace; every workgroup of the main kernel then reads ready operands;
+//  * k_sm_rope: q and k are rotated once (angles reduced in fp64), scaled,
+//    and rounded into the workspace (bf16, bf16 hi + lo, or fp16, by
+//    precision mode); every workgroup of the main kernel then reads ready
+//    operands;
 //  * k_sm_attn: one workgroup = one (query tile, head); streaming softmax
 //    over blocks of 128 keys (64 with split operands).
 //
@@ -25,7 +26,9 @@
 //  * W waves x 32 queries: 8 waves (256-query tiles, one workgroup per CU)
 //    with single bf16 operands, 4 waves (128-query tiles) with split
 //    operands, whose registers allow only one 4-wave workgroup per CU; either
-//    way two waves share a SIMD.  Each staged K/V block serves all W waves.
+//    way two waves share a SIMD (fp16 scores use the split layout with one
+//    score product, v_mfma_f32_16x16x32_f16, instead of three).  Each staged
+//    K/V block serves all W waves.
 //    A wave's rotated Q stays in registers as MFMA operands for the whole
 //    key loop;
 //  * the score tile is produced transposed, S^T = K Q^T
@@ -54,7 +57,7 @@
 //  * the matrix-core sections run at raised wave priority (s_setprio 1), so a
 //    SIMD issues one wave's MFMA stream first and fills its gaps with the
 //    other wave's vector work;
-//  * 138 KB of LDS per workgroup (104.5 KB with split operands); the blockIdx -> (tile, head)
+//  * 138 KB of LDS per workgroup (104.5 KB with split operands, 69 KB with fp16 scores); the blockIdx -> (tile, head)
 //    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
 //    head's K and V share that XCD's L2.
 #pragma once
@@ -63,6 +66,8 @@
 
 namespace la {
 namespace sm {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int D = 128;    // head dim
 // The attention kernel runs W waves of 32 queries each per workgroup: 64 W
@@ -194,7 +199,14 @@ __global__ __launch_bounds__(1024) void k_sm_plan(const int32_t* __restrict__ cu
 
 // ------------------------------------------------------------------ rope --
 
-// Rotary embedding, scale and bf16 rounding of q and k.  16 threads per token
+// Two floats as an fp16 pair (round to nearest even), first in the low half.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// Rotary embedding, scale and bf16 (or, for fp16 scores, fp16) rounding of q
+// and k; q is multiplied by qscale and k by kscale before the rounding.  16 threads per token
 // (thread u owns 8 dimensions), grid-stride over tokens; for each token the
 // rotations are computed once and applied to its H query heads and Hkv key
 // heads.  Thread u < rot/16 rotates dimensions [8u, 8u+8) with their partners
@@ -206,10 +218,11 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const int32_t* __restrict__ cu, int nseq, int T,
                                                  int H, int Hkv, int rot, double log2_base,
-                                                 float qscale, uint16_t* __restrict__ qr,
+                                                 float qscale, float kscale,
+                                                 uint16_t* __restrict__ qr,
                                                  uint16_t* __restrict__ kr,
                                                  uint16_t* __restrict__ qrl,
-                                                 uint16_t* __restrict__ krl) {
+                                                 uint16_t* __restrict__ krl, int f16out) {
     __shared__ double theta[64];
     if ((int)threadIdx.x < rot / 2)
         theta[threadIdx.x] = exp2(-(2.0 * (double)threadIdx.x / (double)rot) * log2_base);
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
             uint16_t* dst = (isq ? qr : kr) + base;
             uint16_t* dlo = isq ? qrl : krl;  // bf16 remainders, or none
             if (dlo) dlo += base;
-            const float sc = isq ? qscale : 1.0f;
+            const float sc = isq ? qscale : kscale;
             if (pair) {
                 const uint4 wa = *(const uint4*)(src + 8 * u);
                 const uint4 wb = *(const uint4*)(src + 8 * u + half);
@@ -255,8 +268,15 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                     const float a0 = bf16_lo_to_f32(a32[p]), a1 = bf16_hi_to_f32(a32[p]);
                     const float b0 = bf16_lo_to_f32(b32[p]), b1 = bf16_hi_to_f32(b32[p]);
                     const float c0 = cs[2 * p], s0 = sn[2 * p], c1 = cs[2 * p + 1], s1 = sn[2 * p + 1];
-                    split2_keep((a0 * c0 - b0 * s0) * sc, (a1 * c1 - b1 * s1) * sc, oa[p], la[p]);
-                    split2_keep((b0 * c0 + a0 * s0) * sc, (b1 * c1 + a1 * s1) * sc, ob[p], lb[p]);
+                    const float ra0 = (a0 * c0 - b0 * s0) * sc, ra1 = (a1 * c1 - b1 * s1) * sc;
+                    const float rb0 = (b0 * c0 + a0 * s0) * sc, rb1 = (b1 * c1 + a1 * s1) * sc;
+                    if (f16out) {
+                        oa[p] = pack_f16x2(ra0, ra1);
+                        ob[p] = pack_f16x2(rb0, rb1);
+                    } else {
+                        split2_keep(ra0, ra1, oa[p], la[p]);
+                        split2_keep(rb0, rb1, ob[p], lb[p]);
+                    }
                 }
                 *(uint4*)(dst + 8 * u) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
                 *(uint4*)(dst + 8 * u + half) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
@@ -269,8 +289,12 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                 const uint32_t w32[4] = {w.x, w.y, w.z, w.w};
                 uint32_t o[4], lo[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    split2_keep(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc, o[p], lo[p]);
+                for (int p = 0; p < 4; ++p) {
+                    if (f16out)
+                        o[p] = pack_f16x2(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc);
+                    else
+                        split2_keep(bf16_lo_to_f32(w32[p]) * sc, bf16_hi_to_f32(w32[p]) * sc, o[p], lo[p]);
+                }
                 *(uint4*)(dst + 8 * u) = make_uint4(o[0], o[1], o[2], o[3]);
                 if (dlo) *(uint4*)(dlo + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             }
@@ -319,7 +343,10 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
 // (hi.hi + lo.hi + hi.lo); the probabilities are split into bf16 hi + lo for
 // two products with V (V is exact).  Both contractions keep ~16 significant
 // bits.  Without SPLIT, q carries the scale and NRK is unused.
-template <typename OutT, bool SPLIT, int W, int NRK = 4>
+// F16S (with SPLIT, NRK = 0): qr and kr hold fp16 (the rotated q and k times
+// 2^-6 each), one fp16 product per score, qs then also carries 2^12; the
+// probabilities are split as above.
+template <typename OutT, bool SPLIT, int W, int NRK = 4, bool F16S = false>
 __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
                                                    const uint16_t* __restrict__ qrl,
@@ -331,10 +358,12 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                                                    int Hkv, OutT* __restrict__ out,
                                                    float* __restrict__ lse, float qs) {
     static_assert(NRK >= 0 && NRK <= 4, "rotated 32-dimension steps");
+    static_assert(!F16S || (SPLIT && NRK == 0), "fp16 scores: split probabilities, no q/k remainders");
+    constexpr bool KLO = SPLIT && NRK > 0;  // bf16 remainders of k staged and used
     constexpr int BN = SPLIT ? kBlockSplit : kBlockPlain;  // keys per K/V block
     constexpr int NKT = BN / 16;  // 16-key score tiles per block
     constexpr int NKS = BN / 32;  // 32-key steps of the P V product
-    __shared__ Smem<SPLIT, BN> sm;
+    __shared__ Smem<KLO, BN> sm;
     constexpr int BQ = Waves<W>::BQ, RP = Waves<W>::RP, NJ = BN / RP;
     const int G = H / Hkv;
     const int b = blockIdx.x;
@@ -421,9 +450,9 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
     const uint32_t rs = (uint32_t)(Hkv * D);
     const uint16_t* kseq = kr + ((size_t)start * Hkv + hk) * D;
     const uint16_t* vseq = v + ((size_t)start * Hkv + hk) * D;
-    const uint16_t* klseq = SPLIT ? krl + ((size_t)start * Hkv + hk) * D : nullptr;
+    const uint16_t* klseq = KLO ? krl + ((size_t)start * Hkv + hk) * D : nullptr;
     const uint32_t voff = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
-    uint4 rk[NJ], rv[NJ], rkl[SPLIT ? NJ : 1];
+    uint4 rk[NJ], rv[NJ], rkl[KLO ? NJ : 1];
     auto load_kv = [&](int blk) {
         const int nvalid = kv_end - blk * BN;
         const int32_t bytes = (int32_t)((uint32_t)(min(nvalid, BN) - 1) * rs * 2u + 2u * D);
@@ -439,7 +468,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             rv[j] = __builtin_bit_cast(
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
         }
-        if constexpr (SPLIT) {
+        if constexpr (KLO) {
             const __amdgpu_buffer_rsrc_t rskl =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(klseq + base), (short)0, bytes, 0x00020000);
 #pragma unroll
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             pk[0] = make_uint2(rk[j].x, rk[j].y);
             pk[1] = make_uint2(rk[j].z, rk[j].w);
             *(uint4*)(sm.v[buf] + r * KSV + (tid & 15) * 8) = rv[j];
-            if constexpr (SPLIT) {
+            if constexpr (KLO) {
                 uint2* pl = (uint2*)(sm.kl[buf] + r * KSK + (tid & 15) * 8);
                 pl[0] = make_uint2(rkl[j].x, rkl[j].y);
                 pl[1] = make_uint2(rkl[j].z, rkl[j].w);
@@ -483,10 +512,15 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                 for (int kt = 0; kt < NKT; ++kt) {
                     const bf16x8_t A = k_operand(kt_, 16 * kt + c, 32 * kk, g);
 #pragma unroll
-                    for (int qt = 0; qt < 2; ++qt)
-                        Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk],
-                                                  kk == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Sc[kt][qt]);
-                    if constexpr (SPLIT) {  // rotated steps: + k_lo . q_hi + k_hi . q_lo
+                    for (int qt = 0; qt < 2; ++qt) {
+                        const f32x4_t c0 = kk == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Sc[kt][qt];
+                        if constexpr (F16S)  // q and k held as fp16 (the same 16-bit lanes)
+                            Sc[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8_t, A), __builtin_bit_cast(f16x8_t, Qf[qt][kk]), c0, 0, 0, 0);
+                        else
+                            Sc[kt][qt] = mfma16x16x32(A, Qf[qt][kk], c0);
+                    }
+                    if constexpr (KLO) {  // rotated steps: + k_lo . q_hi + k_hi . q_lo
                         if (kk < NRK) {
                             const bf16x8_t Al = k_operand(sm.kl[buf], 16 * kt + c, 32 * kk, g);
 #pragma unroll

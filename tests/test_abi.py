@@ -246,7 +246,7 @@ def test_decode_rejects_bad_arguments(lib):
 def test_softmax_default_options(lib):
     o = lib.la_softmax_default_options()
     assert (o.rotary_dim, o.rope_base, o.scale, o.n_timing) == (-1, 10000.0, 0.0, 0)
-    assert o.precision == 1  # split operands: the mode within 1e-2 of the output's rms
+    assert o.precision == 1  # split operands: within 1e-2 of the output's rms for any bf16 input
 
 
 def test_softmax_workspace_bytes(lib):
@@ -266,6 +266,10 @@ def test_softmax_workspace_bytes(lib):
     osp = _lib.softmax_options(precision=1)
     assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
                                           ctypes.byref(osp)) == 2 * (1000 * 4 * 256 + 1000 * 2 * 256)
+    # fp16 scores: the rotated q and k in fp16, no remainders (as single operands)
+    o16 = _lib.softmax_options(precision=2)
+    assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
+                                          ctypes.byref(o16)) == 1000 * 4 * 256 + 1000 * 2 * 256
     # the base is not used (nor checked) without rotation
     o0 = _lib.softmax_options(rotary_dim=0, rope_base=0.0)
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o0)) > 0
@@ -300,7 +304,8 @@ def test_softmax_rejects_bad_arguments(lib):
     assert call(rope_base=0.0) == INVALID
     assert call(rope_base=float("inf")) == INVALID
     assert call(scale=-1.0) == INVALID
-    assert call(precision=2) == INVALID
+    assert call(precision=3) == INVALID
+    assert call(precision=-1) == INVALID
     assert call(out=A[0]) == INVALID                               # out overlaps q
     assert call(lse=ctypes.c_void_p(A[3].value + 64)) == INVALID   # lse overlaps out
     assert call(ws=None) == INVALID

@@ -110,7 +110,7 @@ def test_graph_varlen_with_slots_and_serving_step():
     replay_and_check(g, lambda: pool_g.copy_(pool0), [out_g, pool_g], [out_e, pool_e])
 
 
-@pytest.mark.parametrize("precision", [0, 1])
+@pytest.mark.parametrize("precision", [0, 1, 2])
 def test_graph_softmax_packed(precision):
     # the softmax layer on a packed batch: ordering pass (atomics), rotation and
     # attention kernels captured together

@@ -156,7 +156,7 @@ def test_decode_writes_exactly_its_outputs(gated, odt):
 
 
 @pytest.mark.parametrize("precision,odt", [(0, torch.bfloat16), (0, torch.float32),
-                                           (1, torch.float32)])
+                                           (1, torch.float32), (2, torch.bfloat16)])
 def test_softmax_writes_exactly_its_outputs(precision, odt):
     lib = _lib.load()
     H, Hkv, d = 4, 2, 128
