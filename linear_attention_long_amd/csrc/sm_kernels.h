@@ -452,6 +452,9 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
     const uint16_t* vseq = v + ((size_t)start * Hkv + hk) * D;
     const uint16_t* klseq = KLO ? krl + ((size_t)start * Hkv + hk) * D : nullptr;
     const uint32_t voff = ((uint32_t)(tid >> 4) * rs + (uint32_t)(tid & 15) * 8) * 2u;
+    // the remainders of k are zero past the rotated dimensions: only the
+    // threads whose 8 dimensions lie in the first 32 NRK move them
+    const bool klo_thread = KLO && (tid & 15) < 4 * NRK;
     uint4 rk[NJ], rv[NJ], rkl[KLO ? NJ : 1];
     auto load_kv = [&](int blk) {
         const int nvalid = kv_end - blk * BN;
@@ -469,12 +472,14 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                 uint4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
         }
         if constexpr (KLO) {
-            const __amdgpu_buffer_rsrc_t rskl =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(klseq + base), (short)0, bytes, 0x00020000);
+            if (klo_thread) {
+                const __amdgpu_buffer_rsrc_t rskl =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)(klseq + base), (short)0, bytes, 0x00020000);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                rkl[j] = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rskl, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
+                for (int j = 0; j < NJ; ++j)
+                    rkl[j] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(rskl, voff + (uint32_t)(RP * j) * rs * 2u, 0, 0));
+            }
         }
     };
     auto store_kv = [&](int buf) {
@@ -486,9 +491,11 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
             pk[1] = make_uint2(rk[j].z, rk[j].w);
             *(uint4*)(sm.v[buf] + r * KSV + (tid & 15) * 8) = rv[j];
             if constexpr (KLO) {
-                uint2* pl = (uint2*)(sm.kl[buf] + r * KSK + (tid & 15) * 8);
-                pl[0] = make_uint2(rkl[j].x, rkl[j].y);
-                pl[1] = make_uint2(rkl[j].z, rkl[j].w);
+                if (klo_thread) {
+                    uint2* pl = (uint2*)(sm.kl[buf] + r * KSK + (tid & 15) * 8);
+                    pl[0] = make_uint2(rkl[j].x, rkl[j].y);
+                    pl[1] = make_uint2(rkl[j].z, rkl[j].w);
+                }
             }
         }
     };
@@ -532,12 +539,10 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                     }
                 }
             __builtin_amdgcn_s_setprio(0);
-            if constexpr (SPLIT) {  // scores in log2 units
-#pragma unroll
-                for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-                    for (int qt = 0; qt < 2; ++qt) Sc[kt][qt] *= qs;
-            }
+            // scores in log2 units are Sc * sc: with split operands the
+            // unscaled products (sc = qs > 0, applied below inside the
+            // exponent's argument and to the block maximum), else q carries it
+            const float sc = SPLIT ? qs : 1.0f;
             if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
 #pragma unroll
                     for (int i = 0; i < 4; ++i) x = fmaxf(x, Sc[kt][qt][i]);
                 x = fmaxf(x, __shfl_xor(x, 16, 64));
-                mx[qt] = fmaxf(x, __shfl_xor(x, 32, 64));
+                mx[qt] = fmaxf(x, __shfl_xor(x, 32, 64)) * sc;
                 raise |= mx[qt] > m[qt] + kLazy;
             }
             if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                 for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        Sc[kt][qt][i] = __builtin_amdgcn_exp2f(Sc[kt][qt][i] - m[qt]);
+                        Sc[kt][qt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sc[kt][qt][i], sc, -m[qt]));
             // P^T operands: keys {32 ks + 4g + i} from tile 2ks, {32 ks + 16 + 4g + i}
             // from tile 2ks + 1.
             bf16x8_t Pf[NKS][2], Pl[SPLIT ? NKS : 1][2];
