@@ -85,8 +85,10 @@ extern "C" {
  *               as in "Precision" above.  fp16's normal range then covers
  *               rotated elements of magnitude 2^-8 to 2^22; smaller ones
  *               keep an absolute error below 2^-19, and one of 4.19e6 or
- *               more overflows and makes the outputs of its rows
- *               non-finite.  0: single bf16 operands for both products
+ *               more (or an infinite input) is stored as NaN, so every
+ *               output whose scores it enters is NaN: its query's row, or
+ *               for a key, the rows of the sequence from that key on.
+ *               0: single bf16 operands for both products
  *               (the usual attention kernel, the fastest; error against
  *               fp64 about 1e-3 of the values' scale, on long rows more
  *               than 1e-2 of the output's own rms, see "Precision" above).

@@ -200,9 +200,15 @@ __global__ __launch_bounds__(1024) void k_sm_plan(const int32_t* __restrict__ cu
 // ------------------------------------------------------------------ rope --
 
 // Two floats as an fp16 pair (round to nearest even), first in the low half.
+// A value past fp16's range (or an infinite input) is stored as NaN, not as
+// an infinity: an infinite score can be -inf, which the softmax would take as
+// a masked key, while a NaN reaches every output it touches.
+__device__ __forceinline__ uint16_t f16_bits_or_nan(float a) {
+    const uint16_t u = __builtin_bit_cast(uint16_t, (_Float16)a);
+    return (u & 0x7fffu) == 0x7c00u ? (uint16_t)0x7e00u : u;
+}
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    return (uint32_t)f16_bits_or_nan(a) | ((uint32_t)f16_bits_or_nan(b) << 16);
 }
 
 // Rotary embedding, scale and bf16 (or, for fp16 scores, fp16) rounding of q

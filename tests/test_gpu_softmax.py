@@ -284,6 +284,33 @@ def test_fp16_scores_hold_wide_and_narrow_magnitudes(mag, precision):
     assert lerr <= lse_tol(precision)
 
 
+def test_fp16_scores_overflow_is_nan_in_exactly_the_rows_it_enters():
+    # fp16 scores hold rotated elements below 4.19e6 (times 2^-6 in fp16); a
+    # larger one is stored as NaN: the query row it belongs to, or for a key
+    # every later row of its sequence and key/value head, comes out NaN (a
+    # negative key element would otherwise give -inf scores, i.e. a silently
+    # dropped key); every other output is unaffected.  The split mode holds
+    # such inputs.
+    lengths = [300, 700]
+    H, Hkv, d = 4, 2, 128
+    q, k, v, cu = packed(lengths, H, Hkv, 131)
+    t0, t1 = 450, 520            # both in the second sequence (tokens 300 ..)
+    q[t0, 1, 100] = 6.0e6        # unrotated dimension (rotary_dim = 64)
+    k[t1, 0, 90] = -6.0e6
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7, precision=2)
+    bad = np.zeros((q.shape[0], H), dtype=bool)
+    bad[t0, 1] = True
+    bad[t1:, 0:2] = True         # query heads 0 and 1 read key/value head 0
+    assert np.isnan(got[bad]).all() and np.isnan(lse[bad]).all()
+    assert np.isfinite(got[~bad]).all() and np.isfinite(lse[~bad]).all()
+    ref, lref = SO.attention(q, k, v, cu, rope_base=1e7)
+    rms = float(np.sqrt(np.mean(ref[~bad] ** 2)))
+    assert float(np.abs(got[~bad] - ref[~bad]).max()) / rms <= SPLIT_TOL
+    assert float(np.abs(lse[~bad] - lref[~bad]).max()) <= lse_tol(2)
+    got1, lse1 = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7, precision=1)
+    assert np.isfinite(got1).all() and np.isfinite(lse1).all()
+
+
 def test_fp16_scores_error_grows_with_the_spread():
     # fp16 scores round the rotated q and k to 11 bits, so a score's error
     # scales with the score: with q std 1, 2, 4 (score spreads 1, 2, 4) on a
