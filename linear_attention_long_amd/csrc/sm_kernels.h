@@ -34,10 +34,11 @@
 //  * the score tile is produced transposed, S^T = K Q^T
 //    (v_mfma_f32_16x16x32_bf16), so each lane holds 4 keys of one query: the
 //    running max needs only two cross-lane steps;
-//  * the running sum of the probabilities comes from the matrix cores: an
-//    all-ones operand times P^T gives each query's sum of the same
-//    bf16-rounded weights that multiply V (no vector adds, and numerator and
-//    denominator agree);
+//  * the running sum of the probabilities is taken over the same
+//    bf16-rounded weights that multiply V, so numerator and denominator
+//    agree: each lane adds its own keys' packed weights with
+//    v_dot2_f32_bf16 against (1, 1) (products exact), and the four lane
+//    groups of a query are added once, at the end;
 //  * the k index of every MFMA is permuted so a lane's 8 slots are keys
 //    {32s + 4g + i, 32s + 16 + 4g + i}: that is the order in which two
 //    adjacent 16-key score tiles sit in a lane's accumulators, so the
@@ -321,6 +322,16 @@ __device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, f32x4_t v, flo
     *(uint2*)p = make_uint2(cvt_pk_bf16(v[0] * s, v[1] * s), cvt_pk_bf16(v[2] * s, v[3] * s));
 }
 
+// Sum of eight bf16 values (four packed pairs) into an fp32 accumulator: one
+// v_dot2_f32_bf16 against (1, 1) per pair, products exact.
+__device__ __forceinline__ float sum8_bf16(uint4 u, float acc) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one, acc, false);
+}
+
 // Operand of 32 head dimensions of one LDS row for the permuted k order:
 // columns {k0 + 4g + i, k0 + 16 + 4g + i}; the literal 16 lets the compiler
 // merge the two 8-byte reads into one ds_read2_b64.
@@ -431,18 +442,17 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
         }
     }
 
-    // O^T accumulators; Lc[qt] is the row sum of the bf16 probabilities,
-    // produced by the matrix cores from an all-ones operand (every row of a
-    // lane's 4 holds the same sum), so numerator and denominator see the
-    // same rounded weights.
-    f32x4_t O[8][2], Lc[2];
+    // O^T accumulators; lsum[qt]: this lane's part (its keys 4g + i of every
+    // 16-key tile) of the query's sum of the same rounded weights that
+    // multiply V; the four lane groups are added at the end.
+    f32x4_t O[8][2];
+    float lsum[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        Lc[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lsum[qt] = 0.f;
 #pragma unroll
         for (int ft = 0; ft < 8; ++ft) O[ft][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const bf16x8_t ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
     // Reference maximum per query (log2 units).  Probabilities are exp2(s - m)
     // with m raised only when a score exceeds it by more than kLazy, so the
     // accumulators are rescaled rarely; they stay below 2^kLazy.
@@ -580,7 +590,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                     const float mn = mx[qt] > m[qt] + kLazy ? mx[qt] : m[qt];
                     const float alpha = __builtin_amdgcn_exp2f(m[qt] - mn);
                     m[qt] = mn;
-                    Lc[qt] *= alpha;
+                    lsum[qt] *= alpha;
 #pragma unroll
                     for (int ft = 0; ft < 8; ++ft) O[ft][qt] *= alpha;
                 }
@@ -608,11 +618,13 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                         split2(bq[2], bq[3], h3, l3);
                         Pf[ks][qt] = as_bf16x8(make_uint4(h0, h1, h2, h3));
                         Pl[ks][qt] = as_bf16x8(make_uint4(l0, l1, l2, l3));
+                        lsum[qt] = sum8_bf16(make_uint4(l0, l1, l2, l3),
+                                             sum8_bf16(make_uint4(h0, h1, h2, h3), lsum[qt]));
                     } else {
-                        Pf[ks][qt] = as_bf16x8(make_uint4(cvt_pk_bf16(a[0], a[1]),
-                                                          cvt_pk_bf16(a[2], a[3]),
-                                                          cvt_pk_bf16(bq[0], bq[1]),
-                                                          cvt_pk_bf16(bq[2], bq[3])));
+                        const uint4 p4 = make_uint4(cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]),
+                                                    cvt_pk_bf16(bq[0], bq[1]), cvt_pk_bf16(bq[2], bq[3]));
+                        Pf[ks][qt] = as_bf16x8(p4);
+                        lsum[qt] = sum8_bf16(p4, lsum[qt]);
                     }
                 }
             const uint16_t* vt_ = sm.v[buf];
@@ -628,11 +640,6 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                         if constexpr (SPLIT) O[ft][qt] = mfma16x16x32(A, Pl[ks][qt], O[ft][qt]);
                     }
                 }
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt) {
-                    Lc[qt] = mfma16x16x32(ones, Pf[ks][qt], Lc[qt]);
-                    if constexpr (SPLIT) Lc[qt] = mfma16x16x32(ones, Pl[ks][qt], Lc[qt]);
-                }
             }
             __builtin_amdgcn_s_setprio(0);
         }
@@ -644,7 +651,8 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
     // wq0 + 16 qt + c.
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-        const float lt = Lc[qt][0];
+        float lt = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
         const int row = wq0 + 16 * qt + c;
         if (row < L) {
             const float inv = 1.0f / lt;
