@@ -34,11 +34,11 @@
  * against fp64 the output errs by about 1e-4 of its own rms for any bf16
  * input, within the 1e-2-of-rms bound for bf16 inputs with fp32
  * accumulation.  fp16 scores (2): the rotated q and k rounded to fp16 (11
- * bits), one product per score, the probabilities split as in 1; about 2e-3
- * of the output's rms for scores of unit spread, growing with the spread
- * (the score errors scale with the scores: 5e-3 to 7e-3 at spreads of 2 to
- * 4 on 2K-token rows), so within the bound only where the spread is known
- * to be small.  Single mode (0): bf16 q, k and probabilities, the usual
+ * bits), one product per score, the probabilities split as in 1; 2e-3 to
+ * 4e-3 of the output's rms for scores of unit spread, growing with the
+ * spread (the score errors scale with the scores: 5.6e-3 measured at a
+ * spread of 4 on a 2,050-token row), so within the bound only where the
+ * spread is known to be small.  Single mode (0): bf16 q, k and probabilities, the usual
  * attention kernel; a few 1e-3 of the values' rms for scores of unit
  * spread, growing with the spread, and since a row's output shrinks as its
  * keys grow, far more than 1e-2 of the output's own rms on long sequences.
@@ -81,7 +81,7 @@ extern "C" {
  *               any bf16 input.  2: fp16 scores -- the rotated q and k, each
  *               taken times 2^-6 (exact; the scores are scaled back by
  *               2^12), rounded to fp16, one product per score; the
- *               probabilities split as in 1.  0.79x the time of 1; error
+ *               probabilities split as in 1.  About 0.8x the time of 1; error
  *               as in "Precision" above.  fp16's normal range then covers
  *               rotated elements of magnitude 2^-8 to 2^22; smaller ones
  *               keep an absolute error below 2^-19, and one of 4.19e6 or
@@ -119,8 +119,9 @@ la_softmax_options_t la_softmax_default_options(void);
  *   in_dtype = LA_DTYPE_BF16 (LA_DTYPE_F32 inputs: LA_ERR_UNSUPPORTED),
  *   H * d <= 2^20.
  *   workspace   device scratch of at least la_softmax_workspace_bytes(...)
- *               bytes, 256-byte aligned: the rotated q and k (bf16; in the
- *               split mode also their bf16 remainders) and, for
+ *               bytes, 256-byte aligned: the rotated q and k (bf16, or fp16
+ *               with precision 2; in the split mode also their bf16
+ *               remainders) and, for
  *               num_seqs > 1, the work order.
  * `out` and `lse` must not overlap each other, the inputs or the workspace. */
 la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void* v,
