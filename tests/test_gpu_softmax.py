@@ -85,16 +85,29 @@ def test_packed_ragged_lengths(H, Hkv):
     print("packed H=%d Hkv=%d: max|err|/rms(v) %.2e" % (H, Hkv, check(got, ref, v, lse, lref)))
 
 
+@pytest.mark.parametrize("precision", [0, 1, 2])
 @pytest.mark.parametrize("rot,base,odt", [(0, 1e4, torch.float32), (32, 5e6, torch.bfloat16),
                                           (128, 1e7, torch.float32), (64, 1e7, torch.bfloat16),
                                           (16, 1e4, torch.bfloat16)])
-def test_rotary_dims_bases_and_output_dtypes(rot, base, odt):
+def test_rotary_dims_bases_and_output_dtypes(rot, base, odt, precision):
+    # every rotated width (the rotation kernel's rotated and plain paths, and
+    # in the split mode the count of three-product steps) in every mode
     lengths = [700, 1, 333]
     q, k, v, cu = packed(lengths, 2, 2, 21 + rot)
-    got, lse = run(q, k, v, cu, out_dtype=odt, rotary_dim=rot, rope_base=base)
+    got, lse = run(q, k, v, cu, out_dtype=odt, rotary_dim=rot, rope_base=base, precision=precision)
     ref, lref = SO.attention(q, k, v, cu, rotary_dim=rot, rope_base=base)
-    # a bf16 output adds its own rounding, u * |out| <= 2^-8 * max|v|
-    check(got, ref, v, lse, lref, tol=TOL + (2.0 ** -8 * 5 if odt == torch.bfloat16 else 0))
+    if precision == 0:
+        # a bf16 output adds its own rounding, u * |out| <= 2^-8 * max|v|
+        check(got, ref, v, lse, lref, tol=TOL + (2.0 ** -8 * 5 if odt == torch.bfloat16 else 0))
+        return
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    if odt == torch.bfloat16:
+        err = float((np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)).max()) / rms
+    else:
+        err = float(np.abs(got - ref).max()) / rms
+    assert np.isfinite(got).all()
+    assert err <= SPLIT_TOL, "precision %d: max|err|/rms(out) = %.3e" % (precision, err)
+    assert float(np.abs(lse - lref).max()) <= lse_tol(precision)
 
 
 def test_scale_option_and_wider_score_spread():
@@ -402,18 +415,23 @@ def test_workload_1m_sampled(precision):
         assert err <= SPLIT_TOL and lerr <= lse_tol(precision)
 
 
-def test_many_heads_grouped_and_without_lse():
+@pytest.mark.parametrize("precision", [0, 1, 2])
+def test_many_heads_grouped_and_without_lse(precision):
     # 64 query heads over 8 key/value heads (groups of 8), lengths at and
     # around the 256-query tile; the call without an lse output writes the
     # same out
     lengths = [256, 512, 255, 257, 1]
     q, k, v, cu = packed(lengths, 64, 8, 91)
-    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7)
+    got, lse = run(q, k, v, cu, out_dtype=torch.float32, rope_base=1e7, precision=precision)
     ref, lref = SO.attention(q, k, v, cu, rope_base=1e7)
-    check(got, ref, v, lse, lref)
+    if precision == 0:
+        check(got, ref, v, lse, lref)
+    else:
+        err = float(np.abs(got - ref).max()) / float(np.sqrt(np.mean(ref ** 2)))
+        assert err <= SPLIT_TOL and float(np.abs(lse - lref).max()) <= lse_tol(precision)
     out2, none = api.la_softmax_attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 512,
                                                  out_dtype=torch.float32, rope_base=1e7,
-                                                 precision=0)
+                                                 precision=precision)
     torch.cuda.synchronize()
     assert none is None
     np.testing.assert_array_equal(out2.double().cpu().numpy(), got)
