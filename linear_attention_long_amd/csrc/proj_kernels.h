@@ -36,9 +36,11 @@
 //    four steps ahead: no gain, so load latency is not the limit) and
 //    v_mfma_f32_32x32x16_bf16 tiles (same LDS traffic, a few % slower);
 //  * blockIdx -> tile is XCD-aware: workgroup i runs on XCD i % 8, and each XCD
-//    takes a contiguous range of tiles, ordered in groups of 8 token tiles per
-//    feature tile so that the concurrently running workgroups of an XCD share
-//    their weight and hidden-state slices in that XCD's L2.
+//    takes a contiguous range of tiles, ordered in groups of 4 token tiles per
+//    feature tile so that the concurrently running workgroups of an XCD (4
+//    token tiles x 8 feature tiles) share their weight and hidden-state
+//    slices in that XCD's L2 (measured against groups of 2 to 32: 3 to 6
+//    are within 1% of each other, 8 is 5-15% slower, 16 and 32 slower still).
 #pragma once
 
 #include "la_device.h"
@@ -50,7 +52,7 @@ constexpr int BM = 256;      // tokens per workgroup tile
 constexpr int BN = 256;      // output features per workgroup tile
 constexpr int BK = 64;       // reduction slice per LDS stage (one 128-byte row)
 constexpr int NT = 512;      // threads (8 waves)
-constexpr int GM = 8;        // token tiles per group in the tile order
+constexpr int GM = 4;        // token tiles per group in the tile order
 
 struct __attribute__((aligned(1024))) Smem {
     __attribute__((aligned(1024))) uint16_t w[2][BN * BK];
