@@ -48,8 +48,10 @@ def check_bf16(got, ref):
     assert not bad.any(), "%d elements outside the bf16 storage bound" % bad.sum()
 
 
+# T = 1537: 7 token tiles, a full group of 4 in the tile order and a partial
+# group of 3
 @pytest.mark.parametrize("T,K,F", [(1, 64, 256), (255, 128, 256), (257, 320, 512),
-                                   (1000, 6144, 1024)])
+                                   (1000, 6144, 1024), (1537, 256, 1024)])
 @pytest.mark.parametrize("featurize", [True, False])
 def test_projection_fp32_out(T, K, F, featurize):
     banner("projection T=%d K=%d F=%d featurize=%s fp32 out" % (T, K, F, featurize))
@@ -159,7 +161,7 @@ def make_out(T, K, N, seed):
 
 
 @pytest.mark.parametrize("T,K,N", [(1, 64, 256), (255, 128, 512), (257, 1024, 6144),
-                                   (1000, 1024, 6144)])
+                                   (1000, 1024, 6144), (1537, 256, 768)])
 def test_out_projection_fp32_out(T, K, N):
     banner("out projection T=%d K=%d N=%d fp32 out" % (T, K, N))
     y, w = make_out(T, K, N, 50 + T)
