@@ -895,7 +895,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 32K-token and varlen timings and the copy-bandwidth reference")
-    ap.add_argument("--cpu-tokens", type=int, default=262144)
+    ap.add_argument("--cpu-tokens", type=int, default=524288)
     ap.add_argument("--no-softmax", action="store_true",
                     help="skip the softmax attention layer's workloads")
     ap.add_argument("--no-softmax-1m", action="store_true",
