@@ -762,14 +762,46 @@ PROJECTION_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "projection_gemm_32k_tr
 SOURCES = os.path.join(ROOT, "linear_attention_long_amd", "csrc")
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments and blank lines: each comment
+    becomes one space (a line comment ends at its newline), string and
+    character literals are kept as written, trailing blanks are cut and
+    empty lines dropped.  Edits to comments or blank lines leave it as it
+    is; any change to the code changes it."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        ch = src[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and src[j] != ch and src[j] != "\n":
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).split("\n"))
+    return "\n".join(line for line in lines if line)
+
+
 def _digest(names) -> str:
-    """sha256 over the names and contents of the given csrc/ files, in order."""
+    """sha256 over the names and code (code_text: comments and blank lines
+    left out) of the given csrc/ files, in order."""
     import hashlib
 
     h = hashlib.sha256()
     for name in names:
         h.update(name.encode())
-        h.update(open(os.path.join(SOURCES, name), "rb").read())
+        h.update(code_text(open(os.path.join(SOURCES, name), encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

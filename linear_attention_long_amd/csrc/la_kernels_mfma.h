@@ -10,8 +10,9 @@
 //
 // gfx950 design:
 //  * one workgroup = 4 waves = one (chunk, head); with TB = 32 the LDS of a
-//    workgroup is ~64 KB and two workgroups share a CU, so one's SiLU/split
-//    VALU work overlaps the other's matrix-core work; wave w owns value columns
+//    workgroup is 79 KiB (60 KiB of q, k, v and P^T tiles, the rest the fused
+//    gate's stash of Y and sums) and two workgroups share a CU, so one's
+//    SiLU/split VALU work overlaps the other's matrix-core work; wave w owns value columns
 //    [32w, 32w+32) of the state (128 x 32 fp32 = 64 accumulator registers per
 //    lane) and of the output, so the state never leaves registers;
 //  * q, k, v of a block are staged once into LDS as bf16 hi/lo pairs

@@ -23,12 +23,10 @@
 //    over blocks of 128 keys (64 with split operands).
 //
 // gfx950 design of k_sm_attn:
-//  * W waves x 32 queries: 8 waves (256-query tiles, one workgroup per CU)
-//    with single bf16 operands, 4 waves (128-query tiles) with split
-//    operands, whose registers allow only one 4-wave workgroup per CU; either
-//    way two waves share a SIMD (fp16 scores use the split layout with one
-//    score product, v_mfma_f32_16x16x32_f16, instead of three).  Each staged
-//    K/V block serves all W waves.
+//  * W = 8 waves x 32 queries (256-query tiles) in every precision mode, one
+//    workgroup per CU, two waves per SIMD (fp16 scores use the split layout
+//    with one score product, v_mfma_f32_16x16x32_f16, instead of three).
+//    Each staged K/V block serves all W waves.
 //    A wave's rotated Q stays in registers as MFMA operands for the whole
 //    key loop;
 //  * the score tile is produced transposed, S^T = K Q^T
@@ -58,9 +56,10 @@
 //  * the matrix-core sections run at raised wave priority (s_setprio 1), so a
 //    SIMD issues one wave's MFMA stream first and fills its gaps with the
 //    other wave's vector work;
-//  * 138 KB of LDS per workgroup (104.5 KB with split operands, 69 KB with fp16 scores); the blockIdx -> (tile, head)
-//    map puts key/value head hk on XCD hk mod 8, so the workgroups sharing a
-//    head's K and V share that XCD's L2.
+//  * 138 KiB of LDS per workgroup (102 KiB with split operands, 69 KiB with
+//    fp16 scores); the blockIdx -> (tile, head) map puts key/value head hk on
+//    XCD hk mod 8, so the workgroups sharing a head's K and V share that
+//    XCD's L2.
 #pragma once
 
 #include "la_device.h"
@@ -347,7 +346,7 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
                      lds_read_tr4(tile, KSV, r0 + 16 + 4 * g, c0, c));
 }
 
-// One (128-query tile, query head) of causal softmax attention.
+// One (32 W-query tile, query head) of causal softmax attention.
 //   qr [T, H, D] bf16: rotated q times scale * log2(e); kr [T, Hkv, D] bf16:
 //   rotated k; v [T, Hkv, D] bf16; out [T, H, D]; lse [T, H] (natural log)
 //   or null.  table/ecount: the plan (null for a single sequence, whose

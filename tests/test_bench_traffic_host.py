@@ -53,3 +53,28 @@ def test_committed_summaries_name_their_figures(bench):
         assert "source_sha256: " in text
         for k in keys:
             assert "\n%s: " % k in text
+
+
+def test_code_text_drops_comments_and_blank_lines_only(bench):
+    ct = bench.code_text
+    assert ct("int a; // note\nint b; /* two\n lines */ int c;\n\n   \n") == "int a;\nint b;   int c;"
+    # comment markers inside string and character literals are code
+    assert ct('s = "a//b /*c*/"; // t') == 's = "a//b /*c*/";'
+    assert ct("c = '\\''; // q") == "c = '\\'';"
+    assert ct('p = "\\"//"; x') == 'p = "\\"//"; x'
+    # a comment edit keeps the text; any code edit changes it
+    base = "float f(float x) {\n    return x * 2.0f;  // double\n}\n"
+    assert ct(base) == ct(base.replace("// double", "// twice the input\n\n"))
+    assert ct(base) != ct(base.replace("2.0f", "3.0f"))
+    assert ct(base) != ct(base.replace("x * 2", "x*2"))
+
+
+def test_digest_ignores_comment_edits(bench, tmp_path, monkeypatch):
+    src = tmp_path / "k.h"
+    src.write_text("// header\n__device__ int g(int a) { return a + 1; }\n")
+    monkeypatch.setattr(bench, "SOURCES", str(tmp_path))
+    d0 = bench._digest(("k.h",))
+    src.write_text("// header, reworded\n\n__device__ int g(int a) { return a + 1; }  /* note */\n")
+    assert bench._digest(("k.h",)) == d0
+    src.write_text("// header\n__device__ int g(int a) { return a + 2; }\n")
+    assert bench._digest(("k.h",)) != d0
