@@ -473,17 +473,17 @@ def bench_serving(args, torch, api, inputs, reps=50):
 
 # (workload, timed calls, precision): 1 = split operands in both products
 # (the library's default, within 1e-2 of the output's rms for any bf16
-# input), 2 = fp16 scores with split probabilities, 0 = single bf16 operands
+# input), 2 = fp16 operands (q, k, v, probabilities), 0 = single bf16 operands
 SOFTMAX_WORKLOADS = (("softmax_32k", 10, 1), ("softmax_varlen_512k", 3, 1), ("softmax_1m", 1, 1),
                      ("softmax_32k", 10, 2), ("softmax_varlen_512k", 3, 2),
                      ("softmax_32k", 20, 0), ("softmax_varlen_512k", 5, 0))
-SOFTMAX_KEY = {1: "", 2: "_fp16_scores", 0: "_single"}
+SOFTMAX_KEY = {1: "", 2: "_fp16", 0: "_single"}
 SOFTMAX_NOTE = {
     1: ("split bf16 hi+lo operands in both products (default; within 1e-2 of the output's rms "
         "for any bf16 input)"),
-    2: ("fp16 scores (q, k times 2^-6 rounded to fp16), split bf16 hi+lo probabilities: about "
-        "2e-3 of the output's rms for unit-spread scores, growing with the spread (not the "
-        "library default)"),
+    2: ("fp16 operands (q, k, v times 2^-6 and the probabilities rounded to fp16, one product "
+        "each): about 3e-3 to 5e-3 of the output's rms for scores of unit spread and more, "
+        "growing with the spread (not the library default)"),
     0: ("single bf16 operands: about 1e-3 of the values' scale, which on long rows exceeds "
         "the 1e-2-of-output-rms bound for bf16 inputs (not the library default)"),
 }

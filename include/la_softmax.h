@@ -33,12 +33,13 @@
  * the probabilities are each carried as bf16 hi + lo (~16 significant bits);
  * against fp64 the output errs by about 1e-4 of its own rms for any bf16
  * input, within the 1e-2-of-rms bound for bf16 inputs with fp32
- * accumulation.  fp16 scores (2): the rotated q and k rounded to fp16 (11
- * bits), one product per score, the probabilities split as in 1; 2e-3 to
- * 4e-3 of the output's rms for scores of unit spread, growing with the
- * spread (the score errors scale with the scores: 5.6e-3 measured at a
- * spread of 4 on a 2,050-token row), so within the bound only where the
- * spread is known to be small.  Single mode (0): bf16 q, k and probabilities, the usual
+ * accumulation.  fp16 operands (2): the rotated q and k, v and the
+ * probabilities rounded to fp16 (11 bits; v exact within its range), one
+ * product each, about the speed of mode 0; 3e-3 to 5e-3 of the output's rms
+ * for scores of unit spread and more, growing with the spread (the score
+ * errors scale with the scores: 4.4e-3 at a spread of 1 and 5.2e-3 at 4,
+ * measured on a 2,050-token row), so within the bound only where the spread
+ * is known to be small.  Single mode (0): bf16 q, k and probabilities, the usual
  * attention kernel; a few 1e-3 of the values' rms for scores of unit
  * spread, growing with the spread, and since a row's output shrinks as its
  * keys grow, far more than 1e-2 of the output's own rms on long sequences.
@@ -78,16 +79,20 @@ extern "C" {
  *               each as bf16 hi + lo, three products per score on the
  *               rotated dimensions (one elsewhere, where bf16 inputs are
  *               exact) and two for P V; about 1e-4 of the output's rms for
- *               any bf16 input.  2: fp16 scores -- the rotated q and k, each
- *               taken times 2^-6 (exact; the scores are scaled back by
- *               2^12), rounded to fp16, one product per score; the
- *               probabilities split as in 1.  About 0.8x the time of 1; error
- *               as in "Precision" above.  fp16's normal range then covers
- *               rotated elements of magnitude 2^-8 to 2^22; smaller ones
- *               keep an absolute error below 2^-19, and one of 4.19e6 or
- *               more (or an infinite input) is stored as NaN, so every
- *               output whose scores it enters is NaN: its query's row, or
- *               for a key, the rows of the sequence from that key on.
+ *               any bf16 input.  2: fp16 operands -- the rotated q and k
+ *               and v, each taken times 2^-6 (exact; the scores are scaled
+ *               back by 2^12 and the output by 2^6), rounded to fp16, and
+ *               the probabilities rounded to fp16: one product per score
+ *               and per P V step.  About 0.6x the time of 1; error as in
+ *               "Precision" above.  fp16's normal range then covers
+ *               elements of magnitude 2^-8 to 2^22; smaller ones keep an
+ *               absolute error below 2^-19, and one of 4.19e6 or more (or
+ *               an infinite input) is stored as NaN: in q or k every output
+ *               whose scores it enters is NaN (its query's row, or for a
+ *               key, the rows of the sequence from that key on); in v its
+ *               feature is NaN in the rows of the sequence from the start
+ *               of its 128-key block on (the P V product meets it with the
+ *               block's masked zero weights too).
  *               0: single bf16 operands for both products
  *               (the usual attention kernel, the fastest; error against
  *               fp64 about 1e-3 of the values' scale, on long rows more
@@ -120,8 +125,8 @@ la_softmax_options_t la_softmax_default_options(void);
  *   H * d <= 2^20.
  *   workspace   device scratch of at least la_softmax_workspace_bytes(...)
  *               bytes, 256-byte aligned: the rotated q and k (bf16, or fp16
- *               with precision 2; in the split mode also their bf16
- *               remainders) and, for
+ *               with precision 2, which also stores v there as fp16; in
+ *               the split mode also their bf16 remainders) and, for
  *               num_seqs > 1, the work order.
  * `out` and `lse` must not overlap each other, the inputs or the workspace. */
 la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void* v,

@@ -295,7 +295,7 @@ def la_softmax_attention_varlen(q, k, v, cu_seqlens, max_seqlen, *, rotary_dim=-
     [num_seqs + 1] on the GPU; max_seqlen: host int bounding every length.
     rotary_dim -1 = d/2; scale 0 = 1/sqrt(d); precision 1 (default) = split
     (hi + lo) operands in both products, within 1e-2 of the output's rms;
-    2 = fp16 scores with split probabilities (faster; within that bound for
+    2 = fp16 operands, one product each (faster; within that bound for
     scores of unit spread, error growing with the spread); 0 = single bf16
     operands (fastest, loosest).  Returns (out [total_T, H, d],
     lse [total_T, H] float32 or None)."""

@@ -38,14 +38,14 @@ inline bool dtype_arg_ok(const la_dtype_t& t) {
 // two waves per SIMD with 8.
 constexpr int kWavesPlain = LA_SM_WAVES;
 constexpr int kWavesSplit = LA_SM_WAVES_SPLIT;
-// fp16 scores: q and k are rounded to fp16 times this power of two
+// fp16 operands: q, k and v are rounded to fp16 times this power of two
 constexpr float kF16Pre = 0.015625f;  // 2^-6
 inline int tile_queries(bool split) { return 32 * (split ? kWavesSplit : kWavesPlain); }
 
 struct SmOpts {
     int rot;
-    bool split;    // probabilities split (precision 1 and 2)
-    bool f16s;     // scores from fp16 q and k (precision 2): no q/k remainders
+    bool split;    // split operands (precision 1)
+    bool f16;      // fp16 operands (precision 2)
     double base;
     float scale;
     hipEvent_t* events;
@@ -57,7 +57,8 @@ struct SmLayout {
     int ntmax;        // query tiles of the longest sequence
     int64_t emax;     // bound of the (sequence, tile) pairs
     bool planned;     // num_seqs > 1: the plan kernel orders the tiles
-    size_t off_qr, off_kr, off_qrl, off_krl, off_count, off_table, off_hist, off_off, off_cursor, off_tcu, total;
+    size_t off_qr, off_kr, off_qrl, off_krl, off_vr, off_count, off_table, off_hist, off_off, off_cursor,
+        off_tcu, total;
 };
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -86,8 +87,8 @@ la_status_t sm_parse(const la_softmax_options_t* opt, int d, SmOpts& o) {
     o.events = (hipEvent_t*)x.timing_events;
     o.n_events = x.timing_events ? x.n_timing : 0;
     if (x.precision < 0 || x.precision > 2) return LA_ERR_INVALID_ARGUMENT;
-    o.split = x.precision >= 1;
-    o.f16s = x.precision == 2;
+    o.split = x.precision == 1;
+    o.f16 = x.precision == 2;
     return LA_OK;
 }
 
@@ -106,7 +107,7 @@ la_status_t sm_check(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int3
 }
 
 la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int32_t H,
-                      int32_t H_kv, bool split, bool remainders, SmLayout& p) {
+                      int32_t H_kv, bool split, bool f16, SmLayout& p) {
     const int BQ = tile_queries(split);
     p.bq = BQ;
     p.ntmax = (max_seqlen + BQ - 1) / BQ;
@@ -120,11 +121,15 @@ la_status_t sm_layout(int32_t num_seqs, int32_t total_T, int32_t max_seqlen, int
     o = a256(o + (size_t)total_T * H * sm::D * 2);
     p.off_kr = o;
     o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
-    p.off_qrl = p.off_krl = o;
-    if (remainders) {  // bf16 remainders of the rotated q and k (precision 1)
+    p.off_qrl = p.off_krl = p.off_vr = o;
+    if (split) {  // bf16 remainders of the rotated q and k (precision 1)
         p.off_qrl = o;
         o = a256(o + (size_t)total_T * H * sm::D * 2);
         p.off_krl = o;
+        o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
+    }
+    if (f16) {  // v as fp16 (precision 2)
+        p.off_vr = o;
         o = a256(o + (size_t)total_T * H_kv * sm::D * 2);
     }
     p.off_count = p.off_table = p.off_hist = p.off_off = p.off_cursor = p.off_tcu = o;
@@ -184,7 +189,7 @@ size_t la_softmax_workspace_bytes(int32_t num_seqs, int32_t total_T, int32_t max
     SmOpts o;
     if (sm_parse(opt, d, o) != LA_OK) return (size_t)-1;
     SmLayout p;
-    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.split && !o.f16s, p) != LA_OK) return (size_t)-1;
+    if (sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.f16, p) != LA_OK) return (size_t)-1;
     return p.total;
 }
 
@@ -206,7 +211,7 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         !is_aligned(cu_seqlens, 4) || (lse && !is_aligned(lse, 4)))
         return LA_ERR_INVALID_ARGUMENT;
     SmLayout p;
-    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.split && !o.f16s, p)) != LA_OK) return st;
+    if ((st = sm_layout(num_seqs, total_T, max_seqlen, H, H_kv, o.split, o.f16, p)) != LA_OK) return st;
     const size_t nq = (size_t)total_T * H * d * 2, nkv = (size_t)total_T * H_kv * d * 2;
     const size_t nout = (size_t)total_T * H * d * (out_dtype == LA_DTYPE_BF16 ? 2 : 4);
     const size_t nlse = lse ? (size_t)total_T * H * 4 : 0;
@@ -231,9 +236,9 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
     char* ws = (char*)workspace;
     uint16_t* qr = (uint16_t*)(ws + p.off_qr);
     uint16_t* kr = (uint16_t*)(ws + p.off_kr);
-    const bool rem = o.split && !o.f16s;
-    uint16_t* qrl = rem ? (uint16_t*)(ws + p.off_qrl) : nullptr;
-    uint16_t* krl = rem ? (uint16_t*)(ws + p.off_krl) : nullptr;
+    uint16_t* qrl = o.split ? (uint16_t*)(ws + p.off_qrl) : nullptr;
+    uint16_t* krl = o.split ? (uint16_t*)(ws + p.off_krl) : nullptr;
+    uint16_t* vr = o.f16 ? (uint16_t*)(ws + p.off_vr) : nullptr;
     const int2* table = nullptr;
     const int32_t* count = nullptr;
     if (p.planned) {
@@ -253,47 +258,47 @@ la_status_t la_softmax_attention_varlen(const void* q, const void* k, const void
         const int64_t want = ((int64_t)total_T + 15) / 16;
         const int grid = (int)(want < 16384 ? want : 16384);
         // scores in log2 units: q carries scale * log2(e), except with split
-        // probabilities, where the attention kernel scales the fp32 scores (q
-        // then stays exact outside the rotated dimensions).  fp16 q and k are
-        // both taken times 2^-6 (exact), which moves fp16's normal range to
-        // rotated elements in [2^-8, 2^22); the attention kernel multiplies
-        // the scores back by 2^12.
-        const float qscale = o.f16s ? kF16Pre : o.split ? 1.0f : o.scale * 1.4426950408889634f;
-        const float kscale = o.f16s ? kF16Pre : 1.0f;
+        // or fp16 operands, where the attention kernel scales the fp32 scores
+        // (split: q then stays exact outside the rotated dimensions).  fp16
+        // q, k and v are taken times 2^-6 (exact), which moves fp16's normal
+        // range to elements in [2^-8, 2^22); the attention kernel multiplies
+        // the scores back by 2^12 and the output by 2^6.
+        const float qscale = o.f16 ? kF16Pre : o.split ? 1.0f : o.scale * 1.4426950408889634f;
+        const float kscale = o.f16 ? kF16Pre : 1.0f;
         tm.before();
         sm::k_sm_rope<<<grid, 256, 0, stream>>>((const uint16_t*)q, (const uint16_t*)k, cu_seqlens,
                                                 num_seqs, total_T, H, H_kv, o.rot,
                                                 o.rot > 0 ? std::log2(o.base) : 0.0, qscale, kscale,
-                                                qr, kr,
-                                                qrl, krl, o.f16s ? 1 : 0);
+                                                qr, kr, qrl, krl, o.f16 ? 1 : 0,
+                                                (const uint16_t*)v, vr, kF16Pre);
         tm.after();
     }
     const unsigned grid = (unsigned)(p.emax * H);
     tm.before();
     if (grid > 0) {
-        const float qs = o.scale * 1.4426950408889634f * (o.f16s ? 1.0f / (kF16Pre * kF16Pre) : 1.0f);
+        const float qs = o.scale * 1.4426950408889634f * (o.f16 ? 1.0f / (kF16Pre * kF16Pre) : 1.0f);
+        const float ovs = o.f16 ? 1.0f / kF16Pre : 1.0f;
+        const uint16_t* vin = o.f16 ? vr : (const uint16_t*)v;
         const int nrk = (o.rot + 31) / 32;  // 32-dimension steps holding rotated dimensions
 #define SM_ATTN(OT, SP, W, NRK, F16)                                                                \
-    sm::k_sm_attn<OT, SP, W, NRK, F16><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, (const uint16_t*)v, \
+    sm::k_sm_attn<OT, SP, W, NRK, F16><<<grid, 64 * W, 0, stream>>>(qr, kr, qrl, krl, vin,           \
                                                                cu_seqlens, table, count, H, H_kv,   \
-                                                               (OT*)out, lse, qs)
-#define SM_ATTN_SPLIT(OT)                                               \
-    if (o.f16s) {                                                       \
-        SM_ATTN(OT, true, kWavesSplit, 0, true);                        \
-    } else {                                                            \
-        switch (nrk) {                                                  \
-            case 0: SM_ATTN(OT, true, kWavesSplit, 0, false); break;    \
-            case 1: SM_ATTN(OT, true, kWavesSplit, 1, false); break;    \
-            case 2: SM_ATTN(OT, true, kWavesSplit, 2, false); break;    \
-            case 3: SM_ATTN(OT, true, kWavesSplit, 3, false); break;    \
-            default: SM_ATTN(OT, true, kWavesSplit, 4, false); break;   \
-        }                                                               \
+                                                               (OT*)out, lse, qs, ovs)
+#define SM_ATTN_SPLIT(OT)                                           \
+    switch (nrk) {                                                  \
+        case 0: SM_ATTN(OT, true, kWavesSplit, 0, false); break;    \
+        case 1: SM_ATTN(OT, true, kWavesSplit, 1, false); break;    \
+        case 2: SM_ATTN(OT, true, kWavesSplit, 2, false); break;    \
+        case 3: SM_ATTN(OT, true, kWavesSplit, 3, false); break;    \
+        default: SM_ATTN(OT, true, kWavesSplit, 4, false); break;   \
     }
         if (out_dtype == LA_DTYPE_BF16) {
             if (o.split) { SM_ATTN_SPLIT(uint16_t) }
+            else if (o.f16) SM_ATTN(uint16_t, false, kWavesPlain, 4, true);
             else SM_ATTN(uint16_t, false, kWavesPlain, 4, false);
         } else {
             if (o.split) { SM_ATTN_SPLIT(float) }
+            else if (o.f16) SM_ATTN(float, false, kWavesPlain, 4, true);
             else SM_ATTN(float, false, kWavesPlain, 4, false);
         }
 #undef SM_ATTN_SPLIT

@@ -17,16 +17,16 @@
 //    by decreasing causal work, so the longest tiles start first;
 //  * k_sm_rope: q and k are rotated once (angles reduced in fp64), scaled,
 //    and rounded into the workspace (bf16, bf16 hi + lo, or fp16, by
-//    precision mode); every workgroup of the main kernel then reads ready
-//    operands;
+//    precision mode; with fp16 operands v is scaled and rounded to fp16 as
+//    well); every workgroup of the main kernel then reads ready operands;
 //  * k_sm_attn: one workgroup = one (query tile, head); streaming softmax
 //    over blocks of 128 keys (64 with split operands).
 //
 // gfx950 design of k_sm_attn:
 //  * W = 8 waves x 32 queries (256-query tiles) in every precision mode, one
-//    workgroup per CU, two waves per SIMD (fp16 scores use the split layout
-//    with one score product, v_mfma_f32_16x16x32_f16, instead of three).
-//    Each staged K/V block serves all W waves.
+//    workgroup per CU, two waves per SIMD (fp16 operands use the single
+//    layout with v_mfma_f32_16x16x32_f16 for both products).  Each staged
+//    K/V block serves all W waves.
 //    A wave's rotated Q stays in registers as MFMA operands for the whole
 //    key loop;
 //  * the score tile is produced transposed, S^T = K Q^T
@@ -56,8 +56,8 @@
 //  * the matrix-core sections run at raised wave priority (s_setprio 1), so a
 //    SIMD issues one wave's MFMA stream first and fills its gaps with the
 //    other wave's vector work;
-//  * 138 KiB of LDS per workgroup (102 KiB with split operands, 69 KiB with
-//    fp16 scores); the blockIdx -> (tile, head) map puts key/value head hk on
+//  * 138 KiB of LDS per workgroup (102 KiB with split operands); the
+//    blockIdx -> (tile, head) map puts key/value head hk on
 //    XCD hk mod 8, so the workgroups sharing a head's K and V share that
 //    XCD's L2.
 #pragma once
@@ -211,8 +211,10 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return (uint32_t)f16_bits_or_nan(a) | ((uint32_t)f16_bits_or_nan(b) << 16);
 }
 
-// Rotary embedding, scale and bf16 (or, for fp16 scores, fp16) rounding of q
-// and k; q is multiplied by qscale and k by kscale before the rounding.  16 threads per token
+// Rotary embedding, scale and bf16 (or, for fp16 operands, fp16) rounding of q
+// and k; q is multiplied by qscale and k by kscale before the rounding.  With
+// vr (fp16 operands) v is also multiplied by vscale and rounded to fp16 into vr.
+// 16 threads per token
 // (thread u owns 8 dimensions), grid-stride over tokens; for each token the
 // rotations are computed once and applied to its H query heads and Hkv key
 // heads.  Thread u < rot/16 rotates dimensions [8u, 8u+8) with their partners
@@ -228,7 +230,9 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                                                  uint16_t* __restrict__ qr,
                                                  uint16_t* __restrict__ kr,
                                                  uint16_t* __restrict__ qrl,
-                                                 uint16_t* __restrict__ krl, int f16out) {
+                                                 uint16_t* __restrict__ krl, int f16out,
+                                                 const uint16_t* __restrict__ v,
+                                                 uint16_t* __restrict__ vr, float vscale) {
     __shared__ double theta[64];
     if ((int)threadIdx.x < rot / 2)
         theta[threadIdx.x] = exp2(-(2.0 * (double)threadIdx.x / (double)rot) * log2_base);
@@ -305,6 +309,18 @@ __global__ __launch_bounds__(256) void k_sm_rope(const uint16_t* __restrict__ q,
                 if (dlo) *(uint4*)(dlo + 8 * u) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
             }
         }
+        if (vr) {  // every thread converts its 8 dimensions of each value head
+            for (int hv = 0; hv < Hkv; ++hv) {
+                const size_t base = ((size_t)t * Hkv + hv) * D + 8 * u;
+                const uint4 w = *(const uint4*)(v + base);
+                const uint32_t w32[4] = {w.x, w.y, w.z, w.w};
+                uint32_t o[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    o[p] = pack_f16x2(bf16_lo_to_f32(w32[p]) * vscale, bf16_hi_to_f32(w32[p]) * vscale);
+                *(uint4*)(vr + base) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
     }
 }
 
@@ -329,6 +345,23 @@ __device__ __forceinline__ float sum8_bf16(uint4 u, float acc) {
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.y), one, acc, false);
     acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.z), one, acc, false);
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u.w), one, acc, false);
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed fp16 (round to nearest even), one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+
+// The fp16 form of sum8_bf16: one v_dot2_f32_f16 against (1, 1) per pair.
+__device__ __forceinline__ float sum8_f16(uint4 u, float acc) {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, u.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, u.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, u.z), one, acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, u.w), one, acc, false);
 }
 
 // Operand of 32 head dimensions of one LDS row for the permuted k order:
@@ -359,10 +392,12 @@ __device__ __forceinline__ bf16x8_t v_operand(const uint16_t* tile, int r0, int 
 // (hi.hi + lo.hi + hi.lo); the probabilities are split into bf16 hi + lo for
 // two products with V (V is exact).  Both contractions keep ~16 significant
 // bits.  Without SPLIT, q carries the scale and NRK is unused.
-// F16S (with SPLIT, NRK = 0): qr and kr hold fp16 (the rotated q and k times
-// 2^-6 each), one fp16 product per score, qs then also carries 2^12; the
-// probabilities are split as above.
-template <typename OutT, bool SPLIT, int W, int NRK = 4, bool F16S = false>
+// F16 (without SPLIT): fp16 operands -- qr and kr hold the rotated q and k
+// times 2^-6 each, v holds the values times 2^-6, all fp16; one fp16 product
+// per score (qs then carries 2^12 and is applied in fp32 as with SPLIT) and
+// one per P V step, the probabilities rounded to fp16; ovs (2^6) scales the
+// output back.  ovs is 1 in the other modes.
+template <typename OutT, bool SPLIT, int W, int NRK = 4, bool F16 = false>
 __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(const uint16_t* __restrict__ qr,
                                                    const uint16_t* __restrict__ kr,
                                                    const uint16_t* __restrict__ qrl,
@@ -372,9 +407,9 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                                                    const int2* __restrict__ table,
                                                    const int32_t* __restrict__ ecount, int H,
                                                    int Hkv, OutT* __restrict__ out,
-                                                   float* __restrict__ lse, float qs) {
+                                                   float* __restrict__ lse, float qs, float ovs) {
     static_assert(NRK >= 0 && NRK <= 4, "rotated 32-dimension steps");
-    static_assert(!F16S || (SPLIT && NRK == 0), "fp16 scores: split probabilities, no q/k remainders");
+    static_assert(!F16 || !SPLIT, "fp16 operands: single products");
     constexpr bool KLO = SPLIT && NRK > 0;  // bf16 remainders of k staged and used
     constexpr int BN = SPLIT ? kBlockSplit : kBlockPlain;  // keys per K/V block
     constexpr int NKT = BN / 16;  // 16-key score tiles per block
@@ -536,7 +571,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt) {
                         const f32x4_t c0 = kk == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : Sc[kt][qt];
-                        if constexpr (F16S)  // q and k held as fp16 (the same 16-bit lanes)
+                        if constexpr (F16)  // q and k held as fp16 (the same 16-bit lanes)
                             Sc[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                 __builtin_bit_cast(f16x8_t, A), __builtin_bit_cast(f16x8_t, Qf[qt][kk]), c0, 0, 0, 0);
                         else
@@ -554,10 +589,10 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                     }
                 }
             __builtin_amdgcn_s_setprio(0);
-            // scores in log2 units are Sc * sc: with split operands the
-            // unscaled products (sc = qs > 0, applied below inside the
+            // scores in log2 units are Sc * sc: with split or fp16 operands
+            // the unscaled products (sc = qs > 0, applied below inside the
             // exponent's argument and to the block maximum), else q carries it
-            const float sc = SPLIT ? qs : 1.0f;
+            const float sc = (SPLIT || F16) ? qs : 1.0f;
             if (kb0 + BN - 1 > wq0) {  // causal mask on the diagonal blocks
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt) {
@@ -619,6 +654,11 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                         Pl[ks][qt] = as_bf16x8(make_uint4(l0, l1, l2, l3));
                         lsum[qt] = sum8_bf16(make_uint4(l0, l1, l2, l3),
                                              sum8_bf16(make_uint4(h0, h1, h2, h3), lsum[qt]));
+                    } else if constexpr (F16) {
+                        const uint4 p4 = make_uint4(cvt_pk_f16(a[0], a[1]), cvt_pk_f16(a[2], a[3]),
+                                                    cvt_pk_f16(bq[0], bq[1]), cvt_pk_f16(bq[2], bq[3]));
+                        Pf[ks][qt] = as_bf16x8(p4);  // fp16 bits in the 16-bit lanes
+                        lsum[qt] = sum8_f16(p4, lsum[qt]);
                     } else {
                         const uint4 p4 = make_uint4(cvt_pk_bf16(a[0], a[1]), cvt_pk_bf16(a[2], a[3]),
                                                     cvt_pk_bf16(bq[0], bq[1]), cvt_pk_bf16(bq[2], bq[3]));
@@ -635,7 +675,12 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
                     const bf16x8_t A = v_operand(vt_, 32 * ks, 16 * ft, g, c);
 #pragma unroll
                     for (int qt = 0; qt < 2; ++qt) {
-                        O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
+                        if constexpr (F16)
+                            O[ft][qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8_t, A), __builtin_bit_cast(f16x8_t, Pf[ks][qt]),
+                                O[ft][qt], 0, 0, 0);
+                        else
+                            O[ft][qt] = mfma16x16x32(A, Pf[ks][qt], O[ft][qt]);
                         if constexpr (SPLIT) O[ft][qt] = mfma16x16x32(A, Pl[ks][qt], O[ft][qt]);
                     }
                 }
@@ -654,7 +699,7 @@ __global__ __launch_bounds__(64 * W, (SPLIT || W == 8) ? 1 : 2) void k_sm_attn(c
         lt += __shfl_xor(lt, 32, 64);
         const int row = wq0 + 16 * qt + c;
         if (row < L) {
-            const float inv = 1.0f / lt;
+            const float inv = ovs / lt;
             OutT* op = out + ((size_t)(start + row) * H + h) * D + 4 * g;
 #pragma unroll
             for (int ft = 0; ft < 8; ++ft) store_out4<OutT>(op + 16 * ft, O[ft][qt], inv);

@@ -266,10 +266,10 @@ def test_softmax_workspace_bytes(lib):
     osp = _lib.softmax_options(precision=1)
     assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
                                           ctypes.byref(osp)) == 2 * (1000 * 4 * 256 + 1000 * 2 * 256)
-    # fp16 scores: the rotated q and k in fp16, no remainders (as single operands)
+    # fp16 operands: the rotated q and k in fp16, no remainders, and v in fp16
     o16 = _lib.softmax_options(precision=2)
     assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
-                                          ctypes.byref(o16)) == 1000 * 4 * 256 + 1000 * 2 * 256
+                                          ctypes.byref(o16)) == 1000 * 4 * 256 + 2 * (1000 * 2 * 256)
     # the base is not used (nor checked) without rotation
     o0 = _lib.softmax_options(rotary_dim=0, rope_base=0.0)
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o0)) > 0
