@@ -9,7 +9,8 @@
  *            S_t = S_{t-1} + phi(k_t) v_t^T, z_t = z_{t-1} + phi(k_t).
  *   [Arch]   "MiniMax-Text-01 405B MoE模型架构与训练策略解析", section 2.1:
  *            Q, K, V = SiLU(.), Y = Q (K^T V), out = RMSNorm(Y) * sigmoid(X).
- *   [Deploy] xdnf.cn/news/303307 (MoE memory under long context), section 3:
+ *   [Deploy] "为什么 MoE 稀疏激活在长上下文下反而更吃显存" (the first heading of the
+ *            xdnf.cn page on MoE memory under long context), section 3:
  *            lightning-attention block size 256 with tail pad options
  *            {32, 64, 128}, chunked prefill; section 6: prefill and decode
  *            run as separate calls.

@@ -1,6 +1,6 @@
 """Fixtures under tests/golden: the oracle against its stored regression
 outputs, and the serving defaults against the constants the deployment page
-prints (page at xdnf.cn/news/303307, section 3)."""
+prints (the xdnf.cn page "为什么 MoE 稀疏激活在长上下文下反而更吃显存", section 3)."""
 import inspect
 import json
 import os
