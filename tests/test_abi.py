@@ -270,6 +270,11 @@ def test_softmax_workspace_bytes(lib):
     o16 = _lib.softmax_options(precision=2)
     assert lib.la_softmax_workspace_bytes(1, 1000, 1000, 4, 2, 128, BF16, F32,
                                           ctypes.byref(o16)) == 1000 * 4 * 256 + 2 * (1000 * 2 * 256)
+    # packed: the work order follows the fp16 v, so mode 2 needs exactly the v
+    # bytes more than the single mode for the same batch
+    n0 = lib.la_softmax_workspace_bytes(3, 1000, 600, 4, 2, 128, BF16, BF16, ctypes.byref(o))
+    n2 = lib.la_softmax_workspace_bytes(3, 1000, 600, 4, 2, 128, BF16, BF16, ctypes.byref(o16))
+    assert n2 == n0 + 1000 * 2 * 256
     # the base is not used (nor checked) without rotation
     o0 = _lib.softmax_options(rotary_dim=0, rope_base=0.0)
     assert lib.la_softmax_workspace_bytes(1, 16, 16, 4, 4, 128, BF16, F32, ctypes.byref(o0)) > 0
