@@ -43,6 +43,12 @@ constexpr int kValuDefaultBlock = 64;
 constexpr int kMinAutoChunk = 512;
 constexpr int kMaxAutoChunk = 16384;
 constexpr int64_t kTargetItems = 2048;  // (chunk, head) workgroups aimed for: ~4 per CU slot
+// Fused plans with chunks of at least this many tokens run the chunk-state
+// pass on half chunks, with the one-buffer kernel at four workgroups per CU
+// (the scan adds the two halves): the fused pass sizes its chunks for one
+// resident round of two workgroups per CU, the state pass runs better with
+// more, smaller workgroups.
+constexpr int kSubChunkMin = 8192;
 constexpr int kSpinLimit = 1 << 22;     // bounded waits of the fused gate (~seconds)
 constexpr size_t kStatusBytes = 256;    // the call's device status word, padded
 #ifndef LA_DECODE_SPLIT
@@ -109,7 +115,10 @@ struct Plan {
     bool cdev;         // varlen, fused: the chunk length is searched on the device (<= C)
     int c_lo;          // its lower bound
     int64_t teams;     // fused: resident (chunk, head) teams = items bound
-    size_t off_chunk_off, off_buf, off_y, total;
+    bool half;         // chunk-state pass on half chunks (equal lengths, fused, C >= kSubChunkMin)
+    int cps2;          // its half chunks per sequence
+    int64_t items2;    // and their count
+    size_t off_chunk_off, off_buf, off_part, off_y, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -236,6 +245,9 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
         p.C = (int)(c < 64 ? 64 : c);
     }
     p.items = items_for(varlen, num_seqs, total_T, max_seqlen, p.C);
+    p.half = p.fuse_ok && !varlen && p.chunked && p.C >= kSubChunkMin;
+    p.cps2 = p.half ? (int)((max_seqlen + p.C / 2 - 1) / (p.C / 2)) : 0;
+    p.items2 = p.half ? (int64_t)num_seqs * p.cps2 : 0;
     // Fused varlen batches whose sequences span chunks: C above is sized for
     // the worst case of the lengths (every sequence ends in a short chunk);
     // the chunk planner searches, on the device, the smallest chunk length
@@ -255,6 +267,8 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
     if (varlen) off += align256((size_t)(num_seqs + 2) * sizeof(int32_t));
     p.off_buf = off;
     if (p.chunked) off += align256((size_t)p.items * H * p.stride * sizeof(float));
+    p.off_part = off;
+    if (p.half) off += align256((size_t)p.items2 * H * p.stride * sizeof(float));
     p.off_y = off;
     if (o.gated && out_dtype != LA_DTYPE_F32 && !p.fuse_ok)
         off += align256((size_t)total_T * H * d * sizeof(float));
@@ -324,9 +338,19 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
     if (p.chunked) {
         tm.before();
         if (p.mfma) {
-            const auto ck = norm ? (o.feat ? mf::k_chunk_state<true, true> : mf::k_chunk_state<true, false>)
-                                 : (o.feat ? mf::k_chunk_state<false, true> : mf::k_chunk_state<false, false>);
-            ck<<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            if (p.half) {
+                const auto ck1 = norm ? (o.feat ? mf::k_chunk_state1<true, true> : mf::k_chunk_state1<true, false>)
+                                      : (o.feat ? mf::k_chunk_state1<false, true> : mf::k_chunk_state1<false, false>);
+                ItemMap m2 = map;
+                m2.C = p.C / 2;
+                m2.cps = p.cps2;
+                ck1<<<dim3((unsigned)p.items2, (unsigned)H), mf::NT, 0, st>>>(
+                    (const uint16_t*)k, (const uint16_t*)v, m2, H, (float*)(ws + p.off_part), p.stride);
+            } else {
+                const auto ck = norm ? (o.feat ? mf::k_chunk_state<true, true> : mf::k_chunk_state<true, false>)
+                                     : (o.feat ? mf::k_chunk_state<false, true> : mf::k_chunk_state<false, false>);
+                ck<<<grid, mf::NT, 0, st>>>((const uint16_t*)k, (const uint16_t*)v, map, H, buf, p.stride);
+            }
         } else if (d == 128) {
             if (norm) vk::k_valu_state<128, InT, true><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
             else vk::k_valu_state<128, InT, false><<<grid, vk::NT, 0, st>>>((const InT*)k, (const InT*)v, map, H, buf, p.stride, o.feat ? 1 : 0);
@@ -342,7 +366,8 @@ la_status_t launch_prefill_typed(const Plan& p, const Opts& o, const void* q, co
         k_chunk_scan<<<dim3((unsigned)nblk, (unsigned)H, (unsigned)nseq), 256, 0, st>>>(
             buf, p.stride, map, H, d, E, state_in, norm ? z_in : nullptr, state_out,
             norm ? z_out : nullptr, p.fuse_ok ? (uint64_t*)(ws + p.off_xbuf) : nullptr,
-            p.fuse_ok ? p.xbuf_words + (int64_t)(kStatusBytes / 8) : 0);
+            p.fuse_ok ? p.xbuf_words + (int64_t)(kStatusBytes / 8) : 0,
+            p.half ? (const float*)(ws + p.off_part) : nullptr, p.cps2);
         if (hipGetLastError() != hipSuccess) return LA_ERR_HIP;
         tm.after();
     }

@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
                                                     ItemMap map, int H, int D, int E,
                                                     const float* state_in, const float* z_in,
                                                     float* state_out, float* z_out,
-                                                    uint64_t* __restrict__ xclear, int64_t nclear) {
+                                                    uint64_t* __restrict__ xclear, int64_t nclear,
+                                                    const float* __restrict__ half, int32_t cps2) {
     // the fused gate's exchange buffer (when the main pass that follows has
     // one) is cleared here too, which saves a launch
     if (xclear) {
@@ -100,13 +101,22 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float* __restrict__ buf, int
         else acc = z_in ? z_in[((size_t)row * H + h) * D + (e - DD)] : 0.f;
     }
     // eight increments in flight at a time, then their prefixes in order (the
-    // last chunk has no increment: the main pass writes the final state)
+    // last chunk has no increment: the main pass writes the final state).
+    // With `half` (equal-length sequences) chunk i's increment is the sum of
+    // the increments of its half chunks 2i and 2i + 1, held there.
     constexpr int U = 8;
+    const size_t h0 = (size_t)s * cps2;
     for (int32_t i0 = 0; i0 < count; i0 += U) {
         float dlt[U];
 #pragma unroll
-        for (int j = 0; j < U; ++j)
-            dlt[j] = i0 + j < count - 1 ? buf[((size_t)(first + i0 + j) * H + h) * stride + e] : 0.f;
+        for (int j = 0; j < U; ++j) {
+            const int32_t i = i0 + j;
+            dlt[j] = 0.f;
+            if (i < count - 1)
+                dlt[j] = half ? half[((h0 + 2 * i) * H + h) * stride + e] +
+                                    half[((h0 + 2 * i + 1) * H + h) * stride + e]
+                              : buf[((size_t)(first + i) * H + h) * stride + e];
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             if (i0 + j < count) buf[((size_t)(first + i0 + j) * H + h) * stride + e] = acc;

@@ -412,6 +412,73 @@ __global__ __launch_bounds__(NT, 2) void k_chunk_state(const uint16_t* __restric
     if (NORM && tid < D) dst[D * D + tid] = zacc;
 }
 
+// The same increment with one staging buffer (39 KB of LDS, at most 128
+// VGPRs): four workgroups per CU, whose interleaving hides the latency that
+// the two-buffer pipeline above hides inside one workgroup.  Per 32-token
+// block: stage (SiLU + split), load the next block, barrier, state update,
+// barrier.  Used for plans with twice as many chunks as resident slots of the
+// two-buffer kernel.
+struct SmemState1 {
+    static constexpr int TB = 32;
+    __attribute__((aligned(16))) uint16_t kh[TB * KS];
+    __attribute__((aligned(16))) uint16_t kl[TB * KS];
+    __attribute__((aligned(16))) uint16_t vh[TB * KS];
+    __attribute__((aligned(16))) uint16_t vl[TB * KS];
+    float zpart[4 * D];
+};
+
+template <bool NORM, bool FEAT = false>
+__global__ __launch_bounds__(NT, 4) void k_chunk_state1(const uint16_t* __restrict__ k,
+                                                        const uint16_t* __restrict__ v, ItemMap map,
+                                                        int H, float* __restrict__ buf,
+                                                        int64_t buf_stride) {
+    constexpr int TB = SmemState1::TB;
+    using L = Tile<TB>;
+    __shared__ SmemState1 sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.y;
+    Item it;
+    if (!decode_item(map, blockIdx.x, it) || it.last) return;
+
+    f32x4_t S[8][2];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) S[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float zacc = 0.f;
+
+    const int ntiles = (it.len + TB - 1) / TB;
+    const uint32_t rs = (uint32_t)H * D;
+    const uint16_t* kb = head_row(k, it.t0, H, h);
+    const uint16_t* vb = head_row(v, it.t0, H, h);
+    uint4 rk[L::NJ], rv[L::NJ];
+    load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, it.len), rs, tid);
+    load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, it.len), rs, tid);
+    for (int ti = 0; ti < ntiles; ++ti) {
+        stage_kv<NORM, L::NJ, FEAT>(rk, rv, sm.kh, sm.kl, sm.vh, sm.vl, sm.zpart, tid);
+        kb += (size_t)TB * rs;
+        vb += (size_t)TB * rs;
+        const int n1 = it.len - (ti + 1) * TB;  // <= 0 past the last block: zeros, never staged
+        load_tile_buf<L::NJ>(rk, tile_rsrc(kb, rs, n1), rs, tid);
+        load_tile_buf<L::NJ>(rv, tile_rsrc(vb, rs, n1), rs, tid);
+        __syncthreads();
+        if (NORM && tid < D)
+            zacc += (sm.zpart[tid] + sm.zpart[D + tid]) + (sm.zpart[2 * D + tid] + sm.zpart[3 * D + tid]);
+        state_update<1, FEAT>(S, sm.kh, sm.kl, sm.vh, sm.vl, 1, wave, g, c);
+        __syncthreads();
+    }
+    (void)lane;
+    float* dst = buf + ((size_t)blockIdx.x * H + h) * buf_stride;
+#pragma unroll
+    for (int dkt = 0; dkt < 8; ++dkt)
+#pragma unroll
+        for (int dvt = 0; dvt < 2; ++dvt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[(16 * dkt + 4 * g + i) * D + 32 * wave + 16 * dvt + c] = S[dkt][dvt][i];
+    if (NORM && tid < D) dst[D * D + tid] = zacc;
+}
+
 // Arguments of the fused gate (RMSNorm over all H heads of a token, times
 // w * sigmoid(x)), applied by the main pass when its workgroups run as
 // cooperative teams of H (one per head) that exchange per-token sums of y^2.
