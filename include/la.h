@@ -195,9 +195,12 @@ la_status_t la_prefill(const void* q, const void* k, const void* v,
  * same arguments and result, without a workspace.  Its scratch space is a
  * fixed array of LA_NOALLOC_SCRATCH_BYTES bytes per GPU that the library
  * holds until the process ends (its address is looked up on the first call
- * on a device); the call allocates nothing.  Calls whose plan needs more
- * (la_prefill_workspace_bytes of the same arguments) return
- * LA_ERR_WORKSPACE_TOO_SMALL with no side effects; 64 MiB holds, e.g., the
+ * on a device); the call allocates nothing.  It takes la_prefill's plan
+ * (la_prefill_workspace_bytes of the same arguments), or, when that plan
+ * runs the chunk-state pass on half chunks and does not fit, the same plan
+ * with that pass on whole chunks (the same result up to the rounding order
+ * of the chunk prefixes); a call whose plan still needs more returns
+ * LA_ERR_WORKSPACE_TOO_SMALL with no side effects.  64 MiB holds, e.g., the
  * gated prefill of one 4,194,304-token sequence with 8 heads of d = 128.
  * Every call on one GPU shares that GPU's array: calls that overlap in time
  * on one GPU (on different streams, or from different threads without

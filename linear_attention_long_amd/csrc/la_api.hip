@@ -199,7 +199,7 @@ const void* fused_kernel(bool norm, bool f32_out, bool feat) {
 }
 
 Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqlen, int H, int d,
-               la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o) {
+               la_dtype_t in_dtype, la_dtype_t out_dtype, const Opts& o, bool allow_half = true) {
     Plan p{};
     p.varlen = varlen;
     p.block = o.block;
@@ -245,7 +245,7 @@ Plan make_plan(bool varlen, int64_t num_seqs, int64_t total_T, int64_t max_seqle
         p.C = (int)(c < 64 ? 64 : c);
     }
     p.items = items_for(varlen, num_seqs, total_T, max_seqlen, p.C);
-    p.half = p.fuse_ok && !varlen && p.chunked && p.C >= kSubChunkMin;
+    p.half = allow_half && p.fuse_ok && !varlen && p.chunked && p.C >= kSubChunkMin;
     p.cps2 = p.half ? (int)((max_seqlen + p.C / 2 - 1) / (p.C / 2)) : 0;
     p.items2 = p.half ? (int64_t)num_seqs * p.cps2 : 0;
     // Fused varlen batches whose sequences span chunks: C above is sized for
@@ -717,7 +717,11 @@ la_status_t la_prefill_noalloc(const void* q, const void* k, const void* v, cons
     s = check_prefill_common(q, k, v, x_gate, rms_weight, state_in, z_in, out, state_out, z_out, Bt,
                              total_T, H, d, in_dtype, out_dtype, o);
     if (s != LA_OK) return s;
-    const Plan p = make_plan(false, Bt, total_T, T, H, d, in_dtype, out_dtype, o);
+    Plan p = make_plan(false, Bt, total_T, T, H, d, in_dtype, out_dtype, o);
+    // the half-chunk state pass needs room for its partial increments: without
+    // it the plan may still fit the array
+    if (p.total > (size_t)LA_NOALLOC_SCRATCH_BYTES && p.half)
+        p = make_plan(false, Bt, total_T, T, H, d, in_dtype, out_dtype, o, false);
     if (p.total > (size_t)LA_NOALLOC_SCRATCH_BYTES) return LA_ERR_WORKSPACE_TOO_SMALL;
     void* ws = nullptr;
     if (p.total > 0) {

@@ -74,3 +74,32 @@ def test_noalloc_rejects_a_plan_beyond_its_scratch():
     assert noalloc_call(q, q, q, None, opt, out, None) == _lib.LA_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+def test_noalloc_falls_back_to_whole_chunk_state_pass_when_half_chunks_do_not_fit():
+    """A gated 524,288-token call: with a caller workspace the plan runs the
+    chunk-state pass on half chunks, whose partial increments push it past the
+    fixed array; the entry point then plans the state pass on whole chunks,
+    which fits.  The two plans round the chunk prefixes in different orders,
+    so the outputs agree to fp32 accumulation (held to 1e-4 of rms), not bit
+    for bit."""
+    lib = _lib.load()
+    T, H = 1 << 19, 8
+    banner("noalloc fallback T=%d H=%d gated" % (T, H))
+    opt = _lib.options(gated=True)
+    need = lib.la_prefill_workspace_bytes(1, T, H, 128, BF16, F32, ctypes.byref(opt))
+    assert need > _lib.LA_NOALLOC_SCRATCH_BYTES
+    g = torch.Generator(device=DEV).manual_seed(21)
+    s = 1.0 / np.sqrt(128)
+    q, k, v = ((torch.randn((1, T, H, 128), generator=g, device=DEV) * s).to(torch.bfloat16)
+               for _ in range(3))
+    x = torch.randn((1, T, H * 128), generator=g, device=DEV).to(torch.bfloat16)
+    out = torch.full((1, T, H * 128), float("nan"), device=DEV)
+    so = torch.full((1, H, 128, 128), float("nan"), device=DEV)
+    assert noalloc_call(q, k, v, x, opt, out, so) == _lib.LA_OK
+    ref_out, ref_S, _ = api.la_prefill(q, k, v, x)
+    torch.cuda.synchronize()
+    err = float((out - ref_out).abs().max() / ref_out.pow(2).mean().sqrt())
+    serr = float((so - ref_S).abs().max() / ref_S.pow(2).mean().sqrt())
+    print("noalloc whole-chunk plan against the half-chunk plan: out %.2e, state %.2e of rms" % (err, serr))
+    assert err <= 1e-4 and serr <= 1e-4
