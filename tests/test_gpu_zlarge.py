@@ -83,6 +83,38 @@ def test_prefill_1m_workload_sampled():
     assert e_out <= TOL_BF16 and e_S <= TOL_BF16
 
 
+def test_prefill_512k_normalized_half_chunk_state_pass():
+    """The normalised mode through the plan of long gated prefills (chunk-state
+    pass on half chunks, whose increments carry the column sums of phi(k) for
+    z): 524,288 tokens x 8 heads, gated, against the oracle's normalised
+    recurrence at sampled tokens, final S and z in full."""
+    T, H, d = 1 << 19, 8, 128
+    banner("prefill 512K normalized (half-chunk state pass)")
+    g = torch.Generator(device="cuda").manual_seed(31)
+    s = 1.0 / np.sqrt(d)
+    q, k, v = ((torch.randn((1, T, H, d), generator=g, device="cuda") * s).to(torch.bfloat16)
+               for _ in range(3))
+    x = torch.randn((1, T, H * d), generator=g, device="cuda").to(torch.bfloat16)
+    out, S, z = api.la_prefill(q, k, v, x, normalized=True)
+    torch.cuda.synchronize()
+    C, dev = chunk_tokens(False, 1, T, T, H, d)
+    assert C >= 8192 and not dev  # the half-chunk state pass applies
+    idx = sample_tokens([0], [T], C, 2048, 9)
+    got = np64(out[0, torch.from_numpy(idx).cuda()])
+    S_got, z_got = np64(S), np64(z)
+    del out, S, z
+    qc, kc, vc = (t[0].float().cpu() for t in (q, k, v))
+    xs = x[0, torch.from_numpy(idx).cuda()].float().cpu()
+    del q, k, v, x
+    torch.cuda.empty_cache()
+    y, S_ref, z_ref = O.prefill_sampled_f32(qc, kc, vc, idx, normalized=True, nthreads=H)
+    ref = O.gate(y.reshape(len(idx), H * d), xs, None, 0, 1e-6)
+    e_out, e_S, e_z = rel_err(got, ref), rel_err(S_got, S_ref), rel_err(z_got, z_ref)
+    print("prefill 512K normalized: %d sampled tokens, rel err out %.3e state %.3e z %.3e"
+          % (len(idx), e_out, e_S, e_z))
+    assert e_out <= TOL_BF16 and e_S <= TOL_BF16 and e_z <= TOL_BF16
+
+
 def test_prefill_4m_past_32bit_offsets():
     """One 4,194,307-token sequence (the pages' 4M-token inference context),
     8 heads of 128, gated: each of q, k, v holds 4.29e9 elements, so the last
